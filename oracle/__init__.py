@@ -1,0 +1,61 @@
+"""CPU oracle for the VC-Attention forward pass.
+
+TEST INFRASTRUCTURE ONLY: a plain, slow restatement of the method from the
+pages (see the module docstrings for the sources and every reading taken
+where the pages are silent).  Only tests, the smoke check and the benchmark's
+CPU-baseline leg may import it; the product path never does.
+
+Entry points:
+  prepare_head(K, V, init_idx, ...)   V-Smooth + K smoothing for one head
+  attend_rows(Q, prep, tiles, ...)    ExpCast online-softmax attention for
+                                      selected 128-row query tiles
+  exact_attention, psnr               fp64 reference and fidelity metric
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import formats, kmeans, vsmooth, attention
+from .attention import DEFAULT_BETA, exact_attention, psnr, softmax_scale
+
+Q_TILE = 128
+
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def prepare_head(K: np.ndarray, V: np.ndarray, init_idx: np.ndarray, k: int, iters: int,
+                 kv_block: int, fmt: str = "e4m3", vsmooth_on: bool = True,
+                 quantize: bool = True) -> dict:
+    """K, V: [N, d] fp64 bf16 values of one head."""
+    N = V.shape[0]
+    if vsmooth_on:
+        labels, cents = kmeans.kmeans(V, init_idx, iters)
+        perm = vsmooth.stable_sort_perm(labels, init_idx.shape[0])
+    else:
+        labels, cents = None, []
+        perm = np.arange(N, dtype=np.int32)
+    vs = vsmooth.vsmooth_values(V, perm, kv_block, fmt, vsmooth_on, quantize)
+    ks = vsmooth.ksmooth(K, perm, kv_block, vsmooth_on, quantize)
+    return {"labels": labels, "centroids": cents, "perm": perm, "v": vs, "k": ks,
+            "N": N, "kv_block": kv_block, "fmt": fmt, "quantize": quantize}
+
+
+def attend_rows(Q: np.ndarray, prep: dict, tiles, scale: float = 0.0, beta: float = DEFAULT_BETA,
+                trace: dict | None = None) -> dict:
+    """Returns {tile index: O rows (fp64)} for the requested 128-row tiles."""
+    N, d = Q.shape
+    sc = softmax_scale(d, scale)
+    out = {}
+    for t in tiles:
+        lo, hi = t * Q_TILE, min((t + 1) * Q_TILE, N)
+        out[t] = attention.attend_tile(
+            Q[lo:hi], prep["k"]["kdec"], prep["k"]["k_scale"], prep["v"]["vres"],
+            prep["v"]["col_scale"], prep["v"]["means"], prep["N"], prep["kv_block"], sc,
+            beta, prep["quantize"], trace)
+    return out
+
+
+def n_q_tiles(N: int) -> int:
+    return (N + Q_TILE - 1) // Q_TILE

@@ -1,0 +1,133 @@
+"""Blocked online-softmax attention with ExpCast-FP8 and mean restoration
+(CPU oracle; TEST INFRASTRUCTURE ONLY).
+
+ExpCast-FP8 ([brief] section "ExpCast-FP8"; [clarity]; [rw]): one E4M3 byte
+is roughly 8*log2(p) + 56, so the probability byte is obtained straight from
+the log2-domain score z (relative to the row maximum, z <= 0) by one fused
+multiply-add computing 8z + 56 + beta and rounding, with no fp32 exponential
+and no separate cast.  Readings:
+  * t_j = c * S_j is the log2-domain score, with S the exact dot product of
+    the E4M3 values of the quantised query and key and
+    c = fp32(fp32(fp32(s_q*scale)*log2e) * s_k);
+  * the running maximum m is kept in these units, m = max(m, fp32(c*max_j S_j));
+  * the single FMA is evaluated as  x = fma(S_j, 8c, fp32(56 + beta - 8m))  in
+    binary32 with one rounding, and byte = clamp(rne(x), 0, 56);
+  * beta is not given on the pages; the default -0.45840 = 8/ln2 - 12 makes
+    the mean pre-rounding offset against exact exp2 zero over fractional z.
+  * padded keys score -inf, giving byte 0.
+
+Online softmax and mean restoration ([brief] "V-Smooth", last sentences:
+restoring the mean costs nothing because it comes from the row sums the
+online softmax keeps; [clarity]: one pass over the values):
+  per KV block b in ascending order, with p = decoded bytes,
+    rowsum_b = sum_j p_j,  alpha = 2^(m_old - m_new)  (0 on the first block)
+    l    = alpha*l + rowsum_b
+    acc  = alpha*acc + p . Vres_b
+    accM = alpha*accM + rowsum_b * mean_b
+  O = (col_scale * acc + accM) / l.
+Accumulators are fp64 here.
+
+``quantize=False`` (self-check): no rounding anywhere and p = 2^(t - m)
+exactly, with blocking, permutation, K smoothing and mean restoration kept.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+from .formats import f32, fma_f32, e4m3_encode, e4m3_decode
+
+LOG2E = 1.4426950408889634
+DEFAULT_BETA = 8.0 / math.log(2.0) - 12.0
+
+
+def expcast_bytes(S32: np.ndarray, A: float, B: np.ndarray) -> np.ndarray:
+    """Bytes = clamp(rne(fma_f32(S32, A, B)), 0, 56).  B broadcasts per row."""
+    x = fma_f32(S32, A, B)
+    with np.errstate(invalid="ignore"):
+        c = np.clip(np.rint(x), 0.0, 56.0)
+    c = np.where(np.isnan(c), 0.0, c)
+    return c.astype(np.uint8)
+
+
+def softmax_scale(d: int, scale: float = 0.0) -> float:
+    return float(f32(1.0 / math.sqrt(d))) if scale == 0.0 else float(f32(scale))
+
+
+def quantize_q_tile(Q: np.ndarray):
+    """Per 128-row query tile: s_q = fp32(max|Q|/448) (1 if all zero),
+    codes = E4M3(fp32(Q / s_q))."""
+    amax = float(np.max(np.abs(Q))) if Q.size else 0.0
+    s_q = float(f32(amax / 448.0)) if amax > 0 else 1.0
+    codes = e4m3_encode(f32(Q / s_q))
+    return codes, s_q
+
+
+def attend_tile(Q: np.ndarray, kdec: np.ndarray, k_scale: np.ndarray, vres: np.ndarray,
+                col_scale: np.ndarray, means: np.ndarray, N: int, kv_block: int,
+                scale: float, beta: float = DEFAULT_BETA, quantize: bool = True,
+                trace: dict | None = None) -> np.ndarray:
+    """One query tile (rows of Q, fp64 bf16 values) against all KV blocks.
+    kdec / vres: decoded permuted keys and residuals [nblk*kv_block, d]."""
+    nblk = k_scale.shape[0]
+    n, d = Q.shape
+    dv = vres.shape[1]
+    if quantize:
+        qc, s_q = quantize_q_tile(Q)
+        qdec = e4m3_decode(qc)
+        cq = float(f32(f32(s_q * scale) * f32(LOG2E)))
+        Kc = float(f32(56.0 + beta))
+    else:
+        qdec = Q
+        cq = scale * LOG2E
+    m = np.full(n, -np.inf)
+    l = np.zeros(n)
+    acc = np.zeros((n, dv))
+    accM = np.zeros((n, dv))
+    for b in range(nblk):
+        lo, hi = b * kv_block, (b + 1) * kv_block
+        nvalid = min(hi, N) - lo
+        S = qdec @ kdec[lo:hi].T                     # exact for E4M3 operands
+        if quantize:
+            c = float(f32(cq * k_scale[b]))
+            S32 = f32(S)
+            S32[:, nvalid:] = -np.inf
+            t_max = f32(c * np.max(S32, axis=1))
+            m_new = np.maximum(m, t_max)
+            Brow = f32(Kc - 8.0 * m_new)
+            codes = expcast_bytes(S32, 8.0 * c, Brow[:, None])
+            p = e4m3_decode(codes)
+            if trace is not None:
+                trace.setdefault("codes", []).append(codes)
+                trace.setdefault("S32", []).append(S32)
+                trace.setdefault("A", []).append(8.0 * c)
+                trace.setdefault("B", []).append(Brow)
+        else:
+            t = S * cq
+            t[:, nvalid:] = -np.inf
+            m_new = np.maximum(m, np.max(t, axis=1))
+            p = np.exp2(t - m_new[:, None])
+        rs = np.sum(p, axis=1)
+        with np.errstate(invalid="ignore"):
+            alpha = np.where(np.isneginf(m), 0.0, np.exp2(m - m_new))
+        l = alpha * l + rs
+        acc = alpha[:, None] * acc + p @ vres[lo:hi]
+        accM = alpha[:, None] * accM + rs[:, None] * means[b][None, :]
+        m = m_new
+    return (col_scale[None, :] * acc + accM) / l[:, None]
+
+
+def exact_attention(Q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) -> np.ndarray:
+    """fp64 softmax(Q K^T * scale) V for one head (rows of Q)."""
+    S = (Q @ K.T) * scale
+    S -= np.max(S, axis=1, keepdims=True)
+    P = np.exp(S)
+    return (P @ V) / np.sum(P, axis=1, keepdims=True)
+
+
+def psnr(O: np.ndarray, Oref: np.ndarray) -> float:
+    """10 log10(max|O_ref|^2 / mean((O - O_ref)^2))."""
+    mse = float(np.mean((np.asarray(O, np.float64) - Oref) ** 2))
+    peak = float(np.max(np.abs(Oref))) ** 2
+    return float("inf") if mse == 0 else 10.0 * math.log10(peak / mse)

@@ -1,0 +1,69 @@
+"""Per-head k-means over value tokens (CPU oracle; TEST INFRASTRUCTURE ONLY).
+
+What the pages give: V-Smooth first runs one lightweight k-means that puts
+similar value tokens together ([brief] section "V-Smooth", first of its three
+steps; [rw] "lightweight online clustering"; [clarity] "clusters similar
+value tokens online").  They give no distance arithmetic, initialisation or
+iteration count.  The readings used here (all stated as readings):
+
+* Distances are computed on int8 codes with one scale per head,
+  sV = fp32(max|V| / 127), code = clamp(rne(fp32(x / sV)), -127, 127), for both
+  tokens and centroids, as D = |c|^2 - 2 v.c in exact integers.  "Lightweight"
+  is read as: cheap enough to run inside the attention call.
+* Initial centroids are the value rows at k distinct token indices that the
+  caller supplies (drawn at random by the input generator).
+* ``iters`` assignment passes, with a centroid update between consecutive
+  passes; the final labels are those of the last pass.
+* Ties go to the lowest cluster index.
+* Update: the fp32 rounding of the fp64 mean of the members' original values;
+  a cluster with no members keeps its centroid.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .formats import f32
+
+
+def int8_scale(V: np.ndarray) -> float:
+    amax = float(np.max(np.abs(V))) if V.size else 0.0
+    return float(f32(amax / 127.0)) if amax > 0 else 1.0
+
+
+def quant_i8(X: np.ndarray, sV: float) -> np.ndarray:
+    return np.clip(np.rint(f32(X / sV)), -127, 127)
+
+
+def assign(Vq: np.ndarray, Cq: np.ndarray) -> np.ndarray:
+    """argmin_c (|c|^2 - 2 v.c); np.argmin returns the first (lowest) index on
+    ties.  Integer products and sums stay below 2^53, so fp64 BLAS is exact."""
+    cn = np.sum(Cq * Cq, axis=1)
+    D = cn[None, :] - 2.0 * (Vq @ Cq.T)
+    return np.argmin(D, axis=1).astype(np.int32)
+
+
+def update(V: np.ndarray, labels: np.ndarray, C_old: np.ndarray) -> np.ndarray:
+    k = C_old.shape[0]
+    sums = np.zeros_like(C_old, dtype=np.float64)
+    np.add.at(sums, labels, V)                       # fp64, token order
+    counts = np.bincount(labels, minlength=k).astype(np.float64)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        mean = f32(sums / counts[:, None])
+    return np.where(counts[:, None] > 0, mean, C_old)
+
+
+def kmeans(V: np.ndarray, init_idx: np.ndarray, iters: int):
+    """V: [N, d] float64 holding the bf16 values of one head.
+    Returns (labels int32 [N], centroids_per_pass list of [k, d] arrays: the
+    centroids each assignment pass used)."""
+    sV = int8_scale(V)
+    Vq = quant_i8(V, sV)
+    C = V[np.asarray(init_idx, dtype=np.int64)].astype(np.float64)
+    used = []
+    labels = None
+    for it in range(iters):
+        used.append(C.copy())
+        labels = assign(Vq, quant_i8(C, sV))
+        if it + 1 < iters:
+            C = update(V, labels, C)
+    return labels, used

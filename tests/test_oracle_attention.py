@@ -1,0 +1,134 @@
+"""Pins for the oracle's attention: quantisation-disabled equals fp64 softmax
+attention, the mean-restoration identity in exact rationals, and special
+cases whose result is known in closed form."""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import formats as F
+from oracle.attention import attend_tile, exact_attention, softmax_scale
+from bit_attention_video_amd import inputs
+
+
+def _head(N, d=64, kvb=64, k=16, seed=7):
+    w = inputs.small(inputs.WORKLOADS["tiny"], N=N, d=d, kv_block=kvb, k=k, seed=seed)
+    q, kk, v, init = inputs.gen_head(w, 0, 0)
+    return w, oracle.bf16_to_f64(q), oracle.bf16_to_f64(kk), oracle.bf16_to_f64(v), init
+
+
+def _all_rows(Q, prep, scale=0.0):
+    o = oracle.attend_rows(Q, prep, range(oracle.n_q_tiles(Q.shape[0])), scale)
+    return np.concatenate([o[t] for t in sorted(o)])
+
+
+@pytest.mark.parametrize("N,d,kvb,vs", [(1000, 64, 64, True), (1000, 64, 64, False),
+                                        (700, 128, 128, True), (129, 64, 64, True), (64, 64, 64, True)])
+def test_quantisation_disabled_equals_exact_attention(N, d, kvb, vs):
+    w, Q, K, V, init = _head(N, d, kvb)
+    prep = oracle.prepare_head(K, V, init, w.k, w.iters, kvb, vsmooth_on=vs, quantize=False)
+    O = _all_rows(Q, prep)
+    ref = exact_attention(Q, K, V, softmax_scale(d))
+    assert np.max(np.abs(O - ref)) <= 1e-6 * np.max(np.abs(V))
+    assert np.max(np.abs(O - ref)) <= 1e-12 * np.max(np.abs(V))
+
+
+def test_mean_restoration_identity_exact():
+    # P.(mean 1^T + R) = rowsum * mean^T + P.R, in exact rationals, with
+    # P holding decoded E4M3 bytes and mean / R holding fp32 values
+    rng = np.random.default_rng(20)
+    n, kb, d = 3, 5, 4
+    P = F.e4m3_decode(rng.integers(0, 57, (n, kb)))
+    mean = F.f32(rng.standard_normal(d) * 3)
+    R = F.e4m3_decode(rng.integers(0, 0x7E, (kb, d)))
+    Pf = [[Fraction(float(x)) for x in row] for row in P]
+    Mf = [Fraction(float(x)) for x in mean]
+    Rf = [[Fraction(float(x)) for x in row] for row in R]
+    for i in range(n):
+        rs = sum(Pf[i])
+        for c in range(d):
+            lhs = sum(Pf[i][j] * (Mf[c] + Rf[j][c]) for j in range(kb))
+            rhs = rs * Mf[c] + sum(Pf[i][j] * Rf[j][c] for j in range(kb))
+            assert lhs == rhs
+    # and at a moderate size in fp64
+    P = F.e4m3_decode(rng.integers(0, 57, (128, 128)))
+    mean = F.f32(rng.standard_normal(128) * 3)
+    R = F.e4m3_decode(rng.integers(0, 0x7E, (128, 128)))
+    lhs = P @ (mean[None, :] + R)
+    rhs = P.sum(1)[:, None] * mean[None, :] + P @ R
+    assert np.max(np.abs(lhs - rhs)) <= 1e-12 * np.max(np.abs(lhs))
+
+
+def _dequantised_values(prep, N):
+    v = prep["v"]
+    kvb = prep["kv_block"]
+    return (v["vres"] * v["col_scale"][None, :] + np.repeat(v["means"], kvb, 0))[:N]
+
+
+def test_equal_scores_give_mean_of_dequantised_values():
+    # Q = 0: every score is 0, every byte is 56 (p = 1), so O is the plain mean
+    # of the dequantised (permuted) values over the real keys
+    w, Q, K, V, init = _head(200, 64, 64)
+    prep = oracle.prepare_head(K, V, init, w.k, w.iters, 64)
+    trace = {}
+    O = oracle.attend_rows(np.zeros_like(Q[:128]), prep, [0], trace=trace)[0]
+    assert all(np.all(c[:, :min(64, 200 - 64 * b)] == 56) for b, c in enumerate(trace["codes"]))
+    want = _dequantised_values(prep, 200).mean(0)
+    assert np.max(np.abs(O - want[None, :])) <= 1e-12 * np.max(np.abs(want))
+
+
+def test_dominant_key_gives_its_value_row():
+    # one key scores ~36 log2-units above every other key and sits in the
+    # first block (identity order, V-Smooth off): every later byte is
+    # round(8z+56+beta) with z <= -36, i.e. 0, so O is exactly that key's
+    # dequantised value row.  (Keys in blocks before it would keep a
+    # 2^-36-rescaled share, so the closed form needs it first.)
+    w, Q, K, V, init = _head(300, 64, 64)
+    Q = np.zeros_like(Q)
+    Q[:, 0] = 1.0
+    K = K.copy()
+    K[:, 0] = 0.0
+    K[0, 0] = 200.0
+    prep = oracle.prepare_head(K, V, init, w.k, w.iters, 64, vsmooth_on=False)
+    O = oracle.attend_rows(Q, prep, [0, 1, 2])
+    want = _dequantised_values(prep, 300)[0]
+    for t in O.values():
+        assert np.max(np.abs(t - want[None, :])) <= 1e-12 * np.max(np.abs(want))
+
+
+def test_single_block_and_rowsum_exact_in_fp32():
+    w, Q, K, V, init = _head(64, 64, 64)
+    prep = oracle.prepare_head(K, V, init, w.k, w.iters, 64)
+    trace = {}
+    oracle.attend_rows(Q, prep, [0], trace=trace)
+    assert len(trace["codes"]) == 1
+    p = F.e4m3_decode(trace["codes"][0])
+    # decoded bytes are multiples of 2^-9 and <= 1: a 64- or 128-term sum is
+    # exact in fp32 whatever the order
+    s64 = p.sum(1)
+    s32 = p.astype(np.float32)[:, ::-1].sum(1, dtype=np.float32)
+    assert np.array_equal(s64, s32.astype(np.float64))
+    assert np.all(np.max(p, axis=1) == 1.0)     # the row max always gets byte 56
+
+
+def test_expcast_never_binds_upper_clamp_on_workload():
+    # x = fma(S, 8c, 56+beta-8m) stays below 56.5 for every key, so the upper
+    # clamp of [0, 56] is never what decides a byte on this data
+    w, Q, K, V, init = _head(1024, 64, 64)
+    prep = oracle.prepare_head(K, V, init, w.k, w.iters, 64)
+    trace = {}
+    oracle.attend_rows(Q, prep, range(8), trace=trace)
+    for S32, A, B in zip(trace["S32"], trace["A"], trace["B"]):
+        x = F.fma_f32(S32, A, B[:, None])
+        assert np.nanmax(np.where(np.isfinite(x), x, -1)) < 56.5
+
+
+def test_vsmooth_and_expcast_fidelity_direction():
+    # directional claims of the pages on a synthetic head: with the 4-bit
+    # residual format, V-Smooth raises PSNR against exact attention
+    w, Q, K, V, init = _head(1024, 64, 64, k=16)
+    ref = exact_attention(Q, K, V, softmax_scale(64))
+    on = _all_rows(Q, oracle.prepare_head(K, V, init, 16, 3, 64, fmt="mxfp4", vsmooth_on=True))
+    off = _all_rows(Q, oracle.prepare_head(K, V, init, 16, 3, 64, fmt="mxfp4", vsmooth_on=False))
+    assert oracle.psnr(on, ref) > oracle.psnr(off, ref)

@@ -1,0 +1,189 @@
+"""Pins for the oracle's k-means, stable sort / blocking, V-Smooth residual
+quantisation and K smoothing: brute force on tiny inputs, exact rational
+arithmetic, a library sort, and the quantisers' error bounds."""
+import itertools
+from fractions import Fraction
+
+import numpy as np
+
+from oracle import kmeans as KM
+from oracle import vsmooth as VS
+from oracle import formats as F
+
+
+def brute_assign(Vq, Cq):
+    out = []
+    for v in Vq.astype(int).tolist():
+        best, bi = None, None
+        for ci, c in enumerate(Cq.astype(int).tolist()):
+            dist = sum(x * x for x in c) - 2 * sum(a * b for a, b in zip(v, c))
+            if best is None or dist < best:        # strict: lowest index wins ties
+                best, bi = dist, ci
+        out.append(bi)
+    return np.array(out)
+
+
+def test_assign_matches_brute_force_with_ties():
+    rng = np.random.default_rng(10)
+    for trial in range(30):
+        N, k, d = rng.integers(1, 12), rng.integers(1, 6), rng.integers(1, 5)
+        Vq = rng.integers(-127, 128, size=(N, d)).astype(np.float64)
+        Cq = rng.integers(-127, 128, size=(k, d)).astype(np.float64)
+        if k > 1 and trial % 3 == 0:
+            Cq[k - 1] = Cq[0]                      # exact duplicate: index 0 must win
+        assert np.array_equal(KM.assign(Vq, Cq), brute_assign(Vq, Cq))
+    # equidistant centroids: v=0, c=+-1 have the same distance; lower index wins
+    assert list(KM.assign(np.zeros((1, 1)), np.array([[1.0], [-1.0]]))) == [0]
+    assert list(KM.assign(np.zeros((1, 1)), np.array([[-1.0], [1.0]]))) == [0]
+
+
+def test_int8_quantiser():
+    V = np.array([[1.0, -2.0], [127.0, -127.5]])
+    s = KM.int8_scale(V)
+    assert s == float(F.f32(127.5 / 127.0))
+    q = KM.quant_i8(V, s)
+    assert q.min() >= -127 and q.max() <= 127
+    assert np.array_equal(q, np.clip(np.rint(F.f32(V / s)), -127, 127))
+
+
+def test_update_exact_mean_and_empty_cluster():
+    rng = np.random.default_rng(11)
+    V = F.f32(rng.standard_normal((20, 3)) * 3)
+    labels = rng.integers(0, 3, 20)
+    labels[labels == 2] = 1                       # cluster 2 empty
+    C_old = np.arange(9.0).reshape(3, 3)
+    C = KM.update(V, labels, C_old)
+    assert np.array_equal(C[2], C_old[2])
+    for c in (0, 1):
+        mem = V[labels == c]
+        for j in range(3):
+            exact = sum(Fraction(float(x)) for x in mem[:, j]) / len(mem)
+            assert C[c, j] == float(np.float32(float(exact)))
+
+
+def sse(V, labels, k):
+    tot = 0.0
+    for c in range(k):
+        m = V[labels == c]
+        if len(m):
+            tot += float(np.sum((m - m.mean(0)) ** 2))
+    return tot
+
+
+def test_kmeans_recovers_sse_optimum_on_separated_tiny_instances():
+    rng = np.random.default_rng(12)
+    for trial in range(10):
+        k = int(rng.integers(2, 4))
+        d = int(rng.integers(1, 4))
+        N = int(rng.integers(k + 1, 9))
+        while True:                                # well separated: centres >= 40 apart
+            centers = rng.standard_normal((k, d)) * 100
+            gaps = [np.linalg.norm(centers[i] - centers[j]) for i in range(k) for j in range(i)]
+            if min(gaps) >= 40:
+                break
+        own = np.concatenate([np.arange(k), rng.integers(0, k, N - k)])
+        V = F.f32(centers[own] + rng.standard_normal((N, d)) * 0.5)
+        init = np.array([np.flatnonzero(own == c)[0] for c in range(k)], np.int32)
+        labels, _ = KM.kmeans(V, init, iters=4)
+        best = min(sse(V, np.array(lab), k) for lab in itertools.product(range(k), repeat=N))
+        assert abs(sse(V, labels, k) - best) <= 1e-9 * max(1.0, best)
+
+
+def test_kmeans_pass_count_and_used_centroids():
+    rng = np.random.default_rng(13)
+    V = F.f32(rng.standard_normal((50, 4)))
+    init = rng.choice(50, 5, replace=False).astype(np.int32)
+    labels, used = KM.kmeans(V, init, iters=3)
+    assert len(used) == 3
+    assert np.array_equal(used[0], V[init])
+    # the labels are the assignment made with the last centroids
+    sV = KM.int8_scale(V)
+    assert np.array_equal(labels, KM.assign(KM.quant_i8(V, sV), KM.quant_i8(used[2], sV)))
+    assert np.array_equal(used[1], KM.update(V, KM.assign(KM.quant_i8(V, sV), KM.quant_i8(used[0], sV)), used[0]))
+
+
+def test_stable_sort_matches_library_and_is_bijection():
+    rng = np.random.default_rng(14)
+    for N, k in [(1, 1), (100, 7), (5000, 300)]:
+        lab = rng.integers(0, k, N)
+        perm = VS.stable_sort_perm(lab, k)
+        assert np.array_equal(perm, np.argsort(lab, kind="stable"))
+        assert np.array_equal(np.sort(perm), np.arange(N))
+        assert np.all(np.diff(lab[perm]) >= 0)
+
+
+def test_block_means_exact():
+    rng = np.random.default_rng(15)
+    N, kvb, d = 150, 64, 3
+    Vp = np.zeros((3 * kvb, d))
+    Vp[:N] = F.f32(rng.standard_normal((N, d)))
+    means = VS.block_means(Vp, N, kvb)
+    for b in range(3):
+        lo, hi = b * kvb, min((b + 1) * kvb, N)
+        for j in range(d):
+            exact = sum(Fraction(float(x)) for x in Vp[lo:hi, j]) / (hi - lo)
+            assert means[b, j] == float(np.float32(float(exact)))
+
+
+def test_e4m3_residuals_within_quantiser_bound():
+    rng = np.random.default_rng(16)
+    N, d, kvb = 300, 8, 64
+    V = F.f32(rng.standard_normal((N, d)) * 3)
+    V[5, 2] *= 20
+    perm = rng.permutation(N).astype(np.int32)
+    out = VS.vsmooth_values(V, perm, kvb, "e4m3")
+    means, s_v = out["means"], out["col_scale"]
+    r = np.zeros((5 * kvb, d))
+    r[:N] = F.f32(V[perm] - np.repeat(means, kvb, 0)[:N])
+    deq = out["vres"] * s_v[None, :]
+    # E4M3 RNE: relative error <= 2^-4 in the normal range, absolute <= 2^-10*s below it
+    assert np.all(np.abs(deq - r) <= np.maximum(np.abs(r) * 2 ** -4, s_v[None, :] * 2 ** -10) * (1 + 1e-12))
+    assert np.all(out["codes"][N:] == 0)
+    # per-channel scale is the residual's max magnitude over 448: that element maps to 448
+    amax = np.max(np.abs(r[:N]), axis=0)
+    assert np.array_equal(s_v, F.f32(amax / 448.0))
+
+
+def test_mxfp4_residuals_within_block_bound():
+    rng = np.random.default_rng(17)
+    N, d, kvb = 200, 4, 64
+    V = F.f32(rng.standard_normal((N, d)) * 3)
+    perm = np.arange(N, dtype=np.int32)
+    out = VS.vsmooth_values(V, perm, kvb, "mxfp4")
+    r = np.zeros((256, d))
+    r[:N] = F.f32(V - np.repeat(out["means"], kvb, 0)[:N])
+    X = F.e8m0_decode(out["e8m0"].astype(np.int64))            # [8, d]
+    Xe = np.repeat(X, 32, axis=0)
+    # the block maximum sits in [4X, 8X); E2M1 error <= half a grid step (0.25X .. 1X),
+    # plus clipping of values above 6X
+    err = np.abs(out["vres"] - r)
+    step = np.where(np.abs(r) < 2 * Xe, 0.5, np.where(np.abs(r) < 4 * Xe, 1.0, 2.0)) * Xe
+    clip = np.maximum(np.abs(r) - 6 * Xe, 0)
+    assert np.all(err <= step / 2 + clip + 1e-12)
+
+
+def test_vsmooth_off_is_plain_per_channel_quantisation():
+    rng = np.random.default_rng(18)
+    V = F.f32(rng.standard_normal((100, 4)))
+    out = VS.vsmooth_values(V, np.arange(100, dtype=np.int32), 64, "e4m3", vsmooth=False)
+    assert np.all(out["means"] == 0)
+    s = F.f32(np.max(np.abs(V), 0) / 448)
+    assert np.array_equal(out["codes"][:100], F.e4m3_encode(F.f32(V / s)))
+
+
+def test_ksmooth_per_block_scale_and_shift():
+    rng = np.random.default_rng(19)
+    N, d, kvb = 130, 4, 64
+    K = F.f32(rng.standard_normal((N, d)) + 5.0)
+    perm = rng.permutation(N).astype(np.int32)
+    ks = VS.ksmooth(K, perm, kvb)
+    mu = ks["mu"]
+    for j in range(d):
+        exact = sum(Fraction(float(x)) for x in K[:, j]) / N
+        assert mu[j] == float(np.float32(float(exact)))
+    Kp = F.f32(K - mu)[perm]
+    for b in range(3):
+        lo, hi = b * kvb, min((b + 1) * kvb, N)
+        s = ks["k_scale"][b]
+        assert s == float(F.f32(np.max(np.abs(Kp[lo:hi])) / 448))
+        assert np.max(np.abs(ks["kdec"][lo:hi])) == 448.0
