@@ -1,0 +1,223 @@
+"""Thin Python binding over libvcattn.so (ctypes).
+
+Argument marshalling only: torch provides device memory and the current HIP
+stream; every step of the forward pass runs in the library's HIP kernels.
+There is no fallback: a missing or unloadable library raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libvcattn.so")
+
+# ExpCast offset default: fp32(8/ln2 - 12), the value that centres
+# 8z + 56 + beta on the exact E4M3 code of 2^z over fractional z.
+DEFAULT_BETA = 8.0 / math.log(2.0) - 12.0
+
+E4M3, MXFP4 = 0, 1
+
+
+class VcConfig(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("N", ctypes.c_int32), ("d", ctypes.c_int32),
+                ("kv_block", ctypes.c_int32), ("n_clusters", ctypes.c_int32), ("iters", ctypes.c_int32),
+                ("vsmooth", ctypes.c_int32), ("v_format", ctypes.c_int32), ("out_fp32", ctypes.c_int32),
+                ("softmax_scale", ctypes.c_float), ("beta", ctypes.c_float)]
+
+
+_lib = None
+_P = ctypes.c_void_p
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"libvcattn.so not built ({LIB_PATH}); run __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        cfgp = ctypes.POINTER(VcConfig)
+        L.vc_prepare_workspace_bytes.argtypes = [cfgp]
+        L.vc_prepare_workspace_bytes.restype = ctypes.c_size_t
+        L.vc_attention_workspace_bytes.argtypes = [cfgp]
+        L.vc_attention_workspace_bytes.restype = ctypes.c_size_t
+        L.vsmooth_prepare.argtypes = [cfgp, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+        L.vsmooth_prepare.restype = ctypes.c_int
+        L.vc_attn_fwd.argtypes = [cfgp, _P, _P, _P, _P, _P, _P, _P, _P]
+        L.vc_attn_fwd.restype = ctypes.c_int
+        L.vc_attention.argtypes = [cfgp, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+        L.vc_attention.restype = ctypes.c_int
+        L.vc_status_str.argtypes = [ctypes.c_int]
+        L.vc_status_str.restype = ctypes.c_char_p
+        L.vc_last_error.argtypes = []
+        L.vc_last_error.restype = ctypes.c_char_p
+        L.vc_dbg_expcast.argtypes = [_P, _P, _P, ctypes.c_int64, _P, _P]
+        L.vc_dbg_expcast.restype = ctypes.c_int
+        L.vc_dbg_kmeans_assign.argtypes = [cfgp, _P, _P, _P, _P, ctypes.c_size_t, _P]
+        L.vc_dbg_kmeans_assign.restype = ctypes.c_int
+        L.vc_dbg_sort.argtypes = [cfgp, _P, _P, _P, ctypes.c_size_t, _P]
+        L.vc_dbg_sort.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+class VcError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        L = lib()
+        super().__init__(f"{what}: {L.vc_status_str(status).decode()} ({status}): {L.vc_last_error().decode()}")
+        self.status = status
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        raise VcError(status, what)
+
+
+def make_config(B: int, H: int, N: int, d: int, kv_block: int, n_clusters: int = 1, iters: int = 1,
+                vsmooth: bool = True, v_format: int = E4M3, out_fp32: bool = False,
+                softmax_scale: float = 0.0, beta: float = DEFAULT_BETA) -> VcConfig:
+    return VcConfig(B, H, N, d, kv_block, n_clusters, iters, int(bool(vsmooth)), int(v_format),
+                    int(bool(out_fp32)), softmax_scale, beta)
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _need(t: torch.Tensor, dtype, shape, name: str):
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def workspace_bytes(cfg: VcConfig, attention: bool = False) -> int:
+    f = lib().vc_attention_workspace_bytes if attention else lib().vc_prepare_workspace_bytes
+    n = f(ctypes.byref(cfg))
+    if n == 0:
+        raise VcError(-1, "workspace_bytes")
+    return n
+
+
+def _nblk(cfg):
+    return (cfg.N + cfg.kv_block - 1) // cfg.kv_block
+
+
+@dataclasses.dataclass
+class Prepared:
+    """Blocked K/V as written by vsmooth_prepare (layouts in include/vcattn.h)."""
+    Kq: torch.Tensor
+    k_scale: torch.Tensor
+    Vres: torch.Tensor
+    v_scale: torch.Tensor
+    v_mean: torch.Tensor
+    perm: torch.Tensor
+    labels: torch.Tensor | None
+
+
+def alloc_prepared(cfg: VcConfig, device="cuda", with_labels: bool = True) -> Prepared:
+    B, H, N, d, kvb = cfg.B, cfg.H, cfg.N, cfg.d, cfg.kv_block
+    nblk = _nblk(cfg)
+    Np = nblk * kvb
+    u8 = dict(dtype=torch.uint8, device=device)
+    Vres = torch.empty((B, H, Np // 64, d, 64 if cfg.v_format == E4M3 else 32), **u8)
+    v_scale = (torch.empty((B, H, d), dtype=torch.float32, device=device) if cfg.v_format == E4M3
+               else torch.empty((B, H, Np // 32, d), **u8))
+    return Prepared(
+        Kq=torch.empty((B, H, Np, d), **u8),
+        k_scale=torch.empty((B, H, nblk), dtype=torch.float32, device=device),
+        Vres=Vres, v_scale=v_scale,
+        v_mean=torch.empty((B, H, nblk, d), dtype=torch.float32, device=device),
+        perm=torch.empty((B, H, N), dtype=torch.int32, device=device),
+        labels=torch.empty((B, H, N), dtype=torch.int32, device=device) if with_labels else None)
+
+
+def vsmooth_prepare(cfg: VcConfig, K: torch.Tensor, V: torch.Tensor, init_idx: torch.Tensor | None,
+                    out: Prepared | None = None, ws: torch.Tensor | None = None,
+                    with_labels: bool = True) -> Prepared:
+    shp = (cfg.B, cfg.H, cfg.N, cfg.d)
+    _need(K, torch.bfloat16, shp, "K")
+    _need(V, torch.bfloat16, shp, "V")
+    if cfg.vsmooth:
+        _need(init_idx, torch.int32, (cfg.B, cfg.H, cfg.n_clusters), "init_idx")
+    out = out or alloc_prepared(cfg, K.device, with_labels)
+    nbytes = workspace_bytes(cfg)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=K.device)
+    _check(lib().vsmooth_prepare(ctypes.byref(cfg), _ptr(K), _ptr(V), _ptr(init_idx) if cfg.vsmooth else None,
+                                 _ptr(out.Kq), _ptr(out.k_scale), _ptr(out.Vres), _ptr(out.v_scale),
+                                 _ptr(out.v_mean), _ptr(out.perm), _ptr(out.labels), _ptr(ws), ws.numel(),
+                                 _stream()), "vsmooth_prepare")
+    return out
+
+
+def alloc_out(cfg: VcConfig, device="cuda") -> torch.Tensor:
+    return torch.empty((cfg.B, cfg.H, cfg.N, cfg.d), device=device,
+                       dtype=torch.float32 if cfg.out_fp32 else torch.bfloat16)
+
+
+def vc_attn_fwd(cfg: VcConfig, Q: torch.Tensor, prep: Prepared, out: torch.Tensor | None = None) -> torch.Tensor:
+    _need(Q, torch.bfloat16, (cfg.B, cfg.H, cfg.N, cfg.d), "Q")
+    out = alloc_out(cfg, Q.device) if out is None else out
+    _check(lib().vc_attn_fwd(ctypes.byref(cfg), _ptr(Q), _ptr(prep.Kq), _ptr(prep.k_scale), _ptr(prep.Vres),
+                             _ptr(prep.v_scale), _ptr(prep.v_mean), _ptr(out), _stream()), "vc_attn_fwd")
+    return out
+
+
+def vc_attention(cfg: VcConfig, Q, K, V, init_idx, out=None, ws=None) -> torch.Tensor:
+    shp = (cfg.B, cfg.H, cfg.N, cfg.d)
+    for t, n in ((Q, "Q"), (K, "K"), (V, "V")):
+        _need(t, torch.bfloat16, shp, n)
+    if cfg.vsmooth:
+        _need(init_idx, torch.int32, (cfg.B, cfg.H, cfg.n_clusters), "init_idx")
+    out = alloc_out(cfg, Q.device) if out is None else out
+    nbytes = workspace_bytes(cfg, attention=True)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=Q.device)
+    _check(lib().vc_attention(ctypes.byref(cfg), _ptr(Q), _ptr(K), _ptr(V),
+                              _ptr(init_idx) if cfg.vsmooth else None, _ptr(out), _ptr(ws), ws.numel(),
+                              _stream()), "vc_attention")
+    return out
+
+
+def dbg_expcast(S: torch.Tensor, A: torch.Tensor, B: torch.Tensor) -> torch.Tensor:
+    for t, n in ((S, "S"), (A, "A"), (B, "B")):
+        _need(t, torch.float32, S.shape, n)
+    out = torch.empty(S.shape, dtype=torch.uint8, device=S.device)
+    _check(lib().vc_dbg_expcast(_ptr(S), _ptr(A), _ptr(B), S.numel(), _ptr(out), _stream()), "vc_dbg_expcast")
+    return out
+
+
+def dbg_kmeans_assign(cfg: VcConfig, V: torch.Tensor, C: torch.Tensor) -> torch.Tensor:
+    _need(V, torch.bfloat16, (cfg.B, cfg.H, cfg.N, cfg.d), "V")
+    _need(C, torch.float32, (cfg.B, cfg.H, cfg.n_clusters, cfg.d), "C")
+    labels = torch.empty((cfg.B, cfg.H, cfg.N), dtype=torch.int32, device=V.device)
+    c2 = VcConfig.from_buffer_copy(cfg)
+    c2.vsmooth = 1
+    ws = torch.empty(workspace_bytes(c2), dtype=torch.uint8, device=V.device)
+    _check(lib().vc_dbg_kmeans_assign(ctypes.byref(cfg), _ptr(V), _ptr(C), _ptr(labels), _ptr(ws), ws.numel(),
+                                      _stream()), "vc_dbg_kmeans_assign")
+    return labels
+
+
+def dbg_sort(cfg: VcConfig, labels: torch.Tensor) -> torch.Tensor:
+    _need(labels, torch.int32, (cfg.B, cfg.H, cfg.N), "labels")
+    perm = torch.empty_like(labels)
+    c2 = VcConfig.from_buffer_copy(cfg)
+    c2.vsmooth = 1
+    ws = torch.empty(workspace_bytes(c2), dtype=torch.uint8, device=labels.device)
+    _check(lib().vc_dbg_sort(ctypes.byref(cfg), _ptr(labels), _ptr(perm), _ptr(ws), ws.numel(), _stream()),
+           "vc_dbg_sort")
+    return perm

@@ -1,0 +1,321 @@
+// Host side of libvcattn: argument validation, workspace layout and the launch
+// sequence of the VC-Attention forward pass.  Every check runs before the
+// first launch; the library allocates nothing and never synchronises.
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/vcattn.h"
+#include "vc_internal.hpp"
+
+namespace {
+
+thread_local std::string g_err;
+
+vc_status fail(vc_status s, const std::string& msg) {
+  g_err = msg;
+  return s;
+}
+
+vc_status hip_fail(hipError_t e, const char* where) {
+  g_err = std::string(where) + ": " + hipGetErrorString(e);
+  return VC_ERR_HIP;
+}
+
+bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+struct Dims {
+  int B, H, N, d, kvb, k, kpad, iters, nblk, nstat, nsort;
+  size_t BH;
+};
+
+vc_status validate(const vc_config* c, bool need_kmeans, Dims* out) {
+  if (!c) return fail(VC_ERR_INVALID_ARG, "cfg is NULL");
+  if (c->B < 1 || c->H < 1 || c->N < 1) return fail(VC_ERR_INVALID_ARG, "B, H and N must be >= 1");
+  if (static_cast<int64_t>(c->B) * c->H > 65535) return fail(VC_ERR_UNSUPPORTED, "B*H must be <= 65535");
+  if (c->N > (1 << 26)) return fail(VC_ERR_UNSUPPORTED, "N must be <= 2^26");
+  if (c->d != 64 && c->d != 128) return fail(VC_ERR_UNSUPPORTED, "d must be 64 or 128");
+  if (c->kv_block != 64 && c->kv_block != 128) return fail(VC_ERR_UNSUPPORTED, "kv_block must be 64 or 128");
+  if (c->vsmooth != 0 && c->vsmooth != 1) return fail(VC_ERR_INVALID_ARG, "vsmooth must be 0 or 1");
+  if (c->v_format != 0 && c->v_format != 1) return fail(VC_ERR_UNSUPPORTED, "v_format must be 0 (E4M3) or 1 (MXFP4)");
+  if (c->out_fp32 != 0 && c->out_fp32 != 1) return fail(VC_ERR_INVALID_ARG, "out_fp32 must be 0 or 1");
+  if (!(std::isfinite(c->softmax_scale) && c->softmax_scale >= 0.0f))
+    return fail(VC_ERR_INVALID_ARG, "softmax_scale must be finite and >= 0");
+  if (!(c->beta >= -0.5f && c->beta <= 0.45f)) return fail(VC_ERR_INVALID_ARG, "beta must lie in [-0.5, 0.45]");
+  if (need_kmeans) {
+    if (c->n_clusters < 1 || c->n_clusters > c->N || c->n_clusters > vc::kMaxClusters)
+      return fail(VC_ERR_INVALID_ARG, "n_clusters must lie in [1, min(N, 4096)]");
+    if (c->iters < 1 || c->iters > 16) return fail(VC_ERR_INVALID_ARG, "iters must lie in [1, 16]");
+  }
+  Dims& D = *out;
+  D.B = c->B; D.H = c->H; D.N = c->N; D.d = c->d; D.kvb = c->kv_block;
+  D.k = need_kmeans ? c->n_clusters : 1;
+  D.kpad = (D.k + 31) / 32 * 32;
+  D.iters = c->iters;
+  D.nblk = (c->N + c->kv_block - 1) / c->kv_block;
+  D.nstat = (c->N + 1023) / 1024;
+  D.nsort = (c->N + vc::kSortChunk - 1) / vc::kSortChunk;
+  D.BH = static_cast<size_t>(c->B) * c->H;
+  return VC_OK;
+}
+
+// Carves 256-byte aligned sub-buffers out of a workspace (base == nullptr
+// only measures).
+struct Carver {
+  char* base;
+  size_t off = 0;
+  explicit Carver(void* b) : base(static_cast<char*>(b)) {}
+  template <typename T>
+  T* take(size_t count) {
+    off = (off + 255) & ~static_cast<size_t>(255);
+    T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+    off += count * sizeof(T);
+    return p;
+  }
+};
+
+void carve_prep(Carver& cv, const Dims& D, vc::PrepArgs& a) {
+  const size_t BH = D.BH;
+  a.vamax = cv.take<uint32_t>(BH);
+  a.sV = cv.take<float>(BH);
+  a.kpart = cv.take<double>(BH * D.nstat * D.d);
+  a.mu = cv.take<float>(BH * D.d);
+  a.vramax = cv.take<uint32_t>(BH * D.d);
+  a.Vq = cv.take<int8_t>(BH * D.N * D.d);
+  a.C = cv.take<float>(BH * D.k * D.d);
+  a.Cq = cv.take<int8_t>(BH * D.kpad * D.d);
+  a.cn32 = cv.take<int32_t>(BH * D.kpad);
+  a.labels = cv.take<int32_t>(BH * D.N);
+  a.perm_tmp = cv.take<int32_t>(BH * D.N);
+  a.hist = cv.take<int32_t>(BH * D.nsort * D.k);
+  a.counts = cv.take<int32_t>(BH * D.k);
+  a.starts = cv.take<int32_t>(BH * D.k);
+}
+
+struct OutSizes {
+  size_t kq, ks, vres, vsc_bytes, vmean, perm;
+};
+
+OutSizes out_sizes(const Dims& D, int v_format) {
+  const size_t Np = static_cast<size_t>(D.nblk) * D.kvb;
+  OutSizes s;
+  s.kq = D.BH * Np * D.d;
+  s.ks = D.BH * D.nblk;
+  s.vres = D.BH * Np * D.d / (v_format == 0 ? 1 : 2);
+  s.vsc_bytes = v_format == 0 ? D.BH * D.d * sizeof(float) : D.BH * (Np / 32) * D.d;
+  s.vmean = D.BH * D.nblk * D.d;
+  s.perm = D.BH * D.N;
+  return s;
+}
+
+void fill_prep_args(const vc_config* c, const Dims& D, const void* K, const void* V, vc::PrepArgs& a) {
+  a.B = D.B; a.H = D.H; a.N = D.N; a.d = D.d; a.kvb = D.kvb; a.k = D.k; a.kpad = D.kpad;
+  a.iters = D.iters; a.vsmooth = c->vsmooth; a.v_format = c->v_format;
+  a.nblk = D.nblk; a.nstat = D.nstat; a.nsort = D.nsort;
+  a.K = static_cast<const uint16_t*>(K);
+  a.V = static_cast<const uint16_t*>(V);
+}
+
+#define VC_TRY(expr, where)                    \
+  do {                                         \
+    hipError_t e_ = (expr);                    \
+    if (e_ != hipSuccess) return hip_fail(e_, where); \
+  } while (0)
+
+vc_status run_prepare(const vc_config* c, const Dims& D, vc::PrepArgs& a, const int32_t* init,
+                      const vc::PrepOut& o, int32_t* user_labels, hipStream_t st) {
+  VC_TRY(vc::launch_fill(a.vamax, 0u, D.BH, st), "fill");
+  VC_TRY(vc::launch_fill(a.vramax, 0u, D.BH * D.d, st), "fill");
+  VC_TRY(vc::launch_stats(a, st), "stats");
+  if (c->vsmooth) {
+    VC_TRY(vc::launch_quant_v_i8(a, st), "quant_v_i8");
+    VC_TRY(vc::launch_init_centroids(a, init, st), "init_centroids");
+    for (int it = 0; it < D.iters; ++it) {
+      const bool last = it + 1 == D.iters;
+      int32_t* lab = (last && user_labels) ? user_labels : a.labels;
+      VC_TRY(vc::launch_assign(a, lab, st), "kmeans_assign");
+      if (!last) {
+        VC_TRY(vc::launch_sort(a, lab, a.perm_tmp, st), "sort");
+        VC_TRY(vc::launch_update(a, a.perm_tmp, st), "kmeans_update");
+      } else {
+        VC_TRY(vc::launch_sort(a, lab, o.perm, st), "sort");
+      }
+    }
+  } else {
+    VC_TRY(vc::launch_iota(o.perm, D.N, D.BH * D.N, st), "iota");
+  }
+  VC_TRY(vc::launch_vres_ksmooth(a, o.perm, o, st), "vres_ksmooth");
+  return VC_OK;
+}
+
+void fill_attn_args(const vc_config* c, const Dims& D, vc::AttnArgs& a) {
+  a.B = D.B; a.H = D.H; a.N = D.N; a.d = D.d; a.kvb = D.kvb; a.nblk = D.nblk;
+  a.v_format = c->v_format; a.out_fp32 = c->out_fp32;
+  a.scale = c->softmax_scale == 0.0f ? static_cast<float>(1.0 / std::sqrt(static_cast<double>(D.d)))
+                                     : c->softmax_scale;
+  a.kc = 56.0f + c->beta;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* vc_status_str(vc_status s) {
+  switch (s) {
+    case VC_OK: return "ok";
+    case VC_ERR_INVALID_ARG: return "invalid argument";
+    case VC_ERR_UNSUPPORTED: return "unsupported configuration";
+    case VC_ERR_WORKSPACE: return "workspace too small";
+    case VC_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* vc_last_error(void) { return g_err.c_str(); }
+
+size_t vc_prepare_workspace_bytes(const vc_config* cfg) {
+  Dims D;
+  if (validate(cfg, cfg && cfg->vsmooth, &D) != VC_OK) return 0;
+  Carver cv(nullptr);
+  vc::PrepArgs a{};
+  carve_prep(cv, D, a);
+  return cv.off + 256;
+}
+
+size_t vc_attention_workspace_bytes(const vc_config* cfg) {
+  Dims D;
+  if (validate(cfg, cfg && cfg->vsmooth, &D) != VC_OK) return 0;
+  Carver cv(nullptr);
+  vc::PrepArgs a{};
+  carve_prep(cv, D, a);
+  const OutSizes s = out_sizes(D, cfg->v_format);
+  cv.take<uint8_t>(s.kq);
+  cv.take<float>(s.ks);
+  cv.take<uint8_t>(s.vres);
+  cv.take<uint8_t>(s.vsc_bytes);
+  cv.take<float>(s.vmean);
+  cv.take<int32_t>(s.perm);
+  return cv.off + 256;
+}
+
+vc_status vsmooth_prepare(const vc_config* cfg, const void* K, const void* V, const int32_t* init_idx,
+                          uint8_t* Kq, float* k_scale, uint8_t* Vres, void* v_scale, float* v_mean,
+                          int32_t* perm, int32_t* labels, void* ws, size_t ws_bytes, hipStream_t stream) {
+  g_err.clear();
+  Dims D;
+  if (vc_status s = validate(cfg, cfg && cfg->vsmooth, &D)) return s;
+  if (!K || !V || !Kq || !k_scale || !Vres || !v_scale || !v_mean || !perm || !ws)
+    return fail(VC_ERR_INVALID_ARG, "required pointer is NULL");
+  if (cfg->vsmooth && !init_idx) return fail(VC_ERR_INVALID_ARG, "init_idx is NULL with vsmooth on");
+  if (misaligned(K) || misaligned(V) || misaligned(Kq) || misaligned(Vres) || misaligned(v_scale) ||
+      misaligned(v_mean) || misaligned(ws))
+    return fail(VC_ERR_INVALID_ARG, "tensors and workspace must be 16-byte aligned");
+  if (ws_bytes < vc_prepare_workspace_bytes(cfg)) return fail(VC_ERR_WORKSPACE, "workspace too small");
+  vc::PrepArgs a{};
+  fill_prep_args(cfg, D, K, V, a);
+  Carver cv(reinterpret_cast<void*>((reinterpret_cast<uintptr_t>(ws) + 255) & ~static_cast<uintptr_t>(255)));
+  carve_prep(cv, D, a);
+  vc::PrepOut o{Kq, k_scale, Vres, v_scale, v_mean, perm};
+  return run_prepare(cfg, D, a, init_idx, o, labels, stream);
+}
+
+vc_status vc_attn_fwd(const vc_config* cfg, const void* Q, const uint8_t* Kq, const float* k_scale,
+                      const uint8_t* Vres, const void* v_scale, const float* v_mean, void* O,
+                      hipStream_t stream) {
+  g_err.clear();
+  Dims D;
+  if (vc_status s = validate(cfg, false, &D)) return s;
+  if (!Q || !Kq || !k_scale || !Vres || !v_scale || !v_mean || !O)
+    return fail(VC_ERR_INVALID_ARG, "required pointer is NULL");
+  if (misaligned(Q) || misaligned(Kq) || misaligned(Vres) || misaligned(v_scale) || misaligned(v_mean) ||
+      misaligned(O))
+    return fail(VC_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
+  vc::AttnArgs a{};
+  fill_attn_args(cfg, D, a);
+  a.Q = static_cast<const uint16_t*>(Q);
+  a.Kq = Kq; a.k_scale = k_scale; a.Vres = Vres; a.v_scale = v_scale; a.v_mean = v_mean; a.O = O;
+  VC_TRY(vc::launch_attn(a, stream), "attn_fwd");
+  return VC_OK;
+}
+
+vc_status vc_attention(const vc_config* cfg, const void* Q, const void* K, const void* V,
+                       const int32_t* init_idx, void* O, void* ws, size_t ws_bytes, hipStream_t stream) {
+  g_err.clear();
+  Dims D;
+  if (vc_status s = validate(cfg, cfg && cfg->vsmooth, &D)) return s;
+  if (!Q || !K || !V || !O || !ws) return fail(VC_ERR_INVALID_ARG, "required pointer is NULL");
+  if (cfg->vsmooth && !init_idx) return fail(VC_ERR_INVALID_ARG, "init_idx is NULL with vsmooth on");
+  if (misaligned(Q) || misaligned(K) || misaligned(V) || misaligned(O) || misaligned(ws))
+    return fail(VC_ERR_INVALID_ARG, "tensors and workspace must be 16-byte aligned");
+  if (ws_bytes < vc_attention_workspace_bytes(cfg)) return fail(VC_ERR_WORKSPACE, "workspace too small");
+  vc::PrepArgs a{};
+  fill_prep_args(cfg, D, K, V, a);
+  Carver cv(reinterpret_cast<void*>((reinterpret_cast<uintptr_t>(ws) + 255) & ~static_cast<uintptr_t>(255)));
+  carve_prep(cv, D, a);
+  const OutSizes s = out_sizes(D, cfg->v_format);
+  vc::PrepOut o;
+  o.Kq = cv.take<uint8_t>(s.kq);
+  o.k_scale = cv.take<float>(s.ks);
+  o.Vres = cv.take<uint8_t>(s.vres);
+  o.v_scale = cv.take<uint8_t>(s.vsc_bytes);
+  o.v_mean = cv.take<float>(s.vmean);
+  o.perm = cv.take<int32_t>(s.perm);
+  if (vc_status st = run_prepare(cfg, D, a, init_idx, o, nullptr, stream)) return st;
+  vc::AttnArgs at{};
+  fill_attn_args(cfg, D, at);
+  at.Q = static_cast<const uint16_t*>(Q);
+  at.Kq = o.Kq; at.k_scale = o.k_scale; at.Vres = o.Vres; at.v_scale = o.v_scale; at.v_mean = o.v_mean; at.O = O;
+  VC_TRY(vc::launch_attn(at, stream), "attn_fwd");
+  return VC_OK;
+}
+
+vc_status vc_dbg_expcast(const float* S, const float* A, const float* B, int64_t n, uint8_t* out,
+                         hipStream_t stream) {
+  g_err.clear();
+  if (n < 0) return fail(VC_ERR_INVALID_ARG, "n must be >= 0");
+  if (n > 0 && (!S || !A || !B || !out)) return fail(VC_ERR_INVALID_ARG, "required pointer is NULL");
+  VC_TRY(vc::launch_dbg_expcast(S, A, B, n, out, stream), "dbg_expcast");
+  return VC_OK;
+}
+
+vc_status vc_dbg_kmeans_assign(const vc_config* cfg, const void* V, const float* C, int32_t* labels, void* ws,
+                               size_t ws_bytes, hipStream_t stream) {
+  g_err.clear();
+  Dims D;
+  if (vc_status s = validate(cfg, true, &D)) return s;
+  if (!V || !C || !labels || !ws) return fail(VC_ERR_INVALID_ARG, "required pointer is NULL");
+  if (misaligned(V) || misaligned(ws)) return fail(VC_ERR_INVALID_ARG, "V and workspace must be 16-byte aligned");
+  vc_config c2 = *cfg;
+  c2.vsmooth = 1;
+  if (ws_bytes < vc_prepare_workspace_bytes(&c2)) return fail(VC_ERR_WORKSPACE, "workspace too small");
+  vc::PrepArgs a{};
+  fill_prep_args(&c2, D, V, V, a);
+  Carver cv(reinterpret_cast<void*>((reinterpret_cast<uintptr_t>(ws) + 255) & ~static_cast<uintptr_t>(255)));
+  carve_prep(cv, D, a);
+  a.C = const_cast<float*>(C);
+  VC_TRY(vc::launch_fill(a.vamax, 0u, D.BH, stream), "fill");
+  VC_TRY(vc::launch_stats(a, stream), "stats");
+  VC_TRY(vc::launch_quant_v_i8(a, stream), "quant_v_i8");
+  VC_TRY(vc::launch_assign(a, labels, stream), "kmeans_assign");
+  return VC_OK;
+}
+
+vc_status vc_dbg_sort(const vc_config* cfg, const int32_t* labels, int32_t* perm, void* ws, size_t ws_bytes,
+                      hipStream_t stream) {
+  g_err.clear();
+  Dims D;
+  if (vc_status s = validate(cfg, true, &D)) return s;
+  if (!labels || !perm || !ws) return fail(VC_ERR_INVALID_ARG, "required pointer is NULL");
+  vc_config c2 = *cfg;
+  c2.vsmooth = 1;
+  if (ws_bytes < vc_prepare_workspace_bytes(&c2)) return fail(VC_ERR_WORKSPACE, "workspace too small");
+  vc::PrepArgs a{};
+  fill_prep_args(&c2, D, nullptr, nullptr, a);
+  Carver cv(reinterpret_cast<void*>((reinterpret_cast<uintptr_t>(ws) + 255) & ~static_cast<uintptr_t>(255)));
+  carve_prep(cv, D, a);
+  VC_TRY(vc::launch_sort(a, labels, perm, stream), "sort");
+  return VC_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,584 @@
+// V-Smooth preparation kernels for gfx950: statistics, int8 k-means on the
+// matrix cores, stable counting sort into fixed blocks, block means with
+// per-channel E4M3 (or MXFP4) residuals, and K smoothing with per-block E4M3.
+//
+// Method: chooseai.io brief on VC-Attention, section "V-Smooth" (cluster
+// similar value tokens into one hardware block, subtract the block mean kept
+// in high precision, quantise only the residual); zerohour.day summary, key
+// facts (per-channel E4M3/NVFP4 residuals after block-mean subtraction).
+// Every sum that feeds a stored value is formed in fp64 in a fixed order, so
+// runs are deterministic.
+#include "vc_internal.hpp"
+
+namespace vc {
+
+constexpr int kStatChunk = 1024;   // tokens per partial-sum chunk
+
+__global__ void k_fill_u32(uint32_t* __restrict__ p, uint32_t v, size_t n) {
+  size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  for (; i < n; i += static_cast<size_t>(gridDim.x) * blockDim.x) p[i] = v;
+}
+
+// Per chunk of tokens: fp64 per-channel sums of K (for its mean) and the
+// max |V| of the head (for the int8 k-means scale) and max |V| per channel.
+template <int D>
+__global__ __launch_bounds__(256) void k_stats_partial(const uint16_t* __restrict__ K,
+                                                       const uint16_t* __restrict__ V, int N,
+                                                       int nch, double* __restrict__ kpart,
+                                                       uint32_t* __restrict__ vamax) {
+  constexpr int SUB = 256 / D;
+  __shared__ double sK[256];
+  __shared__ float sMax[4];
+  const int bh = blockIdx.y, ch = blockIdx.x;
+  const int c = threadIdx.x % D, sub = threadIdx.x / D;
+  const size_t base = static_cast<size_t>(bh) * N * D;
+  const int t0 = ch * kStatChunk, t1 = min(N, t0 + kStatChunk);
+  double ks = 0.0;
+  float vm = 0.0f;
+  for (int t = t0 + sub; t < t1; t += SUB) {
+    const size_t o = base + static_cast<size_t>(t) * D + c;
+    ks += static_cast<double>(bf16_to_f32(K[o]));
+    vm = fmaxf(vm, fabsf(bf16_to_f32(V[o])));
+  }
+  sK[threadIdx.x] = ks;
+  vm = wave_max(vm);
+  if ((threadIdx.x & 63) == 0) sMax[threadIdx.x >> 6] = vm;
+  __syncthreads();
+  if (threadIdx.x < D) {
+    double s = 0.0;
+    for (int j = 0; j < SUB; ++j) s += sK[j * D + threadIdx.x];
+    kpart[(static_cast<size_t>(bh) * nch + ch) * D + threadIdx.x] = s;
+  }
+  if (threadIdx.x == 0) {
+    float m = fmaxf(fmaxf(sMax[0], sMax[1]), fmaxf(sMax[2], sMax[3]));
+    atomicMax(vamax + bh, __float_as_uint(m));
+  }
+}
+
+// mu_K = fp32(sum / N) per channel; sV = fp32(max|V| / 127) (1 if V == 0).
+template <int D>
+__global__ void k_stats_final(const double* __restrict__ kpart, const uint32_t* __restrict__ vamax,
+                              int N, int nch, float* __restrict__ mu, float* __restrict__ sV) {
+  const int bh = blockIdx.x, c = threadIdx.x;
+  double s = 0.0;
+  for (int ch = 0; ch < nch; ++ch) s += kpart[(static_cast<size_t>(bh) * nch + ch) * D + c];
+  mu[static_cast<size_t>(bh) * D + c] = static_cast<float>(s / static_cast<double>(N));
+  if (c == 0) {
+    const float a = __uint_as_float(vamax[bh]);
+    sV[bh] = a > 0.0f ? a / 127.0f : 1.0f;
+  }
+}
+
+// int8 codes of V for the k-means distances, 8 elements per thread.
+__global__ void k_quant_v_i8(const uint16_t* __restrict__ V, const float* __restrict__ sV,
+                             size_t per_head, size_t total, int8_t* __restrict__ Vq) {
+  const size_t i8 = (static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x) * 8;
+  if (i8 >= total) return;
+  const float s = sV[i8 / per_head];
+  const uint4 raw = *reinterpret_cast<const uint4*>(V + i8);
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+  uint32_t out[2] = {0u, 0u};
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const uint16_t b = static_cast<uint16_t>(w[e >> 1] >> ((e & 1) * 16));
+    const uint32_t q = static_cast<uint32_t>(i8_code(bf16_to_f32(b), s)) & 0xffu;
+    out[e >> 2] |= q << ((e & 3) * 8);
+  }
+  *reinterpret_cast<uint2*>(Vq + i8) = make_uint2(out[0], out[1]);
+}
+
+template <int D>
+__global__ void k_init_centroids(const uint16_t* __restrict__ V, const int32_t* __restrict__ init,
+                                 int N, int k, float* __restrict__ C) {
+  const int bh = blockIdx.y, i = blockIdx.x, c = threadIdx.x;
+  const int tok = init[static_cast<size_t>(bh) * k + i];
+  C[(static_cast<size_t>(bh) * k + i) * D + c] =
+      bf16_to_f32(V[(static_cast<size_t>(bh) * N + tok) * D + c]);
+}
+
+// int8 centroid codes and the packed distance offsets cn32 = 32*|c|^2 + (row % 32);
+// rows k..kpad-1 are padding (codes 0, offset INT_MAX: never the minimum).
+template <int D>
+__global__ __launch_bounds__(256) void k_quant_centroids(const float* __restrict__ C,
+                                                         const float* __restrict__ sV, int k,
+                                                         int kpad, int8_t* __restrict__ Cq,
+                                                         int32_t* __restrict__ cn32) {
+  constexpr int PER = D / 64;
+  const int bh = blockIdx.y;
+  const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (i >= kpad) return;
+  const float s = sV[bh];
+  int32_t sq = 0;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    const int c = lane * PER + e;
+    int32_t q = 0;
+    if (i < k) q = i8_code(C[(static_cast<size_t>(bh) * k + i) * D + c], s);
+    Cq[(static_cast<size_t>(bh) * kpad + i) * D + c] = static_cast<int8_t>(q);
+    sq += q * q;
+  }
+  for (int o = 32; o > 0; o >>= 1) sq += __shfl_xor(sq, o, 64);
+  if (lane == 0)
+    cn32[static_cast<size_t>(bh) * kpad + i] = i < k ? sq * 32 + (i & 31) : 0x7fffffff;
+}
+
+// One assignment pass: label = argmin_c (|c_q|^2 - 2 v_q.c_q), lowest index on
+// ties.  C^T = Cq . Vq^T runs on v_mfma_i32_32x32x32_i8 (exact int32); each
+// lane folds its 16 accumulator rows of a 32-centroid tile into keys
+// 32*D + row-in-tile (min = lowest distance, then lowest row), keeps a tile's
+// minimum only if its distance is strictly lower than the best so far, and
+// the two lane halves that share a token column are merged on (D, index).
+// A workgroup covers 256 tokens (4 waves x 2 column tiles of 32); centroids
+// stream through LDS in chunks of 128.
+template <int D>
+__global__ __launch_bounds__(256) void k_kmeans_assign(const int8_t* __restrict__ Vq,
+                                                       const int8_t* __restrict__ Cq,
+                                                       const int32_t* __restrict__ cn32, int N,
+                                                       int kpad, int32_t* __restrict__ labels) {
+  constexpr int NDC = D / 32;
+  constexpr int CSTR = D + 16;
+  constexpr int CCH = 128;
+  __shared__ __attribute__((aligned(16))) int8_t sC[CCH * CSTR];
+  __shared__ __attribute__((aligned(16))) int32_t sCn[CCH];
+  const int bh = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 5, col = lane & 31;
+  const int8_t* vq = Vq + static_cast<size_t>(bh) * N * D;
+  const int8_t* cq = Cq + static_cast<size_t>(bh) * kpad * D;
+  const int32_t* cn = cn32 + static_cast<size_t>(bh) * kpad;
+  const int tok0 = blockIdx.x * 256 + wave * 64;
+
+  v4i bop[2][NDC];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int tok = tok0 + j * 32 + col;
+#pragma unroll
+    for (int c = 0; c < NDC; ++c) {
+      if (tok < N)
+        bop[j][c] = *reinterpret_cast<const v4i*>(vq + static_cast<size_t>(tok) * D + 32 * c + 16 * g);
+      else
+        bop[j][c] = v4i{0, 0, 0, 0};
+    }
+  }
+  int best[2] = {0x7fffffff, 0x7fffffff};
+  int btile[2] = {0, 0};
+  for (int c0 = 0; c0 < kpad; c0 += CCH) {
+    const int rows = min(CCH, kpad - c0);
+    __syncthreads();
+    for (int p = threadIdx.x; p < rows * (D / 16); p += 256) {
+      const int r = p / (D / 16), q16 = p % (D / 16);
+      *reinterpret_cast<uint4*>(sC + r * CSTR + q16 * 16) =
+          *reinterpret_cast<const uint4*>(cq + static_cast<size_t>(c0 + r) * D + q16 * 16);
+    }
+    for (int r = threadIdx.x; r < rows; r += 256) sCn[r] = cn[c0 + r];
+    __syncthreads();
+    for (int tile = 0; tile < rows / 32; ++tile) {
+      v4i a[NDC];
+#pragma unroll
+      for (int c = 0; c < NDC; ++c)
+        a[c] = *reinterpret_cast<const v4i*>(sC + (tile * 32 + col) * CSTR + 32 * c + 16 * g);
+      int32_t off[16];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int4 o4 = *reinterpret_cast<const int4*>(sCn + tile * 32 + 8 * i + 4 * g);
+        off[4 * i + 0] = o4.x; off[4 * i + 1] = o4.y; off[4 * i + 2] = o4.z; off[4 * i + 3] = o4.w;
+      }
+      const int gt = c0 / 32 + tile;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        v16i acc = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+        for (int c = 0; c < NDC; ++c)
+          acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[c], bop[j][c], acc, 0, 0, 0);
+        int tmin = 0x7fffffff;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) tmin = min(tmin, off[r] - 64 * acc[r]);
+        // tiles arrive in increasing index order: a later tile must win on
+        // distance alone (the packed row only orders rows inside one tile)
+        if ((tmin >> 5) < (best[j] >> 5)) { best[j] = tmin; btile[j] = gt; }
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int dist = best[j] >> 5;
+    const int idx = btile[j] * 32 + (best[j] & 31);
+    const int pd = __shfl_xor(dist, 32, 64);
+    const int pi = __shfl_xor(idx, 32, 64);
+    const int lab = (pd < dist || (pd == dist && pi < idx)) ? pi : idx;
+    const int tok = tok0 + j * 32 + col;
+    if (g == 0 && tok < N) labels[static_cast<size_t>(bh) * N + tok] = lab;
+  }
+}
+
+// ---- stable counting sort by label ------------------------------------------------
+__global__ __launch_bounds__(256) void k_sort_hist(const int32_t* __restrict__ labels, int N, int k,
+                                                   int nch, int32_t* __restrict__ hist) {
+  __shared__ int32_t cnt[kMaxClusters];
+  const int bh = blockIdx.y, ch = blockIdx.x;
+  for (int i = threadIdx.x; i < k; i += 256) cnt[i] = 0;
+  __syncthreads();
+  const int t0 = ch * kSortChunk, t1 = min(N, t0 + kSortChunk);
+  for (int t = t0 + threadIdx.x; t < t1; t += 256) {
+    const int L = labels[static_cast<size_t>(bh) * N + t];
+    if (static_cast<unsigned>(L) < static_cast<unsigned>(k)) atomicAdd(&cnt[L], 1);
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < k; i += 256)
+    hist[(static_cast<size_t>(bh) * nch + ch) * k + i] = cnt[i];
+}
+
+// hist[ch][L] <- first sorted position of chunk ch's tokens with label L;
+// counts[L] = cluster size, starts[L] = first sorted position of cluster L.
+__global__ __launch_bounds__(1024) void k_sort_scan(int32_t* __restrict__ hist, int k, int nch,
+                                                    int32_t* __restrict__ counts,
+                                                    int32_t* __restrict__ starts) {
+  __shared__ int32_t part[1024];
+  const int bh = blockIdx.x;
+  int32_t* h = hist + static_cast<size_t>(bh) * nch * k;
+  constexpr int PER = kMaxClusters / 1024;
+  int tot[PER];
+  int mysum = 0;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    const int L = threadIdx.x * PER + e;
+    int run = 0;
+    if (L < k) {
+      for (int ch = 0; ch < nch; ++ch) {
+        const int v = h[static_cast<size_t>(ch) * k + L];
+        h[static_cast<size_t>(ch) * k + L] = run;
+        run += v;
+      }
+    }
+    tot[e] = run;
+    mysum += run;
+  }
+  part[threadIdx.x] = mysum;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {         // inclusive Hillis-Steele scan
+    const int v = threadIdx.x >= o ? part[threadIdx.x - o] : 0;
+    __syncthreads();
+    part[threadIdx.x] += v;
+    __syncthreads();
+  }
+  int run = part[threadIdx.x] - mysum;         // exclusive prefix of this thread
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    const int L = threadIdx.x * PER + e;
+    if (L < k) {
+      counts[static_cast<size_t>(bh) * k + L] = tot[e];
+      starts[static_cast<size_t>(bh) * k + L] = run;
+      for (int ch = 0; ch < nch; ++ch) h[static_cast<size_t>(ch) * k + L] += run;
+    }
+    run += tot[e];
+  }
+}
+
+// Tokens of a chunk are placed in token order: each round of 256 tokens ranks
+// every token among equal labels of the round, then advances the per-label base.
+__global__ __launch_bounds__(256) void k_sort_scatter(const int32_t* __restrict__ labels,
+                                                      const int32_t* __restrict__ hist, int N,
+                                                      int k, int nch, int32_t* __restrict__ perm) {
+  __shared__ int32_t base[kMaxClusters];
+  __shared__ int32_t lab[256];
+  const int bh = blockIdx.y, ch = blockIdx.x;
+  for (int i = threadIdx.x; i < k; i += 256)
+    base[i] = hist[(static_cast<size_t>(bh) * nch + ch) * k + i];
+  const int t0 = ch * kSortChunk, t1 = min(N, t0 + kSortChunk);
+  for (int r0 = t0; r0 < t1; r0 += 256) {
+    const int t = r0 + threadIdx.x;
+    int L = t < t1 ? labels[static_cast<size_t>(bh) * N + t] : -1;
+    if (static_cast<unsigned>(L) >= static_cast<unsigned>(k)) L = -1;   // out-of-range labels are dropped
+    __syncthreads();
+    lab[threadIdx.x] = L;
+    __syncthreads();
+    int before = 0, total = 0;
+    for (int j = 0; j < 256; ++j) {
+      const int lj = lab[j];
+      if (lj == L) { ++total; before += j < static_cast<int>(threadIdx.x) ? 1 : 0; }
+    }
+    if (L >= 0) perm[static_cast<size_t>(bh) * N + base[L] + before] = t;
+    __syncthreads();
+    if (L >= 0 && before == total - 1) base[L] += total;
+  }
+}
+
+// New centroid = fp32(fp64 mean of the members' values), summed in sorted
+// (= token) order; an empty cluster keeps its centroid.
+template <int D>
+__global__ void k_kmeans_update(const uint16_t* __restrict__ V, const int32_t* __restrict__ perm,
+                                const int32_t* __restrict__ counts,
+                                const int32_t* __restrict__ starts, int N, int k,
+                                float* __restrict__ C) {
+  const int bh = blockIdx.y, i = blockIdx.x, c = threadIdx.x;
+  const int cnt = counts[static_cast<size_t>(bh) * k + i];
+  if (cnt == 0) return;
+  const int s = starts[static_cast<size_t>(bh) * k + i];
+  const int32_t* pp = perm + static_cast<size_t>(bh) * N + s;
+  const uint16_t* vv = V + static_cast<size_t>(bh) * N * D + c;
+  double sum = 0.0;
+  for (int j = 0; j < cnt; ++j) sum += static_cast<double>(bf16_to_f32(vv[static_cast<size_t>(pp[j]) * D]));
+  C[(static_cast<size_t>(bh) * k + i) * D + c] = static_cast<float>(sum / static_cast<double>(cnt));
+}
+
+__global__ void k_iota(int32_t* __restrict__ perm, int N, size_t total) {
+  size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < total) perm[i] = static_cast<int32_t>(i % N);
+}
+
+// ---- V-Smooth residuals -----------------------------------------------------------
+// Block mean over the block's real tokens (fp64, sorted order) and, for E4M3,
+// the per-channel max |v - mean| of the head.
+template <int D>
+__global__ void k_vblock_stats(const uint16_t* __restrict__ V, const int32_t* __restrict__ perm,
+                               int N, int kvb, int nblk, int vsmooth, int want_amax,
+                               float* __restrict__ v_mean, uint32_t* __restrict__ vramax) {
+  const int bh = blockIdx.y, b = blockIdx.x, c = threadIdx.x;
+  const int p0 = b * kvb, nv = min(kvb, N - p0);
+  const int32_t* pp = perm + static_cast<size_t>(bh) * N + p0;
+  const uint16_t* vv = V + static_cast<size_t>(bh) * N * D + c;
+  float mean = 0.0f;
+  if (vsmooth) {
+    double s = 0.0;
+    for (int j = 0; j < nv; ++j) s += static_cast<double>(bf16_to_f32(vv[static_cast<size_t>(pp[j]) * D]));
+    mean = static_cast<float>(s / static_cast<double>(nv));
+  }
+  v_mean[(static_cast<size_t>(bh) * nblk + b) * D + c] = mean;
+  if (want_amax) {
+    float am = 0.0f;
+    for (int j = 0; j < nv; ++j) {
+      const float r = bf16_to_f32(vv[static_cast<size_t>(pp[j]) * D]) - mean;
+      am = fmaxf(am, fabsf(r));
+    }
+    atomicMax(vramax + static_cast<size_t>(bh) * D + c, __float_as_uint(am));
+  }
+}
+
+// E4M3 residual codes in the [Np/64][d][64] layout with the per-channel scale
+// s_v = fp32(max|r| / 448); position-ordered rows of 64 codes per channel.
+template <int D>
+__global__ __launch_bounds__(256) void k_vres_e4m3(const uint16_t* __restrict__ V,
+                                                   const int32_t* __restrict__ perm,
+                                                   const float* __restrict__ v_mean,
+                                                   const uint32_t* __restrict__ vramax, int N,
+                                                   int kvb, int nblk, uint8_t* __restrict__ Vres,
+                                                   float* __restrict__ v_scale) {
+  const int bh = blockIdx.y, b = blockIdx.x;
+  const int p0 = b * kvb;
+  const int32_t* pp = perm + static_cast<size_t>(bh) * N;
+  const uint16_t* vv = V + static_cast<size_t>(bh) * N * D;
+  const float* mean = v_mean + (static_cast<size_t>(bh) * nblk + b) * D;
+  for (int w = threadIdx.x; w < D * kvb / 4; w += 256) {
+    const int c = w % D, p4 = (w / D) * 4;
+    const float am = __uint_as_float(vramax[static_cast<size_t>(bh) * D + c]);
+    const float s = am > 0.0f ? am / 448.0f : 1.0f;
+    if (b == 0 && p4 == 0) v_scale[static_cast<size_t>(bh) * D + c] = s;
+    const float mc = mean[c];
+    uint32_t word = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int pos = p0 + p4 + e;
+      uint32_t code = 0;
+      if (pos < N) {
+        const float r = bf16_to_f32(vv[static_cast<size_t>(pp[pos]) * D + c]) - mc;
+        code = e4m3_encode(r / s);
+      }
+      word |= code << (8 * e);
+    }
+    const int gpos = p0 + p4;
+    *reinterpret_cast<uint32_t*>(Vres + ((static_cast<size_t>(bh) * (nblk * kvb / 64) + gpos / 64) * D + c) * 64 +
+                                 (gpos & 63)) = word;
+  }
+}
+
+// MXFP4 residuals: per 32 sorted positions x channel, E8M0 exponent
+// floor(log2 amax) - 2 (clamped to [-127, 127]; 0 for an all-zero group) and
+// E2M1 codes of r / 2^e; layout [Np/64][d][32 bytes], even position low nibble.
+template <int D>
+__global__ __launch_bounds__(256) void k_vres_mxfp4(const uint16_t* __restrict__ V,
+                                                    const int32_t* __restrict__ perm,
+                                                    const float* __restrict__ v_mean, int N,
+                                                    int kvb, int nblk, uint8_t* __restrict__ Vres,
+                                                    uint8_t* __restrict__ e8m0) {
+  const int bh = blockIdx.y, b = blockIdx.x;
+  const int p0 = b * kvb;
+  const int32_t* pp = perm + static_cast<size_t>(bh) * N;
+  const uint16_t* vv = V + static_cast<size_t>(bh) * N * D;
+  const float* mean = v_mean + (static_cast<size_t>(bh) * nblk + b) * D;
+  const int ngrp = kvb / 32;
+  for (int w = threadIdx.x; w < D * ngrp; w += 256) {
+    const int c = w % D, grp = w / D;
+    const float mc = mean[c];
+    float r[32];
+    float am = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+      const int pos = p0 + grp * 32 + e;
+      r[e] = pos < N ? bf16_to_f32(vv[static_cast<size_t>(pp[pos]) * D + c]) - mc : 0.0f;
+      am = fmaxf(am, fabsf(r[e]));
+    }
+    int ex = 0;
+    if (am > 0.0f) {
+      int fe;
+      frexpf(am, &fe);                   // am = f * 2^fe, f in [0.5, 1)
+      ex = min(max(fe - 1 - 2, -127), 127);
+    }
+    const int gpos = p0 + grp * 32;
+    e8m0[(static_cast<size_t>(bh) * (nblk * kvb / 32) + gpos / 32) * D + c] = static_cast<uint8_t>(ex + 127);
+    uint32_t words[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 32; ++e) words[e >> 3] |= e2m1_encode(ldexpf(r[e], -ex)) << (4 * (e & 7));
+    *reinterpret_cast<uint4*>(Vres + ((static_cast<size_t>(bh) * (nblk * kvb / 64) + gpos / 64) * D + c) * 32 +
+                              (gpos & 63) / 2) = make_uint4(words[0], words[1], words[2], words[3]);
+  }
+}
+
+// K smoothing: K' = fp32(K - mu_K) gathered in sorted order; per block
+// s_k = fp32(max|K'| / 448); codes stored in k-step row order.
+template <int D, int KVB>
+__global__ __launch_bounds__(256) void k_ksmooth(const uint16_t* __restrict__ K,
+                                                 const int32_t* __restrict__ perm,
+                                                 const float* __restrict__ mu, int N, int nblk,
+                                                 uint8_t* __restrict__ Kq, float* __restrict__ k_scale) {
+  constexpr int TPR = 256 / KVB;      // threads per row
+  constexpr int CPT = D / TPR;        // channels per thread (16, 32 or 64)
+  __shared__ float sMax[4];
+  const int bh = blockIdx.y, b = blockIdx.x;
+  const int row = threadIdx.x / TPR, part = threadIdx.x % TPR;
+  const int pos = b * KVB + row;
+  float x[CPT];
+  float am = 0.0f;
+  if (pos < N) {
+    const int tok = perm[static_cast<size_t>(bh) * N + pos];
+    const uint16_t* kr = K + (static_cast<size_t>(bh) * N + tok) * D + part * CPT;
+    const float* m = mu + static_cast<size_t>(bh) * D + part * CPT;
+#pragma unroll
+    for (int e = 0; e < CPT; ++e) {
+      x[e] = bf16_to_f32(kr[e]) - m[e];
+      am = fmaxf(am, fabsf(x[e]));
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < CPT; ++e) x[e] = 0.0f;
+  }
+  am = wave_max(am);
+  if ((threadIdx.x & 63) == 0) sMax[threadIdx.x >> 6] = am;
+  __syncthreads();
+  const float bm = fmaxf(fmaxf(sMax[0], sMax[1]), fmaxf(sMax[2], sMax[3]));
+  const float s = bm > 0.0f ? bm / 448.0f : 1.0f;
+  if (threadIdx.x == 0) k_scale[static_cast<size_t>(bh) * nblk + b] = s;
+  const int prow = (row & ~63) | kstep_row_of_pos(row & 63);
+  uint8_t* dst = Kq + (static_cast<size_t>(bh) * nblk * KVB + b * KVB + prow) * D + part * CPT;
+#pragma unroll
+  for (int q = 0; q < CPT / 16; ++q) {
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const uint32_t code = pos < N ? e4m3_encode(x[q * 16 + e] / s) : 0u;
+      w[e >> 2] |= code << (8 * (e & 3));
+    }
+    *reinterpret_cast<uint4*>(dst + q * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+// ---- host launchers ---------------------------------------------------------------
+static inline unsigned blocks_for(size_t n, int per) { return static_cast<unsigned>((n + per - 1) / per); }
+
+hipError_t launch_fill(uint32_t* p, uint32_t v, size_t n, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  const unsigned nb = static_cast<unsigned>(std::min<size_t>(blocks_for(n, 256), 4096));
+  hipLaunchKernelGGL(k_fill_u32, dim3(nb), dim3(256), 0, st, p, v, n);
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t prep_stats_t(const PrepArgs& a, hipStream_t st) {
+  const int BH = a.B * a.H;
+  hipLaunchKernelGGL(k_stats_partial<D>, dim3(a.nstat, BH), dim3(256), 0, st, a.K, a.V, a.N, a.nstat,
+                     a.kpart, a.vamax);
+  hipLaunchKernelGGL(k_stats_final<D>, dim3(BH), dim3(D), 0, st, a.kpart, a.vamax, a.N, a.nstat, a.mu, a.sV);
+  return hipGetLastError();
+}
+
+hipError_t launch_stats(const PrepArgs& a, hipStream_t st) {
+  return a.d == 64 ? prep_stats_t<64>(a, st) : prep_stats_t<128>(a, st);
+}
+
+hipError_t launch_quant_v_i8(const PrepArgs& a, hipStream_t st) {
+  const size_t per_head = static_cast<size_t>(a.N) * a.d;
+  const size_t total = per_head * a.B * a.H;
+  hipLaunchKernelGGL(k_quant_v_i8, dim3(blocks_for(total / 8, 256)), dim3(256), 0, st, a.V, a.sV, per_head,
+                     total, a.Vq);
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t init_t(const PrepArgs& a, const int32_t* init, hipStream_t st) {
+  hipLaunchKernelGGL(k_init_centroids<D>, dim3(a.k, a.B * a.H), dim3(D), 0, st, a.V, init, a.N, a.k, a.C);
+  return hipGetLastError();
+}
+hipError_t launch_init_centroids(const PrepArgs& a, const int32_t* init, hipStream_t st) {
+  return a.d == 64 ? init_t<64>(a, init, st) : init_t<128>(a, init, st);
+}
+
+template <int D>
+static hipError_t assign_t(const PrepArgs& a, int32_t* labels, hipStream_t st) {
+  const int BH = a.B * a.H;
+  hipLaunchKernelGGL(k_quant_centroids<D>, dim3((a.kpad + 3) / 4, BH), dim3(256), 0, st, a.C, a.sV, a.k, a.kpad,
+                     a.Cq, a.cn32);
+  hipLaunchKernelGGL(k_kmeans_assign<D>, dim3((a.N + 255) / 256, BH), dim3(256), 0, st, a.Vq, a.Cq, a.cn32, a.N,
+                     a.kpad, labels);
+  return hipGetLastError();
+}
+hipError_t launch_assign(const PrepArgs& a, int32_t* labels, hipStream_t st) {
+  return a.d == 64 ? assign_t<64>(a, labels, st) : assign_t<128>(a, labels, st);
+}
+
+hipError_t launch_sort(const PrepArgs& a, const int32_t* labels, int32_t* perm, hipStream_t st) {
+  const int BH = a.B * a.H;
+  hipLaunchKernelGGL(k_sort_hist, dim3(a.nsort, BH), dim3(256), 0, st, labels, a.N, a.k, a.nsort, a.hist);
+  hipLaunchKernelGGL(k_sort_scan, dim3(BH), dim3(1024), 0, st, a.hist, a.k, a.nsort, a.counts, a.starts);
+  hipLaunchKernelGGL(k_sort_scatter, dim3(a.nsort, BH), dim3(256), 0, st, labels, a.hist, a.N, a.k, a.nsort, perm);
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t update_t(const PrepArgs& a, const int32_t* perm, hipStream_t st) {
+  hipLaunchKernelGGL(k_kmeans_update<D>, dim3(a.k, a.B * a.H), dim3(D), 0, st, a.V, perm, a.counts, a.starts,
+                     a.N, a.k, a.C);
+  return hipGetLastError();
+}
+hipError_t launch_update(const PrepArgs& a, const int32_t* perm, hipStream_t st) {
+  return a.d == 64 ? update_t<64>(a, perm, st) : update_t<128>(a, perm, st);
+}
+
+hipError_t launch_iota(int32_t* perm, int N, size_t total, hipStream_t st) {
+  hipLaunchKernelGGL(k_iota, dim3(blocks_for(total, 256)), dim3(256), 0, st, perm, N, total);
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t vres_t(const PrepArgs& a, const int32_t* perm, const PrepOut& o, hipStream_t st) {
+  const int BH = a.B * a.H;
+  const int e4 = a.v_format == 0;
+  hipLaunchKernelGGL(k_vblock_stats<D>, dim3(a.nblk, BH), dim3(D), 0, st, a.V, perm, a.N, a.kvb, a.nblk,
+                     a.vsmooth, e4, o.v_mean, a.vramax);
+  if (e4)
+    hipLaunchKernelGGL(k_vres_e4m3<D>, dim3(a.nblk, BH), dim3(256), 0, st, a.V, perm, o.v_mean, a.vramax, a.N,
+                       a.kvb, a.nblk, o.Vres, reinterpret_cast<float*>(o.v_scale));
+  else
+    hipLaunchKernelGGL(k_vres_mxfp4<D>, dim3(a.nblk, BH), dim3(256), 0, st, a.V, perm, o.v_mean, a.N, a.kvb,
+                       a.nblk, o.Vres, reinterpret_cast<uint8_t*>(o.v_scale));
+  if (a.kvb == 64)
+    hipLaunchKernelGGL((k_ksmooth<D, 64>), dim3(a.nblk, BH), dim3(256), 0, st, a.K, perm, a.mu, a.N, a.nblk,
+                       o.Kq, o.k_scale);
+  else
+    hipLaunchKernelGGL((k_ksmooth<D, 128>), dim3(a.nblk, BH), dim3(256), 0, st, a.K, perm, a.mu, a.N, a.nblk,
+                       o.Kq, o.k_scale);
+  return hipGetLastError();
+}
+hipError_t launch_vres_ksmooth(const PrepArgs& a, const int32_t* perm, const PrepOut& o, hipStream_t st) {
+  return a.d == 64 ? vres_t<64>(a, perm, o, st) : vres_t<128>(a, perm, o, st);
+}
+
+}  // namespace vc

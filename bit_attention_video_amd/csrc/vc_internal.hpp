@@ -1,0 +1,69 @@
+// Internal declarations shared by the host library and the kernel files.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <algorithm>
+#include "vc_device.hpp"
+
+namespace vc {
+
+constexpr int kMaxClusters = 4096;   // k-means clusters per head (LDS histogram size)
+constexpr int kSortChunk = 4096;     // tokens per counting-sort chunk
+
+struct PrepArgs {
+  int B, H, N, d, kvb, k, kpad, iters, vsmooth, v_format;
+  int nblk, nstat, nsort;
+  const uint16_t* K;
+  const uint16_t* V;
+  // workspace
+  uint32_t* vamax;     // [BH]       max |V| bits
+  float* sV;           // [BH]       int8 scale of V
+  double* kpart;       // [BH,nstat,d]
+  float* mu;           // [BH,d]     K channel means
+  int8_t* Vq;          // [BH,N,d]
+  float* C;            // [BH,k,d]   centroids
+  int8_t* Cq;          // [BH,kpad,d]
+  int32_t* cn32;       // [BH,kpad]
+  int32_t* labels;     // [BH,N]
+  int32_t* perm_tmp;   // [BH,N]
+  int32_t* hist;       // [BH,nsort,k]
+  int32_t* counts;     // [BH,k]
+  int32_t* starts;     // [BH,k]
+  uint32_t* vramax;    // [BH,d]     residual channel max bits
+};
+
+struct PrepOut {
+  uint8_t* Kq;
+  float* k_scale;
+  uint8_t* Vres;
+  void* v_scale;
+  float* v_mean;
+  int32_t* perm;
+};
+
+struct AttnArgs {
+  int B, H, N, d, kvb, nblk, v_format, out_fp32;
+  float scale, kc;     // softmax scale, fp32(56 + beta)
+  const uint16_t* Q;
+  const uint8_t* Kq;
+  const float* k_scale;
+  const uint8_t* Vres;
+  const void* v_scale;
+  const float* v_mean;
+  void* O;
+};
+
+hipError_t launch_fill(uint32_t* p, uint32_t v, size_t n, hipStream_t st);
+hipError_t launch_stats(const PrepArgs& a, hipStream_t st);
+hipError_t launch_quant_v_i8(const PrepArgs& a, hipStream_t st);
+hipError_t launch_init_centroids(const PrepArgs& a, const int32_t* init, hipStream_t st);
+hipError_t launch_assign(const PrepArgs& a, int32_t* labels, hipStream_t st);
+hipError_t launch_sort(const PrepArgs& a, const int32_t* labels, int32_t* perm, hipStream_t st);
+hipError_t launch_update(const PrepArgs& a, const int32_t* perm, hipStream_t st);
+hipError_t launch_iota(int32_t* perm, int N, size_t total, hipStream_t st);
+hipError_t launch_vres_ksmooth(const PrepArgs& a, const int32_t* perm, const PrepOut& o, hipStream_t st);
+hipError_t launch_attn(const AttnArgs& a, hipStream_t st);
+hipError_t launch_dbg_expcast(const float* S, const float* A, const float* B, int64_t n, uint8_t* out,
+                              hipStream_t st);
+
+}  // namespace vc

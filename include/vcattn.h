@@ -1,0 +1,149 @@
+/*
+ * vcattn.h - C ABI of the VC-Attention forward pass for AMD MI355X (gfx950).
+ *
+ * The method (web pages on VC-Attention):
+ *   - V-Smooth: a lightweight k-means groups similar value tokens into the same
+ *     fixed-size hardware block; each block's mean is subtracted and kept in
+ *     high precision, only the residual is quantised (per-channel E4M3, or a
+ *     4-bit format), and the mean is restored from the row sums the online
+ *     softmax keeps.  (chooseai.io brief, section "V-Smooth"; zerohour.day
+ *     summary, key facts: per-channel E4M3/NVFP4 residuals after block-mean
+ *     subtraction; theclarity.today story: one pass over the values.)
+ *   - ExpCast-FP8: the softmax probability byte is computed from the log2
+ *     score z by one fused multiply-add, round(8z + 56 + beta), clamped to
+ *     [0, 56], instead of an fp32 exp2 followed by a cast.  (chooseai.io brief,
+ *     section "ExpCast-FP8".)
+ *   - QK^T and PV both run on FP8 E4M3 matrix instructions.
+ *
+ * Conventions for every entry point
+ *   - All tensor pointers are DEVICE pointers of the current HIP device.  The
+ *     caller owns every buffer, including the workspace; the library never
+ *     allocates or frees device memory and keeps no state between calls
+ *     (except the per-thread error string).
+ *   - Work is enqueued on `stream`; nothing synchronises.  Calls on different
+ *     streams need different workspaces and outputs.
+ *   - Arguments are validated before anything is launched.  On an invalid
+ *     argument nothing runs and VC_ERR_INVALID_ARG / VC_ERR_UNSUPPORTED /
+ *     VC_ERR_WORKSPACE is returned; a failed launch returns VC_ERR_HIP and
+ *     vc_last_error() holds the HIP message.  No exception crosses the ABI.
+ *   - bf16 tensors are raw 16-bit bfloat16 patterns.
+ *   - Shapes: Q, K, V, O are [B, H, N, d] row-major.  d in {64, 128},
+ *     kv_block in {64, 128}, query tiles are 128 rows (natural token order).
+ *     nblk = ceil(N / kv_block); Np = nblk * kv_block (padded length).
+ *
+ * Blocked layouts written by vsmooth_prepare (all per (b, h), in that order):
+ *   perm     int32 [B,H,N]   perm[j] = original index of the token at sorted
+ *                            position j (stable sort by cluster label).
+ *   Kq       uint8 [B,H,Np,d] E4M3 codes of the smoothed, permuted keys.  Rows
+ *                            are stored in "k-step order": sorted positions
+ *                            come in groups of 64; inside a group the sorted
+ *                            position kappa = 32t + 16g + 4i + j (t,g in {0,1},
+ *                            i,j in 0..3) is stored at row 32t + 8i + 4g + j.
+ *                            Padded rows (position >= N) are 0.
+ *   k_scale  fp32 [B,H,nblk] per-block key scale.
+ *   Vres     E4M3:  uint8 [B,H,Np/64,d,64]  per group of 64 sorted positions,
+ *                   one 64-byte row per channel (position order).
+ *            MXFP4: uint8 [B,H,Np/64,d,32]  same, two E2M1 codes per byte, the
+ *                   even position in the low nibble.
+ *   v_scale  E4M3:  fp32 [B,H,d]  per-channel residual scale.
+ *            MXFP4: uint8 E8M0 [B,H,Np/32,d]  one scale per 32 sorted
+ *                   positions and channel.
+ *   v_mean   fp32 [B,H,nblk,d]  block means (zero when V-Smooth is off).
+ */
+#ifndef VCATTN_H
+#define VCATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  VC_OK = 0,
+  VC_ERR_INVALID_ARG = -1,
+  VC_ERR_UNSUPPORTED = -2,
+  VC_ERR_WORKSPACE = -3,
+  VC_ERR_HIP = -4
+} vc_status;
+
+typedef struct {
+  int32_t B, H, N, d;       /* N >= 1; d in {64, 128}                              */
+  int32_t kv_block;         /* 64 or 128 tokens per hardware block                 */
+  int32_t n_clusters;       /* k-means clusters k, 1 <= k <= min(N, 4096)          */
+  int32_t iters;            /* k-means assignment passes I, 1..16                  */
+  int32_t vsmooth;          /* 1: V-Smooth on; 0: identity order, zero means       */
+  int32_t v_format;         /* 0: E4M3 residuals, per-channel scale; 1: MXFP4      */
+  int32_t out_fp32;         /* 0: O is bf16; 1: O is fp32                          */
+  float softmax_scale;      /* 0 selects fp32(1/sqrt(d))                           */
+  float beta;               /* ExpCast offset, -0.5 <= beta <= 0.45                */
+} vc_config;
+
+/* Bytes of workspace vsmooth_prepare needs (k-means and sort scratch). */
+size_t vc_prepare_workspace_bytes(const vc_config* cfg);
+/* Bytes of workspace vc_attention needs (prepare scratch + blocked K/V). */
+size_t vc_attention_workspace_bytes(const vc_config* cfg);
+
+/*
+ * vsmooth_prepare: V-Smooth and K smoothing (chooseai.io brief, "V-Smooth").
+ *   K, V      bf16 [B,H,N,d]
+ *   init_idx  int32 [B,H,k]  initial centroid token indices, distinct, in
+ *             [0, N) (the method's random initialisation, drawn by the caller;
+ *             ignored when vsmooth == 0, may be NULL then)
+ *   outputs   Kq, k_scale, Vres, v_scale, v_mean, perm in the layouts above;
+ *             labels int32 [B,H,N] final cluster labels (nullable)
+ *   ws        device workspace of at least vc_prepare_workspace_bytes(cfg)
+ * Readings where the pages are silent: k-means distances on int8 codes with
+ * one per-head scale, ties to the lowest cluster index, fp32 centroid means;
+ * stable sort by label and fixed blocks; K smoothed by its per-channel mean
+ * and quantised per block.
+ */
+vc_status vsmooth_prepare(const vc_config* cfg, const void* K, const void* V,
+                          const int32_t* init_idx, uint8_t* Kq, float* k_scale,
+                          uint8_t* Vres, void* v_scale, float* v_mean, int32_t* perm,
+                          int32_t* labels, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * vc_attn_fwd: fused forward (chooseai.io brief, "ExpCast-FP8" and the last
+ * sentences of "V-Smooth").  Q bf16 [B,H,N,d] in natural order; Kq..v_mean as
+ * written by vsmooth_prepare; O [B,H,N,d] bf16 or fp32 (cfg->out_fp32), rows in
+ * natural token order.  Per 128-row query tile: E4M3 query codes with one
+ * scale; per KV block in ascending order: S = Qq.Kq^T on FP8 MFMA, running
+ * log2 maximum m, bytes = cvt_u8(fma(S, 8c, 56 + beta - 8m)), row sums of the
+ * decoded bytes, acc = alpha*acc + P.Vres + rowsum * mean; O = scale*acc / l.
+ */
+vc_status vc_attn_fwd(const vc_config* cfg, const void* Q, const uint8_t* Kq,
+                      const float* k_scale, const uint8_t* Vres, const void* v_scale,
+                      const float* v_mean, void* O, hipStream_t stream);
+
+/* vc_attention: vsmooth_prepare + vc_attn_fwd with the blocked K/V kept in the
+ * workspace (the clustering happens inside the attention call, as the
+ * theclarity.today story describes).  ws >= vc_attention_workspace_bytes. */
+vc_status vc_attention(const vc_config* cfg, const void* Q, const void* K, const void* V,
+                       const int32_t* init_idx, void* O, void* ws, size_t ws_bytes,
+                       hipStream_t stream);
+
+const char* vc_status_str(vc_status s);
+/* Message of the last failure on the calling thread ("" if none). */
+const char* vc_last_error(void);
+
+/* ---- test entry points (same kernels as the path above) --------------------
+ * vc_dbg_expcast: out[i] = the ExpCast byte the attention kernel computes from
+ *   fp32 score S[i] with per-element A[i] = 8c and B[i] = 56 + beta - 8m.
+ * vc_dbg_kmeans_assign: one assignment pass given centroids C fp32 [B,H,k,d]
+ *   (int8 codes with the per-head scale of V), labels int32 [B,H,N].
+ * vc_dbg_sort: perm int32 [B,H,N] = stable sort of labels int32 [B,H,N] with
+ *   k = cfg->n_clusters. */
+vc_status vc_dbg_expcast(const float* S, const float* A, const float* B, int64_t n,
+                         uint8_t* out, hipStream_t stream);
+vc_status vc_dbg_kmeans_assign(const vc_config* cfg, const void* V, const float* C,
+                               int32_t* labels, void* ws, size_t ws_bytes, hipStream_t stream);
+vc_status vc_dbg_sort(const vc_config* cfg, const int32_t* labels, int32_t* perm,
+                      void* ws, size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* VCATTN_H */

@@ -12,8 +12,9 @@ and no separate cast.  Readings:
   * the running maximum m is kept in these units, m = max(m, fp32(c*max_j S_j));
   * the single FMA is evaluated as  x = fma(S_j, 8c, fp32(56 + beta - 8m))  in
     binary32 with one rounding, and byte = clamp(rne(x), 0, 56);
-  * beta is not given on the pages; the default -0.45840 = 8/ln2 - 12 makes
-    the mean pre-rounding offset against exact exp2 zero over fractional z.
+  * beta is not given on the pages; it is a binary32 parameter, and the
+    default fp32(8/ln2 - 12) = -0.45840 makes the mean pre-rounding offset
+    against exact exp2 zero over fractional z.
   * padded keys score -inf, giving byte 0.
 
 Online softmax and mean restoration ([brief] "V-Smooth", last sentences:
@@ -77,7 +78,7 @@ def attend_tile(Q: np.ndarray, kdec: np.ndarray, k_scale: np.ndarray, vres: np.n
         qc, s_q = quantize_q_tile(Q)
         qdec = e4m3_decode(qc)
         cq = float(f32(f32(s_q * scale) * f32(LOG2E)))
-        Kc = float(f32(56.0 + beta))
+        Kc = float(f32(56.0 + float(f32(beta))))   # beta is a binary32 parameter
     else:
         qdec = Q
         cq = scale * LOG2E

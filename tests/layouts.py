@@ -1,0 +1,41 @@
+"""Test helpers: undo the library's blocked storage layouts (as documented in
+include/vcattn.h) so GPU results can be compared with the oracle's
+natural-order arrays, and move seeded inputs to the device."""
+from __future__ import annotations
+
+import numpy as np
+
+
+def kstep_rows() -> np.ndarray:
+    """row[kappa] = stored row of sorted position kappa inside a 64-key group:
+    kappa = 32t + 16g + 4i + j is stored at 32t + 8i + 4g + j."""
+    row = np.empty(64, np.int64)
+    for t in range(2):
+        for g in range(2):
+            for i in range(4):
+                for j in range(4):
+                    row[32 * t + 16 * g + 4 * i + j] = 32 * t + 8 * i + 4 * g + j
+    return row
+
+
+def kq_natural(Kq: np.ndarray) -> np.ndarray:
+    """[..., Np, d] stored rows -> sorted-position order."""
+    Np = Kq.shape[-2]
+    pos = np.arange(Np)
+    src = (pos & ~63) | kstep_rows()[pos & 63]
+    return Kq[..., src, :]
+
+
+def vres_natural(Vres: np.ndarray, fmt: str) -> np.ndarray:
+    """E4M3 [..., Np/64, d, 64] or MXFP4 [..., Np/64, d, 32] -> codes [..., Np, d]."""
+    if fmt == "mxfp4":
+        lo = Vres & 0x0F
+        hi = Vres >> 4
+        Vres = np.stack([lo, hi], axis=-1).reshape(*Vres.shape[:-1], 64)
+    x = np.swapaxes(Vres, -1, -2)                     # [..., Np/64, 64, d]
+    return x.reshape(*x.shape[:-3], x.shape[-3] * 64, x.shape[-1])
+
+
+def to_device_bf16(bits: np.ndarray, device="cuda"):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(device)

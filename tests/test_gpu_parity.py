@@ -1,0 +1,250 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle.
+
+Bit-exact: ExpCast bytes given the same fp32 scores, k-means labels given the
+oracle's centroids for every pass, the stable sort given labels, and the whole
+V-Smooth preparation (labels, perm, Kq, k_scale, residual codes, scales,
+means).  Within the stated tolerance (relative L2 <= 1e-2 and
+max-abs <= 3e-2 * max|V|): the attention output O.  Large workloads are checked
+on sampled heads and query tiles in the launch configuration the benchmark
+times (all heads launched together).
+"""
+import sys
+import time
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import formats as F
+from oracle.attention import DEFAULT_BETA, exact_attention, expcast_bytes, softmax_scale
+from bit_attention_video_amd import binding as vb
+from bit_attention_video_amd import inputs
+from layouts import kq_natural, vres_natural, to_device_bf16
+
+pytestmark = pytest.mark.gpu
+
+REL_L2 = 1e-2
+MAXABS_FRAC = 3e-2
+
+
+def log(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    vb.lib()
+
+
+def fmt_id(fmt):
+    return vb.E4M3 if fmt == "e4m3" else vb.MXFP4
+
+
+def cfg_for(w, H=None, N=None, vsmooth=True, fmt=None, out_fp32=True, beta=DEFAULT_BETA):
+    fmt = fmt or w.v_format
+    N = N or w.N
+    return vb.make_config(w.B, H or w.H, N, w.d, w.kv_block, min(w.k, N), w.iters, vsmooth, fmt_id(fmt),
+                          out_fp32, 0.0, beta)
+
+
+def gen(w, H=None, N=None):
+    q, k, v, init = inputs.gen_all(w, N=N, H=H)
+    dev = dict(Q=to_device_bf16(q), K=to_device_bf16(k), V=to_device_bf16(v),
+               init=torch.from_numpy(init).cuda())
+    return (q, k, v, init), dev
+
+
+def prep_to_numpy(prep: vb.Prepared, fmt):
+    out = {k: getattr(prep, k).cpu().numpy() for k in ("Kq", "k_scale", "Vres", "v_scale", "v_mean", "perm")}
+    out["labels"] = prep.labels.cpu().numpy() if prep.labels is not None else None
+    out["Kq_nat"] = kq_natural(out["Kq"])
+    out["Vres_nat"] = vres_natural(out["Vres"], fmt)
+    return out
+
+
+def oracle_head(w, host, b, h, vsmooth=True, fmt=None):
+    q, k, v, init = host
+    K = oracle.bf16_to_f64(k[b, h])
+    V = oracle.bf16_to_f64(v[b, h])
+    return oracle.prepare_head(K, V, init[b, h], init.shape[-1], w.iters, w.kv_block,
+                               fmt or w.v_format, vsmooth)
+
+
+def compare_prep(g, o, b, h, fmt, vsmooth=True):
+    N = o["N"]
+    if vsmooth:
+        assert np.array_equal(g["labels"][b, h], o["labels"]), "labels differ"
+    assert np.array_equal(g["perm"][b, h], o["perm"]), "perm differs"
+    assert np.array_equal(g["k_scale"][b, h], o["k"]["k_scale"].astype(np.float32)), "k_scale differs"
+    kq_diff = np.count_nonzero(g["Kq_nat"][b, h] != o["k"]["codes"])
+    assert kq_diff == 0, f"{kq_diff} Kq codes differ"
+    assert np.array_equal(g["v_mean"][b, h], o["v"]["means"].astype(np.float32)), "means differ"
+    v_diff = np.count_nonzero(g["Vres_nat"][b, h] != o["v"]["codes"])
+    assert v_diff == 0, f"{v_diff} residual codes differ"
+    if fmt == "e4m3":
+        assert np.array_equal(g["v_scale"][b, h], o["v"]["col_scale"].astype(np.float32)), "s_v differs"
+    else:
+        assert np.array_equal(g["v_scale"][b, h], o["v"]["e8m0"]), "E8M0 scales differ"
+
+
+def check_close(O, Oref, vmax, what=""):
+    err = O - Oref
+    rel = float(np.linalg.norm(err) / np.linalg.norm(Oref))
+    mab = float(np.max(np.abs(err)))
+    log(f"  {what}: rel-L2 {rel:.3e}  max-abs {mab:.3e} ({mab / vmax:.2e} of max|V|)")
+    assert rel <= REL_L2 and mab <= MAXABS_FRAC * vmax, (rel, mab, vmax)
+    return rel, mab
+
+
+# ------------------------------------------------------------------ ExpCast bytes
+def test_expcast_bytes_bit_exact():
+    rng = np.random.default_rng(100)
+    rows, cols = 512, 256
+    S = (rng.standard_normal((rows, cols)) * rng.uniform(1, 3e4, (rows, 1))).astype(np.float32)
+    S[:, -3:] = -np.inf
+    c = F.f32(rng.uniform(1e-6, 1e-3, rows))
+    m = F.f32(c * np.max(np.where(np.isfinite(S), S, -np.inf), axis=1))
+    A = (8.0 * c).astype(np.float32)
+    B = F.f32(F.f32(56.0 + float(F.f32(DEFAULT_BETA))) - 8.0 * m).astype(np.float32)
+    want = expcast_bytes(S.astype(np.float64), A[:, None].astype(np.float64), B[:, None].astype(np.float64))
+    # exact ties k + 0.5 (A = 1, B = 0) and clamping at 0
+    ties = np.concatenate([np.arange(0, 56) + 0.5, [-0.5, -0.49, -3.0, 0.4999, 55.49]]).astype(np.float32)
+    St = np.concatenate([S.ravel(), ties])
+    At = np.concatenate([np.repeat(A, cols), np.ones_like(ties)])
+    Bt = np.concatenate([np.repeat(B, cols), np.zeros_like(ties)])
+    wantt = np.concatenate([want.ravel(), expcast_bytes(ties.astype(np.float64), 1.0, np.zeros(ties.size))])
+    got = vb.dbg_expcast(torch.from_numpy(St).cuda(), torch.from_numpy(At).cuda(), torch.from_numpy(Bt).cuda())
+    got = got.cpu().numpy()
+    assert np.array_equal(got, wantt), np.count_nonzero(got != wantt)
+    assert list(got[-61:-5]) == [int(k) + (int(k) & 1) for k in range(56)]
+
+
+# ------------------------------------------------------------------ sort
+@pytest.mark.parametrize("N,k", [(1, 1), (1000, 16), (77777, 1024), (20000, 4096), (5000, 1)])
+def test_sort_bit_exact(N, k):
+    rng = np.random.default_rng(N + k)
+    lab = rng.integers(0, k, (1, 2, N)).astype(np.int32)
+    if k > 4:
+        lab[0, 1, : N // 2] = 3                    # a large cluster
+    cfg = vb.make_config(1, 2, N, 64, 64, k, 1)
+    perm = vb.dbg_sort(cfg, torch.from_numpy(lab).cuda()).cpu().numpy()
+    for h in range(2):
+        assert np.array_equal(perm[0, h], np.argsort(lab[0, h], kind="stable"))
+
+
+# ------------------------------------------------------------------ k-means assignment
+@pytest.mark.parametrize("name,H,N", [("tiny", 2, None), ("mid", 2, None), ("video", 1, None), ("tiny", 1, 333)])
+def test_kmeans_assign_given_oracle_centroids(name, H, N):
+    w = inputs.WORKLOADS[name]
+    host, dev = gen(w, H=H, N=N)
+    cfg = cfg_for(w, H=H, N=N)
+    for h in range(H):
+        V = oracle.bf16_to_f64(host[2][0, h])
+        labels, cents = oracle.kmeans.kmeans(V, host[3][0, h], w.iters)
+        sV = oracle.kmeans.int8_scale(V)
+        Vq = oracle.kmeans.quant_i8(V, sV)
+        for it, C in enumerate(cents):
+            Call = np.zeros((1, H, cfg.n_clusters, w.d), np.float32)
+            Call[0, h] = C
+            got = vb.dbg_kmeans_assign(cfg, dev["V"], torch.from_numpy(Call).cuda()).cpu().numpy()[0, h]
+            want = oracle.kmeans.assign(Vq, oracle.kmeans.quant_i8(C, sV))
+            nd = np.count_nonzero(got != want)
+            log(f"  {name} h{h} pass {it}: {nd} label mismatches of {got.size}")
+            assert nd == 0
+
+
+# ------------------------------------------------------------------ preparation
+@pytest.mark.parametrize("name,H,N,vsmooth,fmt", [
+    ("tiny", 2, None, True, "e4m3"), ("tiny", 2, None, False, "e4m3"), ("tiny", 2, None, True, "mxfp4"),
+    ("tiny", 1, 1000, True, "e4m3"), ("tiny", 1, 1, True, "e4m3"), ("mid", 2, None, True, "e4m3"),
+    ("mid", 1, 3000, True, "mxfp4"),
+])
+def test_prepare_bit_exact(name, H, N, vsmooth, fmt):
+    w = inputs.WORKLOADS[name]
+    host, dev = gen(w, H=H, N=N)
+    cfg = cfg_for(w, H=H, N=N, vsmooth=vsmooth, fmt=fmt)
+    g = prep_to_numpy(vb.vsmooth_prepare(cfg, dev["K"], dev["V"], dev["init"]), fmt)
+    for h in range(H):
+        o = oracle_head(w, host, 0, h, vsmooth, fmt)
+        compare_prep(g, o, 0, h, fmt, vsmooth)
+
+
+# ------------------------------------------------------------------ attention
+def oracle_rows(w, host, b, h, prep_o, tiles, beta=DEFAULT_BETA):
+    Q = oracle.bf16_to_f64(host[0][b, h])
+    return oracle.attend_rows(Q, prep_o, tiles, 0.0, beta)
+
+
+@pytest.mark.parametrize("name,H,N,vsmooth,fmt,kvb,d", [
+    ("tiny", 2, None, True, "e4m3", None, None),
+    ("tiny", 2, None, False, "e4m3", None, None),
+    ("tiny", 2, None, True, "mxfp4", None, None),
+    ("tiny", 1, 1000, True, "e4m3", 128, None),     # ragged query tile and KV block
+    ("tiny", 1, 77, True, "e4m3", 64, None),        # one partial block
+    ("tiny", 1, 1, True, "e4m3", 64, None),         # a single token
+    ("tiny", 1, 700, True, "mxfp4", 128, 128),
+    ("mid", 2, None, True, "e4m3", None, None),
+])
+def test_attention_parity(name, H, N, vsmooth, fmt, kvb, d):
+    import dataclasses
+    w = inputs.WORKLOADS[name]
+    w = dataclasses.replace(w, kv_block=kvb or w.kv_block, d=d or w.d)
+    host, dev = gen(w, H=H, N=N)
+    N = N or w.N
+    cfg = cfg_for(w, H=H, N=N, vsmooth=vsmooth, fmt=fmt)
+    prep = vb.vsmooth_prepare(cfg, dev["K"], dev["V"], dev["init"])
+    O = vb.vc_attn_fwd(cfg, dev["Q"], prep).cpu().numpy()
+    O2 = vb.vc_attention(cfg, dev["Q"], dev["K"], dev["V"], dev["init"]).cpu().numpy()
+    assert np.array_equal(O, O2), "vc_attention differs from prepare + fwd"
+    ntile = oracle.n_q_tiles(N)
+    tiles = list(range(ntile)) if N <= 4096 else sorted({0, 1, ntile // 2, ntile - 1})
+    for h in range(H):
+        po = oracle_head(w, host, 0, h, vsmooth, fmt)
+        rows = oracle_rows(w, host, 0, h, po, tiles)
+        Oref = np.concatenate([rows[t] for t in tiles])
+        Og = np.concatenate([O[0, h, t * 128:min((t + 1) * 128, N)] for t in tiles])
+        vmax = float(np.max(np.abs(oracle.bf16_to_f64(host[2][0, h]))))
+        check_close(Og, Oref, vmax, f"{name} N={N} h{h} vs={vsmooth} {fmt}")
+
+
+def test_bf16_output_and_determinism():
+    w = inputs.WORKLOADS["mid"]
+    host, dev = gen(w, H=2)
+    c32 = cfg_for(w, H=2, out_fp32=True)
+    c16 = cfg_for(w, H=2, out_fp32=False)
+    O32 = vb.vc_attention(c32, dev["Q"], dev["K"], dev["V"], dev["init"])
+    Oa = vb.vc_attention(c16, dev["Q"], dev["K"], dev["V"], dev["init"])
+    Ob = vb.vc_attention(c16, dev["Q"], dev["K"], dev["V"], dev["init"])
+    assert torch.equal(Oa.view(torch.int16), Ob.view(torch.int16)), "two runs differ"
+    assert torch.equal(Oa, O32.to(torch.bfloat16)), "bf16 output is not the RNE of the fp32 output"
+
+
+# ------------------------------------------------------------------ full-size workloads, sampled
+@pytest.mark.parametrize("name", ["video", "mxfp4"])
+def test_full_size_sampled(name):
+    w = inputs.WORKLOADS[name]
+    t0 = time.time()
+    host, dev = gen(w)
+    log(f"  generated {name} in {time.time() - t0:.1f}s")
+    cfg = cfg_for(w, out_fp32=False)
+    prep = vb.vsmooth_prepare(cfg, dev["K"], dev["V"], dev["init"])
+    O = vb.vc_attn_fwd(cfg, dev["Q"], prep)
+    torch.cuda.synchronize()
+    g = prep_to_numpy(prep, w.v_format)
+    O = O.float().cpu().numpy()
+    ntile = oracle.n_q_tiles(w.N)
+    for h in (0, w.H - 1):
+        t0 = time.time()
+        po = oracle_head(w, host, 0, h)
+        compare_prep(g, po, 0, h, w.v_format)
+        tiles = [0, ntile // 2, ntile - 1]
+        rows = oracle_rows(w, host, 0, h, po, tiles)
+        vmax = float(np.max(np.abs(oracle.bf16_to_f64(host[2][0, h]))))
+        for t in tiles:
+            lo, hi = t * 128, min((t + 1) * 128, w.N)
+            check_close(O[0, h, lo:hi], rows[t], vmax, f"{name} h{h} tile {t}")
+        log(f"  head {h} checked in {time.time() - t0:.1f}s")
