@@ -67,7 +67,11 @@ def _bf16_round(x: np.ndarray) -> np.ndarray:
     """fp32 -> bf16 bit patterns (uint16), round-to-nearest-even."""
     u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
     nan = np.isnan(x)
-    r = ((u.astype(np.uint64) + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    r = (u >> 16) & 1
+    r += 0x7FFF
+    r += u                      # no wrap: only NaN patterns exceed 0xFFFF7FFF
+    r >>= 16
+    r = r.astype(np.uint16)
     if nan.any():
         r[nan] = 0x7FC0
     return r
@@ -108,7 +112,11 @@ def iter_heads(w: Workload, N: int | None = None, d: int | None = None) -> Itera
 
 
 def gen_all(w: Workload, N: int | None = None, d: int | None = None, H: int | None = None):
-    """All heads as numpy arrays: q, k, v uint16 bf16 bits [B,H,N,d]; init int32 [B,H,k]."""
+    """All heads as numpy arrays: q, k, v uint16 bf16 bits [B,H,N,d]; init int32 [B,H,k].
+    Heads are drawn in parallel threads; each has its own generator, so the
+    result does not depend on the thread count."""
+    import concurrent.futures
+    import os
     N = w.N if N is None else N
     d = w.d if d is None else d
     H = w.H if H is None else H
@@ -117,9 +125,14 @@ def gen_all(w: Workload, N: int | None = None, d: int | None = None, H: int | No
     k = np.empty_like(q)
     v = np.empty_like(q)
     init = np.empty((w.B, H, kk), np.int32)
-    for b in range(w.B):
-        for h in range(H):
-            q[b, h], k[b, h], v[b, h], init[b, h] = gen_head(w, b, h, N, d)
+
+    def one(bh):
+        b, h = divmod(bh, H)
+        q[b, h], k[b, h], v[b, h], init[b, h] = gen_head(w, b, h, N, d)
+
+    workers = max(1, min(16, os.cpu_count() or 1, w.B * H))
+    with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as ex:
+        list(ex.map(one, range(w.B * H)))
     return q, k, v, init
 
 
