@@ -28,6 +28,8 @@
 // (bytes 0..15 from tile 0, 16..31 from tile 1); residual rows are stored in
 // kappa order, so fp8 A reads bytes [16g, 16g+16) and [32+16g, 48+16g) and FP4 A
 // reads nibbles [32g, 32g+32) = one E8M0 scale group.
+#include <type_traits>
+
 #include "vc_internal.hpp"
 
 namespace vc {
@@ -52,21 +54,244 @@ __global__ void k_dbg_expcast(const float* __restrict__ S, const float* __restri
   if (i < n) out[i] = static_cast<uint8_t>(expcast4(S[i], 0.f, 0.f, 0.f, A[i], B[i]) & 0xffu);
 }
 
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef __attribute__((address_space(1))) void* glb_ptr_t;
+
+// Swizzled 16-byte chunk inside an LDS row of RB bytes: consecutive rows that
+// share a 128-byte bank line get different chunk positions, so the 16-byte
+// operand reads of 8 consecutive rows hit distinct banks.
+template <int RB>
+__device__ __forceinline__ int swz(int row, int chunk) {
+  constexpr int CPR = RB / 16;          // chunks per row
+  constexpr int RPL = 128 / RB;         // rows per 128-byte line
+  return chunk ^ ((row / RPL) & (CPR - 1));
+}
+
+// max of v over lanes l and l^32 (v_permlane32_swap returns both halves)
+__device__ __forceinline__ float max_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(fmaxf(v, __uint_as_float(r[0])), __uint_as_float(r[1]));
+}
+
+template <int D, int KVB, int VF>
+struct AttnTile {
+  static constexpr int NDC = D / 64;      // 64-deep chunks of the QK^T contraction
+  static constexpr int NKT = KVB / 32;    // 32-key tiles of S^T per block
+  static constexpr int NKS = KVB / 64;    // 64-key steps of the PV contraction
+  static constexpr int NDT = D / 32;      // 32-channel tiles of O^T
+  static constexpr int VROW = VF == 0 ? 64 : 32;
+  static constexpr int KBYTES = KVB * D;
+  static constexpr int VBYTES = NKS * D * VROW;
+  static constexpr int SBYTES = VF == 1 ? (KVB / 32) * D : 0;
+  static constexpr int STAGE = KBYTES + VBYTES + (SBYTES + 1023) / 1024 * 1024;
+  static constexpr int MSLOT = 8;         // blocks per mean-restoration flush
+};
+
+// Per-lane offsets that stay fixed for the whole kernel.  With the swizzle
+// above, the chunk a lane reads depends only on its lane position (tile rows
+// start at multiples of 32), so every LDS operand address is lane offset +
+// compile-time tile offset, and every direct-load source is block base + lane
+// offset.
+template <int D, int KVB, int VF>
+struct LaneOffsets {
+  using T = AttnTile<D, KVB, VF>;
+  static constexpr int KR = T::KBYTES / 4096;           // direct-load rounds for K
+  static constexpr int VR = (T::VBYTES + 4095) / 4096;  // ... and for the residuals
+  int k_rd[T::NDC][2];   // K operand: 16-byte halves of the 32-byte chunk (c, h)
+  int v_rd[2];           // residual operand chunks (E4M3: g and 2+g; MXFP4: g)
+  int k_src, v_src;      // source offsets of this lane's direct loads (round 0)
+  __device__ __forceinline__ LaneOffsets(int lane) {
+    const int g = lane >> 5, col = lane & 31;
+#pragma unroll
+    for (int c = 0; c < T::NDC; ++c)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) k_rd[c][h] = col * D + swz<D>(col, 4 * c + 2 * g + h) * 16;
+    v_rd[0] = col * T::VROW + swz<T::VROW>(col, g) * 16;
+    v_rd[1] = col * T::VROW + swz<T::VROW>(col, VF == 0 ? 2 + g : g) * 16;
+    // round r fetches chunk 256r + tid: its row is 256r/(D/16) rows further
+    // down, a multiple of 32, so the swizzled chunk is the same as in round 0
+    const int t = threadIdx.x;
+    const int krow = t / (D / 16), vrow = t / (T::VROW / 16);
+    k_src = krow * D + swz<D>(krow, t % (D / 16)) * 16;
+    v_src = vrow * T::VROW + swz<T::VROW>(vrow, t % (T::VROW / 16)) * 16;
+  }
+};
+
+// Stage one block (K rows, residual rows, E8M0 scales) into LDS with direct
+// global->LDS loads (global_load_lds_dwordx4: lane i of a wave writes bytes
+// [16i, 16i+16) after the wave-uniform base); the swizzle is applied on the
+// global side by choosing which chunk each lane fetches.
+template <int D, int KVB, int VF>
+__device__ __forceinline__ void stage_block(uint8_t* st, const uint8_t* kq_blk, const uint8_t* vr_blk,
+                                            const uint8_t* sc_blk, const LaneOffsets<D, KVB, VF>& lo, int wave,
+                                            int lane) {
+  using T = AttnTile<D, KVB, VF>;
+  using L = LaneOffsets<D, KVB, VF>;
+  static_assert((256 / (D / 16)) % 32 == 0 || L::KR == 1, "K rows per round must keep the swizzle");
+#pragma unroll
+  for (int r = 0; r < L::KR; ++r)
+    __builtin_amdgcn_global_load_lds((glb_ptr_t)(kq_blk + lo.k_src + r * 4096),
+                                     (lds_ptr_t)(st + (r * 256 + wave * 64) * 16), 16, 0, 0);
+  uint8_t* sv = st + T::KBYTES;
+#pragma unroll
+  for (int r = 0; r < L::VR; ++r)
+    if ((r * 256 + wave * 64) * 16 < T::VBYTES)
+      __builtin_amdgcn_global_load_lds((glb_ptr_t)(vr_blk + lo.v_src + r * 4096),
+                                       (lds_ptr_t)(sv + (r * 256 + wave * 64) * 16), 16, 0, 0);
+  if constexpr (VF == 1) {
+    if (wave == 0 && lane < T::SBYTES / 16)
+      __builtin_amdgcn_global_load_lds((glb_ptr_t)(sc_blk + lane * 16), (lds_ptr_t)(sv + T::VBYTES), 16, 0, 0);
+  }
+}
+
+__device__ __forceinline__ uint32_t bf16_bits(float f) { return f32_to_bf16_rne(f); }
+__device__ __forceinline__ float bf16_val(uint32_t b) { return __uint_as_float(b << 16); }
+
+__device__ __forceinline__ v8i join8(uint4 lo, uint4 hi) {
+  return v8i{static_cast<int>(lo.x), static_cast<int>(lo.y), static_cast<int>(lo.z), static_cast<int>(lo.w),
+             static_cast<int>(hi.x), static_cast<int>(hi.y), static_cast<int>(hi.z), static_cast<int>(hi.w)};
+}
+
+// Per-wave running state of the online softmax.
+template <int NDT, int MS>
+struct SoftmaxState {
+  v16f acc[NDT];
+  float RS[MS];        // row sums of the blocks since the last mean flush
+  float m_run, l_run;
+};
+
+// One KV block: S^T on FP8 MFMA, row max, ExpCast bytes, row sums (ones.P^T),
+// rescale, PV on FP8 / scaled FP8xFP4 MFMA, and every MSLOT blocks the mean
+// restoration flush.
+template <int D, int KVB, int VF, bool MASK>
+__device__ __forceinline__ void attn_block(
+    SoftmaxState<D / 32, AttnTile<D, KVB, VF>::MSLOT>& st, const uint8_t* sK, const uint16_t* sMhalf,
+    const LaneOffsets<D, KVB, VF>& lo, const v8i* qb, float cb, float kc, int b, int nblk, int nvalid,
+    int g, int col) {
+  using TT = AttnTile<D, KVB, VF>;
+  constexpr int NDC = TT::NDC, NKT = TT::NKT, NKS = TT::NKS, NDT = TT::NDT, VROW = TT::VROW, MS = TT::MSLOT;
+  const uint8_t* sV = sK + TT::KBYTES;
+  const uint8_t* sS = sV + TT::VBYTES;
+  const v8i ones = {0x22222222, 0x22222222, 0x22222222, 0x22222222, 0, 0, 0, 0};   // E2M1 1.0 (FP4 operand)
+
+  v16f S[NKT];
+#pragma unroll
+  for (int kt = 0; kt < NKT; ++kt) {
+#pragma unroll
+    for (int c = 0; c < NDC; ++c) {
+      const v8i a = join8(*reinterpret_cast<const uint4*>(sK + kt * 32 * D + lo.k_rd[c][0]),
+                          *reinterpret_cast<const uint4*>(sK + kt * 32 * D + lo.k_rd[c][1]));
+      S[kt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qb[c], c == 0 ? v16f{} : S[kt], 0, 0, 0, 0, 0, 0);
+    }
+  }
+  if constexpr (MASK) {
+#pragma unroll
+    for (int kt = 0; kt < NKT; ++kt) {
+      const int lim = nvalid - ((kt >> 1) * 64 + (kt & 1) * 32 + 16 * g);   // keep r < lim
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (r >= lim) S[kt][r] = -__builtin_inff();
+    }
+  }
+  float mx = -__builtin_inff();
+#pragma unroll
+  for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) mx = fmaxf(fmaxf(mx, S[kt][r]), S[kt][r + 1]);
+  mx = max_xor32(mx);
+
+  const float m_new = fmaxf(st.m_run, cb * mx);
+  const float Bq = __builtin_fmaf(-8.0f, m_new, kc);
+  const float A8 = 8.0f * cb;
+
+  v8i P[NKS];
+#pragma unroll
+  for (int s = 0; s < NKS; ++s)
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const v16f& sv = S[2 * s + t];
+        P[s][4 * t + q4] =
+            static_cast<int>(expcast4(sv[4 * q4], sv[4 * q4 + 1], sv[4 * q4 + 2], sv[4 * q4 + 3], A8, Bq));
+      }
+  // row sums of the decoded bytes on the matrix core: ones(FP4) . P^T, exact
+  v16f rsum = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, P[0], v16f{}, 4, 0, 0, 127, 0, 127);
+#pragma unroll
+  for (int s = 1; s < NKS; ++s)
+    rsum = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, P[s], rsum, 4, 0, 0, 127, 0, 127);
+
+  if (__builtin_amdgcn_ballot_w64(m_new > st.m_run)) {
+    const float alpha = exp2f(st.m_run - m_new);
+#pragma unroll
+    for (int T = 0; T < NDT; ++T)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st.acc[T][r] *= alpha;
+#pragma unroll
+    for (int i = 0; i < MS; ++i) st.RS[i] *= alpha;
+    st.l_run *= alpha;
+  }
+  st.m_run = m_new;
+
+#pragma unroll
+  for (int s = 0; s < NKS; ++s)
+#pragma unroll
+    for (int T = 0; T < NDT; ++T) {
+      const uint8_t* vb = sV + (s * D + 32 * T) * VROW;
+      if constexpr (VF == 0) {
+        const v8i a = join8(*reinterpret_cast<const uint4*>(vb + lo.v_rd[0]),
+                            *reinterpret_cast<const uint4*>(vb + lo.v_rd[1]));
+        st.acc[T] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, P[s], st.acc[T], 0, 0, 0, 0, 0, 0);
+      } else {
+        const uint4 q = *reinterpret_cast<const uint4*>(vb + lo.v_rd[0]);
+        const v8i a = {static_cast<int>(q.x), static_cast<int>(q.y), static_cast<int>(q.z), static_cast<int>(q.w),
+                       0, 0, 0, 0};
+        const int sc = sS[(2 * s + g) * D + 32 * T + col];
+        st.acc[T] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, P[s], st.acc[T], 4, 0, 0, sc, 0, 127);
+      }
+    }
+  const float rs = rsum[0];
+  st.l_run += rs;
+  const int slot = b & (MS - 1);
+#pragma unroll
+  for (int i = 0; i < MS; ++i) st.RS[i] = i == slot ? rs : st.RS[i];
+
+  if (slot == MS - 1 || b == nblk - 1) {
+    // acc += (mean/s_v)^T . rowsums over the last MS blocks, on
+    // v_mfma_f32_32x32x16_bf16 with both factors split into bf16 hi + lo
+    // (lane group 0 feeds the hi means, group 1 the lo means)
+    v4i bhi, blo;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t h0 = bf16_bits(st.RS[2 * i]), h1 = bf16_bits(st.RS[2 * i + 1]);
+      const uint32_t l0 = bf16_bits(st.RS[2 * i] - bf16_val(h0)), l1 = bf16_bits(st.RS[2 * i + 1] - bf16_val(h1));
+      bhi[i] = static_cast<int>(h0 | (h1 << 16));
+      blo[i] = static_cast<int>(l0 | (l1 << 16));
+    }
+    typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+#pragma unroll
+    for (int T = 0; T < NDT; ++T) {
+      const v4i a = *reinterpret_cast<const v4i*>(sMhalf + (g * D + 32 * T + col) * MS);
+      st.acc[T] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, bhi),
+                                                          st.acc[T], 0, 0, 0);
+      st.acc[T] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, blo),
+                                                          st.acc[T], 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < MS; ++i) st.RS[i] = 0.0f;
+  }
+}
+
 template <int D, int KVB, int VF, int O32>
 __global__ __launch_bounds__(256, 2) void k_attn_fwd(AttnArgs p) {
-  constexpr int NDC = D / 64;     // 64-deep chunks of the QK^T contraction
-  constexpr int NKT = KVB / 32;   // 32-key tiles of S^T per block
-  constexpr int NKS = KVB / 64;   // 64-key steps of the PV contraction
-  constexpr int NDT = D / 32;     // 32-channel tiles of O^T
-  constexpr int KSTR = D + 16;    // padded LDS row strides (conflict-free 16-byte reads)
-  constexpr int VROW = VF == 0 ? 64 : 32;
-  constexpr int VSTR = VROW + 16;
-  __shared__ __attribute__((aligned(16))) uint8_t sK[KVB * KSTR];
-  __shared__ __attribute__((aligned(16))) uint8_t sV[NKS * D * VSTR];
-  __shared__ __attribute__((aligned(16))) uint8_t sVs[VF == 1 ? (KVB / 32) * D : 16];
-  __shared__ __attribute__((aligned(16))) float sMean[D];
-  __shared__ __attribute__((aligned(16))) float sCol[D];
-  __shared__ float sRed[4];
+  using TT = AttnTile<D, KVB, VF>;
+  constexpr int NDC = TT::NDC, NKS = TT::NKS, NDT = TT::NDT, VROW = TT::VROW;
+  constexpr int MS = TT::MSLOT;
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+  uint8_t* stages = smem;                                            // 2 x STAGE bytes
+  uint16_t* sM = reinterpret_cast<uint16_t*>(smem + 2 * TT::STAGE); // [2 halves][2 hi/lo][D][MS]
+  float* sCol = reinterpret_cast<float*>(sM + 2 * 2 * D * MS);       // [D]
+  float* sRed = sCol + D;                                            // [4]
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 5, col = lane & 31;
   const int N = p.N, nblk = p.nblk;
@@ -74,9 +299,24 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(AttnArgs p) {
   const int bh = blockIdx.x / nqt, qt = blockIdx.x % nqt;
   const int qrow = qt * kQTile + wave * 32 + col;
 
-  if (threadIdx.x < D)
-    sCol[threadIdx.x] = VF == 0 ? reinterpret_cast<const float*>(p.v_scale)[static_cast<size_t>(bh) * D + threadIdx.x]
-                                : 1.0f;
+  const uint8_t* kq = p.Kq + static_cast<size_t>(bh) * nblk * KVB * D;
+  const uint8_t* vr = p.Vres + static_cast<size_t>(bh) * nblk * NKS * D * VROW;
+  const uint8_t* scb = VF == 1 ? reinterpret_cast<const uint8_t*>(p.v_scale) +
+                                     static_cast<size_t>(bh) * nblk * (KVB / 32) * D
+                               : nullptr;
+  const float* ks = p.k_scale + static_cast<size_t>(bh) * nblk;
+  const float* vm = p.v_mean + static_cast<size_t>(bh) * nblk * D;
+  const LaneOffsets<D, KVB, VF> lo(lane);
+
+  // block 0 in flight while the query tile is prepared
+  stage_block<D, KVB, VF>(stages, kq, vr, scb, lo, wave, lane);
+
+  for (int i = threadIdx.x; i < 2 * 2 * D * MS; i += 256) sM[i] = 0;
+  float colv = 1.0f;
+  if (threadIdx.x < D) {
+    if (VF == 0) colv = reinterpret_cast<const float*>(p.v_scale)[static_cast<size_t>(bh) * D + threadIdx.x];
+    sCol[threadIdx.x] = colv;
+  }
 
   // ---- query tile: E4M3 codes with one scale per 128 rows ----
   v8i qb[NDC];
@@ -86,7 +326,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(AttnArgs p) {
     float am = 0.0f;
     const uint16_t* qp = p.Q + (static_cast<size_t>(bh) * N + qrow) * D;
 #pragma unroll
-    for (int c = 0; c < NDC; ++c) {
+    for (int c = 0; c < NDC; ++c)
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         uint4 raw = make_uint4(0u, 0u, 0u, 0u);
@@ -99,14 +339,13 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(AttnArgs p) {
           am = fmaxf(am, fabsf(f));
         }
       }
-    }
     am = wave_max(am);
     if (lane == 0) sRed[wave] = am;
     __syncthreads();
     const float amax = fmaxf(fmaxf(sRed[0], sRed[1]), fmaxf(sRed[2], sRed[3]));
     const float sq = amax > 0.0f ? amax / 448.0f : 1.0f;
 #pragma unroll
-    for (int c = 0; c < NDC; ++c) {
+    for (int c = 0; c < NDC; ++c)
 #pragma unroll
       for (int w = 0; w < 8; ++w) {
         uint32_t word = 0u;
@@ -114,155 +353,82 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(AttnArgs p) {
         for (int e = 0; e < 4; ++e) word |= e4m3_encode(qv[c][4 * w + e] / sq) << (8 * e);
         qb[c][w] = static_cast<int>(word);
       }
-    }
     const float t = sq * p.scale;
     cq = t * kLog2e;
   }
 
-  float m_run = -__builtin_inff(), l_run = 0.0f;
-  v16f acc[NDT];
-#pragma unroll
-  for (int T = 0; T < NDT; ++T)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[T][r] = 0.0f;
+  // mean of block 0 into the restoration ring (slot 0 of half 0)
+  if (threadIdx.x < D) {
+    const float ms = vm[threadIdx.x] / colv;
+    const uint32_t hi = bf16_bits(ms);
+    sM[(0 * D + threadIdx.x) * MS + 0] = static_cast<uint16_t>(hi);
+    sM[(1 * D + threadIdx.x) * MS + 0] = static_cast<uint16_t>(bf16_bits(ms - bf16_val(hi)));
+  }
 
-  const uint8_t* kq = p.Kq + static_cast<size_t>(bh) * nblk * KVB * D;
-  const uint8_t* vr = p.Vres + static_cast<size_t>(bh) * nblk * NKS * D * VROW;
-  const float* ks = p.k_scale + static_cast<size_t>(bh) * nblk;
-  const float* vm = p.v_mean + static_cast<size_t>(bh) * nblk * D;
+  SoftmaxState<NDT, MS> st;
+  st.m_run = -__builtin_inff();
+  st.l_run = 0.0f;
+#pragma unroll
+  for (int T = 0; T < NDT; ++T) st.acc[T] = v16f{};
+#pragma unroll
+  for (int i = 0; i < MS; ++i) st.RS[i] = 0.0f;
 
-  for (int b = 0; b < nblk; ++b) {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  const int ntail = N - (nblk - 1) * KVB;            // real keys of the last block
+  const int nfull = ntail < KVB ? nblk - 1 : nblk;   // blocks without padded keys
+
+  // after block b: stage the mean of block b+1 into its ring slot, wait for
+  // block b+1's direct loads, and make both visible to the workgroup
+  auto finish = [&](int b, float mnext) {
+    if (b + 1 < nblk && threadIdx.x < D) {
+      const int nb = b + 1;
+      const float ms = mnext / colv;
+      const uint32_t hi = bf16_bits(ms);
+      uint16_t* mh = sM + ((nb >> 3) & 1) * 2 * D * MS;
+      mh[(0 * D + threadIdx.x) * MS + (nb & (MS - 1))] = static_cast<uint16_t>(hi);
+      mh[(1 * D + threadIdx.x) * MS + (nb & (MS - 1))] = static_cast<uint16_t>(bf16_bits(ms - bf16_val(hi)));
+    }
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    for (int i = threadIdx.x; i < KVB * D / 16; i += 256) {
-      const int r = i / (D / 16), q16 = i % (D / 16);
-      *reinterpret_cast<uint4*>(sK + r * KSTR + q16 * 16) =
-          *reinterpret_cast<const uint4*>(kq + static_cast<size_t>(b) * KVB * D + r * D + q16 * 16);
+  };
+  auto prefetch = [&](int b) -> float {
+    float mnext = 0.0f;
+    if (b + 1 < nblk) {
+      stage_block<D, KVB, VF>(stages + ((b + 1) & 1) * TT::STAGE, kq + static_cast<size_t>(b + 1) * KVB * D,
+                              vr + static_cast<size_t>(b + 1) * NKS * D * VROW,
+                              VF == 1 ? scb + static_cast<size_t>(b + 1) * (KVB / 32) * D : nullptr, lo, wave,
+                              lane);
+      if (threadIdx.x < D) mnext = vm[static_cast<size_t>(b + 1) * D + threadIdx.x];
     }
-    for (int i = threadIdx.x; i < NKS * D * VROW / 16; i += 256) {
-      const int row = i / (VROW / 16), q16 = i % (VROW / 16);
-      *reinterpret_cast<uint4*>(sV + row * VSTR + q16 * 16) =
-          *reinterpret_cast<const uint4*>(vr + (static_cast<size_t>(b) * NKS * D + row) * VROW + q16 * 16);
-    }
-    if constexpr (VF == 1) {
-      const uint8_t* sc = reinterpret_cast<const uint8_t*>(p.v_scale) +
-                          (static_cast<size_t>(bh) * nblk * (KVB / 32) + static_cast<size_t>(b) * (KVB / 32)) * D;
-      for (int i = threadIdx.x; i < (KVB / 32) * D / 16; i += 256)
-        *reinterpret_cast<uint4*>(sVs + i * 16) = *reinterpret_cast<const uint4*>(sc + i * 16);
-    }
-    if (threadIdx.x < D) {
-      const float mv = vm[static_cast<size_t>(b) * D + threadIdx.x];
-      sMean[threadIdx.x] = VF == 0 ? mv / sCol[threadIdx.x] : mv;
-    }
-    __syncthreads();
-
-    // ---- S^T = Kq . Qq^T ----
-    v16f S[NKT];
-#pragma unroll
-    for (int kt = 0; kt < NKT; ++kt) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) S[kt][r] = 0.0f;
-#pragma unroll
-      for (int c = 0; c < NDC; ++c) {
-        const v8i a = *reinterpret_cast<const v8i*>(sK + (kt * 32 + col) * KSTR + 64 * c + 32 * g);
-        S[kt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qb[c], S[kt], 0, 0, 0, 0, 0, 0);
-      }
-    }
-    const int nvalid = min(KVB, N - b * KVB);
-    if (nvalid < KVB) {
-#pragma unroll
-      for (int kt = 0; kt < NKT; ++kt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int kappa = (kt >> 1) * 64 + (kt & 1) * 32 + 16 * g + r;
-          if (kappa >= nvalid) S[kt][r] = -__builtin_inff();
-        }
-    }
-    float mx = -__builtin_inff();
-#pragma unroll
-    for (int kt = 0; kt < NKT; ++kt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[kt][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-
-    const float cb = cq * ks[b];
-    const float tmax = cb * mx;
-    const float m_new = fmaxf(m_run, tmax);
-    const float Bq = __builtin_fmaf(-8.0f, m_new, p.kc);
-    const float A8 = 8.0f * cb;
-    const float alpha = exp2f(m_run - m_new);
-
-    // ---- ExpCast bytes, packed straight into the PV B operand ----
-    v8i P[NKS];
-#pragma unroll
-    for (int s = 0; s < NKS; ++s)
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const v16f& st = S[2 * s + t];
-          P[s][4 * t + q4] = static_cast<int>(
-              expcast4(st[4 * q4], st[4 * q4 + 1], st[4 * q4 + 2], st[4 * q4 + 3], A8, Bq));
-        }
-    float rs = 0.0f;
-#pragma unroll
-    for (int s = 0; s < NKS; ++s)
-#pragma unroll
-      for (int w = 0; w < 8; ++w) rs += fp8x4_sum(static_cast<uint32_t>(P[s][w]));
-    rs += __shfl_xor(rs, 32, 64);
-    l_run = alpha * l_run + rs;
-
-#pragma unroll
-    for (int T = 0; T < NDT; ++T)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[T][r] *= alpha;
-
-    // ---- acc += Vres^T . P^T ----
-#pragma unroll
-    for (int s = 0; s < NKS; ++s)
-#pragma unroll
-      for (int T = 0; T < NDT; ++T) {
-        const uint8_t* vrow = sV + (s * D + 32 * T + col) * VSTR;
-        if constexpr (VF == 0) {
-          const uint4 lo = *reinterpret_cast<const uint4*>(vrow + 16 * g);
-          const uint4 hi = *reinterpret_cast<const uint4*>(vrow + 32 + 16 * g);
-          const v8i a = {static_cast<int>(lo.x), static_cast<int>(lo.y), static_cast<int>(lo.z), static_cast<int>(lo.w),
-                         static_cast<int>(hi.x), static_cast<int>(hi.y), static_cast<int>(hi.z), static_cast<int>(hi.w)};
-          acc[T] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, P[s], acc[T], 0, 0, 0, 0, 0, 0);
-        } else {
-          const uint4 q = *reinterpret_cast<const uint4*>(vrow + 16 * g);
-          const v8i a = {static_cast<int>(q.x), static_cast<int>(q.y), static_cast<int>(q.z), static_cast<int>(q.w),
-                         0, 0, 0, 0};
-          const int sc = sVs[(2 * s + g) * D + 32 * T + col];
-          acc[T] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, P[s], acc[T], 4, 0, 0, sc, 0, 127);
-        }
-      }
-    // ---- mean restoration from the block row sum ----
-#pragma unroll
-    for (int T = 0; T < NDT; ++T)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float4 mv = *reinterpret_cast<const float4*>(sMean + 32 * T + 8 * i + 4 * g);
-        acc[T][4 * i + 0] = __builtin_fmaf(rs, mv.x, acc[T][4 * i + 0]);
-        acc[T][4 * i + 1] = __builtin_fmaf(rs, mv.y, acc[T][4 * i + 1]);
-        acc[T][4 * i + 2] = __builtin_fmaf(rs, mv.z, acc[T][4 * i + 2]);
-        acc[T][4 * i + 3] = __builtin_fmaf(rs, mv.w, acc[T][4 * i + 3]);
-      }
-    m_run = m_new;
+    return mnext;
+  };
+  for (int b = 0; b < nfull; ++b) {
+    const float mnext = prefetch(b);
+    attn_block<D, KVB, VF, false>(st, stages + (b & 1) * TT::STAGE, sM + ((b >> 3) & 1) * 2 * D * MS, lo, qb,
+                                  cq * ks[b], p.kc, b, nblk, KVB, g, col);
+    finish(b, mnext);
+  }
+  if (nfull < nblk) {
+    const int b = nblk - 1;
+    attn_block<D, KVB, VF, true>(st, stages + (b & 1) * TT::STAGE, sM + ((b >> 3) & 1) * 2 * D * MS, lo, qb,
+                                 cq * ks[b], p.kc, b, nblk, ntail, g, col);
   }
 
   // ---- O = s_v * acc / l ----
   if (qrow < N) {
-    const float inv_l = 1.0f / l_run;
+    const float inv_l = 1.0f / st.l_run;
 #pragma unroll
     for (int T = 0; T < NDT; ++T)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int c0 = 32 * T + 8 * i + 4 * g;
         const float4 cs = *reinterpret_cast<const float4*>(sCol + c0);
-        const float o0 = acc[T][4 * i + 0] * cs.x * inv_l;
-        const float o1 = acc[T][4 * i + 1] * cs.y * inv_l;
-        const float o2 = acc[T][4 * i + 2] * cs.z * inv_l;
-        const float o3 = acc[T][4 * i + 3] * cs.w * inv_l;
+        const float o0 = st.acc[T][4 * i + 0] * cs.x * inv_l;
+        const float o1 = st.acc[T][4 * i + 1] * cs.y * inv_l;
+        const float o2 = st.acc[T][4 * i + 2] * cs.z * inv_l;
+        const float o3 = st.acc[T][4 * i + 3] * cs.w * inv_l;
         const size_t off = (static_cast<size_t>(bh) * N + qrow) * D + c0;
         if constexpr (O32) {
           *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.O) + off) = make_float4(o0, o1, o2, o3);
@@ -276,13 +442,29 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(AttnArgs p) {
 }
 
 template <int D, int KVB, int VF>
-static void launch_attn_t(const AttnArgs& a, hipStream_t st) {
+static constexpr size_t attn_smem_bytes() {
+  using TT = AttnTile<D, KVB, VF>;
+  return 2 * TT::STAGE + 2 * 2 * D * TT::MSLOT * 2 + D * 4 + 16;
+}
+
+template <int D, int KVB, int VF, int O32>
+static void launch_attn_o(const AttnArgs& a, hipStream_t st) {
+  constexpr size_t smem = attn_smem_bytes<D, KVB, VF>();
+  static bool attr_set = false;          // raising the limit is idempotent
+  if (!attr_set) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn_fwd<D, KVB, VF, O32>),
+                        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
+    attr_set = true;
+  }
   const int nqt = (a.N + kQTile - 1) / kQTile;
   const dim3 grid(static_cast<unsigned>(a.B * a.H * nqt));
-  if (a.out_fp32)
-    hipLaunchKernelGGL((k_attn_fwd<D, KVB, VF, 1>), grid, dim3(256), 0, st, a);
-  else
-    hipLaunchKernelGGL((k_attn_fwd<D, KVB, VF, 0>), grid, dim3(256), 0, st, a);
+  hipLaunchKernelGGL((k_attn_fwd<D, KVB, VF, O32>), grid, dim3(256), smem, st, a);
+}
+
+template <int D, int KVB, int VF>
+static void launch_attn_t(const AttnArgs& a, hipStream_t st) {
+  if (a.out_fp32) launch_attn_o<D, KVB, VF, 1>(a, st);
+  else launch_attn_o<D, KVB, VF, 0>(a, st);
 }
 
 template <int D, int KVB>
