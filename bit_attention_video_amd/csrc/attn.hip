@@ -57,14 +57,18 @@ __global__ void k_dbg_expcast(const float* __restrict__ S, const float* __restri
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef __attribute__((address_space(1))) void* glb_ptr_t;
 
-// Swizzled 16-byte chunk inside an LDS row of RB bytes: consecutive rows that
-// share a 128-byte bank line get different chunk positions, so the 16-byte
-// operand reads of 8 consecutive rows hit distinct banks.
+// Swizzled 16-byte chunk inside an LDS row of RB bytes.  A 16-byte operand
+// read is served 8 lanes per cycle from 32 banks or 16 lanes per cycle from
+// 64 banks; the XOR below gives the consecutive rows read together distinct
+// bank groups in both cases (rows sharing a 128-byte line differ in the bits
+// above the line index, rows sharing a 256-byte line in the next bit up).
 template <int RB>
 __device__ __forceinline__ int swz(int row, int chunk) {
-  constexpr int CPR = RB / 16;          // chunks per row
-  constexpr int RPL = 128 / RB;         // rows per 128-byte line
-  return chunk ^ ((row / RPL) & (CPR - 1));
+  // the XOR uses only row bits 0..3, so tiles and load rounds that start at
+  // multiples of 32 rows share one per-lane pattern
+  if constexpr (RB == 128) return chunk ^ ((row & 7) ^ ((row >> 3) & 1));
+  else if constexpr (RB == 64) return chunk ^ (((row >> 1) ^ (row >> 2)) & 3);
+  else return chunk ^ (((row >> 2) ^ (row >> 3)) & 1);
 }
 
 // max of v over lanes l and l^32 (v_permlane32_swap returns both halves)
@@ -144,7 +148,11 @@ __device__ __forceinline__ void stage_block(uint8_t* st, const uint8_t* kq_blk, 
   }
 }
 
-__device__ __forceinline__ uint32_t bf16_bits(float f) { return f32_to_bf16_rne(f); }
+// bf16 round-to-nearest-even of a finite value (row sums and block means)
+__device__ __forceinline__ uint32_t bf16_bits(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
 __device__ __forceinline__ float bf16_val(uint32_t b) { return __uint_as_float(b << 16); }
 
 __device__ __forceinline__ v8i join8(uint4 lo, uint4 hi) {
@@ -204,23 +212,7 @@ __device__ __forceinline__ void attn_block(
   const float Bq = __builtin_fmaf(-8.0f, m_new, kc);
   const float A8 = 8.0f * cb;
 
-  v8i P[NKS];
-#pragma unroll
-  for (int s = 0; s < NKS; ++s)
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const v16f& sv = S[2 * s + t];
-        P[s][4 * t + q4] =
-            static_cast<int>(expcast4(sv[4 * q4], sv[4 * q4 + 1], sv[4 * q4 + 2], sv[4 * q4 + 3], A8, Bq));
-      }
-  // row sums of the decoded bytes on the matrix core: ones(FP4) . P^T, exact
-  v16f rsum = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, P[0], v16f{}, 4, 0, 0, 127, 0, 127);
-#pragma unroll
-  for (int s = 1; s < NKS; ++s)
-    rsum = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, P[s], rsum, 4, 0, 0, 127, 0, 127);
-
+  // the accumulator moves to the new maximum before this block's P.V lands
   if (__builtin_amdgcn_ballot_w64(m_new > st.m_run)) {
     const float alpha = exp2f(st.m_run - m_new);
 #pragma unroll
@@ -233,23 +225,38 @@ __device__ __forceinline__ void attn_block(
   }
   st.m_run = m_new;
 
+  // per 64-key step: ExpCast bytes straight into the PV B operand, then the
+  // row-sum and P.V MFMAs (the next step's bytes overlap these MFMAs)
+  v16f rsum;
 #pragma unroll
-  for (int s = 0; s < NKS; ++s)
+  for (int s = 0; s < NKS; ++s) {
+    v8i P;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const v16f& sv = S[2 * s + t];
+        P[4 * t + q4] =
+            static_cast<int>(expcast4(sv[4 * q4], sv[4 * q4 + 1], sv[4 * q4 + 2], sv[4 * q4 + 3], A8, Bq));
+      }
+    // row sums of the decoded bytes on the matrix core: ones(FP4) . P^T, exact
+    rsum = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, P, s == 0 ? v16f{} : rsum, 4, 0, 0, 127, 0, 127);
 #pragma unroll
     for (int T = 0; T < NDT; ++T) {
       const uint8_t* vb = sV + (s * D + 32 * T) * VROW;
       if constexpr (VF == 0) {
         const v8i a = join8(*reinterpret_cast<const uint4*>(vb + lo.v_rd[0]),
                             *reinterpret_cast<const uint4*>(vb + lo.v_rd[1]));
-        st.acc[T] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, P[s], st.acc[T], 0, 0, 0, 0, 0, 0);
+        st.acc[T] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, P, st.acc[T], 0, 0, 0, 0, 0, 0);
       } else {
         const uint4 q = *reinterpret_cast<const uint4*>(vb + lo.v_rd[0]);
         const v8i a = {static_cast<int>(q.x), static_cast<int>(q.y), static_cast<int>(q.z), static_cast<int>(q.w),
                        0, 0, 0, 0};
         const int sc = sS[(2 * s + g) * D + 32 * T + col];
-        st.acc[T] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, P[s], st.acc[T], 4, 0, 0, sc, 0, 127);
+        st.acc[T] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, P, st.acc[T], 4, 0, 0, sc, 0, 127);
       }
     }
+  }
   const float rs = rsum[0];
   st.l_run += rs;
   const int slot = b & (MS - 1);
@@ -317,6 +324,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(AttnArgs p) {
     if (VF == 0) colv = reinterpret_cast<const float*>(p.v_scale)[static_cast<size_t>(bh) * D + threadIdx.x];
     sCol[threadIdx.x] = colv;
   }
+  const float rcol = 1.0f / colv;   // block means enter the accumulator in residual units
 
   // ---- query tile: E4M3 codes with one scale per 128 rows ----
   v8i qb[NDC];
@@ -359,7 +367,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(AttnArgs p) {
 
   // mean of block 0 into the restoration ring (slot 0 of half 0)
   if (threadIdx.x < D) {
-    const float ms = vm[threadIdx.x] / colv;
+    const float ms = vm[threadIdx.x] * rcol;
     const uint32_t hi = bf16_bits(ms);
     sM[(0 * D + threadIdx.x) * MS + 0] = static_cast<uint16_t>(hi);
     sM[(1 * D + threadIdx.x) * MS + 0] = static_cast<uint16_t>(bf16_bits(ms - bf16_val(hi)));
@@ -384,7 +392,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(AttnArgs p) {
   auto finish = [&](int b, float mnext) {
     if (b + 1 < nblk && threadIdx.x < D) {
       const int nb = b + 1;
-      const float ms = mnext / colv;
+      const float ms = mnext * rcol;
       const uint32_t hi = bf16_bits(ms);
       uint16_t* mh = sM + ((nb >> 3) & 1) * 2 * D * MS;
       mh[(0 * D + threadIdx.x) * MS + (nb & (MS - 1))] = static_cast<uint16_t>(hi);
