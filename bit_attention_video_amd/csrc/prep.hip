@@ -20,37 +20,46 @@ __global__ void k_fill_u32(uint32_t* __restrict__ p, uint32_t v, size_t n) {
 }
 
 // Per chunk of tokens: fp64 per-channel sums of K (for its mean) and the
-// max |V| of the head (for the int8 k-means scale) and max |V| per channel.
+// max |V| of the head (for the int8 k-means scale).  Each thread reads
+// 16-byte pieces (8 channels) of every RG-th row; partial sums are combined
+// in a fixed order.
 template <int D>
 __global__ __launch_bounds__(256) void k_stats_partial(const uint16_t* __restrict__ K,
                                                        const uint16_t* __restrict__ V, int N,
                                                        int nch, double* __restrict__ kpart,
                                                        uint32_t* __restrict__ vamax) {
-  constexpr int SUB = 256 / D;
-  __shared__ double sK[256];
+  constexpr int CG = D / 8;          // 16-byte channel groups per row
+  constexpr int RG = 256 / CG;       // rows read in parallel
+  __shared__ double sK[RG][D];
   __shared__ float sMax[4];
   const int bh = blockIdx.y, ch = blockIdx.x;
-  const int c = threadIdx.x % D, sub = threadIdx.x / D;
-  const size_t base = static_cast<size_t>(bh) * N * D;
+  const int cg = threadIdx.x % CG, r0 = threadIdx.x / CG;
+  const size_t base = static_cast<size_t>(bh) * N * D + cg * 8;
   const int t0 = ch * kStatChunk, t1 = min(N, t0 + kStatChunk);
-  double ks = 0.0;
+  double ks[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   float vm = 0.0f;
-  for (int t = t0 + sub; t < t1; t += SUB) {
-    const size_t o = base + static_cast<size_t>(t) * D + c;
-    ks += static_cast<double>(bf16_to_f32(K[o]));
-    vm = fmaxf(vm, fabsf(bf16_to_f32(V[o])));
+  for (int t = t0 + r0; t < t1; t += RG) {
+    const uint4 kr = *reinterpret_cast<const uint4*>(K + base + static_cast<size_t>(t) * D);
+    const uint4 vr = *reinterpret_cast<const uint4*>(V + base + static_cast<size_t>(t) * D);
+    const uint32_t kw[4] = {kr.x, kr.y, kr.z, kr.w}, vw[4] = {vr.x, vr.y, vr.z, vr.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      ks[e] += static_cast<double>(bf16_to_f32(static_cast<uint16_t>(kw[e >> 1] >> ((e & 1) * 16))));
+      vm = fmaxf(vm, fabsf(bf16_to_f32(static_cast<uint16_t>(vw[e >> 1] >> ((e & 1) * 16)))));
+    }
   }
-  sK[threadIdx.x] = ks;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) sK[r0][cg * 8 + e] = ks[e];
   vm = wave_max(vm);
   if ((threadIdx.x & 63) == 0) sMax[threadIdx.x >> 6] = vm;
   __syncthreads();
   if (threadIdx.x < D) {
     double s = 0.0;
-    for (int j = 0; j < SUB; ++j) s += sK[j * D + threadIdx.x];
+    for (int j = 0; j < RG; ++j) s += sK[j][threadIdx.x];
     kpart[(static_cast<size_t>(bh) * nch + ch) * D + threadIdx.x] = s;
   }
   if (threadIdx.x == 0) {
-    float m = fmaxf(fmaxf(sMax[0], sMax[1]), fmaxf(sMax[2], sMax[3]));
+    const float m = fmaxf(fmaxf(sMax[0], sMax[1]), fmaxf(sMax[2], sMax[3]));
     atomicMax(vamax + bh, __float_as_uint(m));
   }
 }
@@ -304,12 +313,13 @@ __global__ __launch_bounds__(256) void k_sort_scatter(const int32_t* __restrict_
 }
 
 // New centroid = fp32(fp64 mean of the members' values), summed in sorted
-// (= token) order; an empty cluster keeps its centroid.
+// (= token) order; an empty cluster keeps its centroid.  Member loads are
+// issued 8 at a time (independent), the additions stay in member order.
 template <int D>
-__global__ void k_kmeans_update(const uint16_t* __restrict__ V, const int32_t* __restrict__ perm,
-                                const int32_t* __restrict__ counts,
-                                const int32_t* __restrict__ starts, int N, int k,
-                                float* __restrict__ C) {
+__global__ __launch_bounds__(D) void k_kmeans_update(const uint16_t* __restrict__ V, const int32_t* __restrict__ perm,
+                                                     const int32_t* __restrict__ counts,
+                                                     const int32_t* __restrict__ starts, int N, int k,
+                                                     float* __restrict__ C) {
   const int bh = blockIdx.y, i = blockIdx.x, c = threadIdx.x;
   const int cnt = counts[static_cast<size_t>(bh) * k + i];
   if (cnt == 0) return;
@@ -317,7 +327,15 @@ __global__ void k_kmeans_update(const uint16_t* __restrict__ V, const int32_t* _
   const int32_t* pp = perm + static_cast<size_t>(bh) * N + s;
   const uint16_t* vv = V + static_cast<size_t>(bh) * N * D + c;
   double sum = 0.0;
-  for (int j = 0; j < cnt; ++j) sum += static_cast<double>(bf16_to_f32(vv[static_cast<size_t>(pp[j]) * D]));
+  int j = 0;
+  for (; j + 8 <= cnt; j += 8) {
+    float x[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) x[u] = bf16_to_f32(vv[static_cast<size_t>(pp[j + u]) * D]);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) sum += static_cast<double>(x[u]);
+  }
+  for (; j < cnt; ++j) sum += static_cast<double>(bf16_to_f32(vv[static_cast<size_t>(pp[j]) * D]));
   C[(static_cast<size_t>(bh) * k + i) * D + c] = static_cast<float>(sum / static_cast<double>(cnt));
 }
 
@@ -327,67 +345,141 @@ __global__ void k_iota(int32_t* __restrict__ perm, int N, size_t total) {
 }
 
 // ---- V-Smooth residuals -----------------------------------------------------------
-// Block mean over the block's real tokens (fp64, sorted order) and, for E4M3,
-// the per-channel max |v - mean| of the head.
-template <int D>
-__global__ void k_vblock_stats(const uint16_t* __restrict__ V, const int32_t* __restrict__ perm,
-                               int N, int kvb, int nblk, int vsmooth, int want_amax,
-                               float* __restrict__ v_mean, uint32_t* __restrict__ vramax) {
-  const int bh = blockIdx.y, b = blockIdx.x, c = threadIdx.x;
-  const int p0 = b * kvb, nv = min(kvb, N - p0);
-  const int32_t* pp = perm + static_cast<size_t>(bh) * N + p0;
-  const uint16_t* vv = V + static_cast<size_t>(bh) * N * D + c;
-  float mean = 0.0f;
-  if (vsmooth) {
-    double s = 0.0;
-    for (int j = 0; j < nv; ++j) s += static_cast<double>(bf16_to_f32(vv[static_cast<size_t>(pp[j]) * D]));
-    mean = static_cast<float>(s / static_cast<double>(nv));
+// A workgroup owns one block.  Thread (cg, q) holds channels 8cg..8cg+7 of
+// the sorted positions 4q..4q+3 (+ 4*RQ per pass), read as whole 16-byte
+// pieces of the gathered rows and kept in registers.
+template <int D, int KVB>
+struct BlockRows {
+  static constexpr int CG = D / 8;            // channel groups of 8
+  static constexpr int RQ = 256 / CG;         // 4-row quads covered per pass
+  static constexpr int PASS = (KVB / 4 + RQ - 1) / RQ;
+  float v[PASS][4][8];
+  __device__ __forceinline__ void load(const uint16_t* vv, const int32_t* pp, int p0, int N) {
+    const int cg = threadIdx.x % CG, q = threadIdx.x / CG;
+#pragma unroll
+    for (int ps = 0; ps < PASS; ++ps)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int r = (ps * RQ + q) * 4 + rr;
+        const int pos = p0 + r;
+        uint4 raw = make_uint4(0u, 0u, 0u, 0u);
+        if (r < KVB && pos < N) raw = *reinterpret_cast<const uint4*>(vv + static_cast<size_t>(pp[pos]) * D + cg * 8);
+        const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[ps][rr][e] = bf16_to_f32(static_cast<uint16_t>(w[e >> 1] >> ((e & 1) * 16)));
+      }
   }
-  v_mean[(static_cast<size_t>(bh) * nblk + b) * D + c] = mean;
-  if (want_amax) {
-    float am = 0.0f;
-    for (int j = 0; j < nv; ++j) {
-      const float r = bf16_to_f32(vv[static_cast<size_t>(pp[j]) * D]) - mean;
-      am = fmaxf(am, fabsf(r));
+};
+
+// Block mean over the block's real tokens (fp64) and, for E4M3, the
+// per-channel max |v - mean| of the head.
+template <int D, int KVB>
+__global__ __launch_bounds__(256) void k_vblock_stats(const uint16_t* __restrict__ V, const int32_t* __restrict__ perm,
+                                                      int N, int nblk, int vsmooth, int want_amax,
+                                                      float* __restrict__ v_mean, uint32_t* __restrict__ vramax) {
+  using BR = BlockRows<D, KVB>;
+  __shared__ double sPart[BR::RQ][D];
+  __shared__ float sMean[D];
+  __shared__ float sAm[BR::RQ][D];
+  const int bh = blockIdx.y, b = blockIdx.x;
+  const int p0 = b * KVB, nv = min(KVB, N - p0);
+  const int cg = threadIdx.x % BR::CG, q = threadIdx.x / BR::CG;
+  BR rows;
+  rows.load(V + static_cast<size_t>(bh) * N * D, perm + static_cast<size_t>(bh) * N, p0, N);
+  if (vsmooth) {
+    double ps[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+    for (int pass = 0; pass < BR::PASS; ++pass)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ps[e] += static_cast<double>(rows.v[pass][rr][e]);   // padded rows hold 0
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sPart[q][cg * 8 + e] = ps[e];
+    __syncthreads();
+    if (threadIdx.x < D) {
+      double sm = 0.0;
+      for (int j = 0; j < BR::RQ; ++j) sm += sPart[j][threadIdx.x];
+      sMean[threadIdx.x] = static_cast<float>(sm / static_cast<double>(nv));
     }
-    atomicMax(vramax + static_cast<size_t>(bh) * D + c, __float_as_uint(am));
+  } else if (threadIdx.x < D) {
+    sMean[threadIdx.x] = 0.0f;
+  }
+  __syncthreads();
+  if (threadIdx.x < D) v_mean[(static_cast<size_t>(bh) * nblk + b) * D + threadIdx.x] = sMean[threadIdx.x];
+  if (!want_amax) return;
+  float am[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+  for (int pass = 0; pass < BR::PASS; ++pass)
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int r = (pass * BR::RQ + q) * 4 + rr;
+      if (r < nv) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) am[e] = fmaxf(am[e], fabsf(rows.v[pass][rr][e] - sMean[cg * 8 + e]));
+      }
+    }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) sAm[q][cg * 8 + e] = am[e];
+  __syncthreads();
+  if (threadIdx.x < D) {
+    float m = 0.0f;
+    for (int j = 0; j < BR::RQ; ++j) m = fmaxf(m, sAm[j][threadIdx.x]);
+    atomicMax(vramax + static_cast<size_t>(bh) * D + threadIdx.x, __float_as_uint(m));
   }
 }
 
-// E4M3 residual codes in the [Np/64][d][64] layout with the per-channel scale
-// s_v = fp32(max|r| / 448); position-ordered rows of 64 codes per channel.
-template <int D>
+// E4M3 residual codes with the per-channel scale s_v = fp32(max|r| / 448),
+// transposed through LDS into the [Np/64][d][64] layout.
+template <int D, int KVB>
 __global__ __launch_bounds__(256) void k_vres_e4m3(const uint16_t* __restrict__ V,
                                                    const int32_t* __restrict__ perm,
                                                    const float* __restrict__ v_mean,
-                                                   const uint32_t* __restrict__ vramax, int N,
-                                                   int kvb, int nblk, uint8_t* __restrict__ Vres,
-                                                   float* __restrict__ v_scale) {
+                                                   const uint32_t* __restrict__ vramax, int N, int nblk,
+                                                   uint8_t* __restrict__ Vres, float* __restrict__ v_scale) {
+  using BR = BlockRows<D, KVB>;
+  __shared__ float sMean[D];
+  __shared__ float sS[D];
+  __shared__ __attribute__((aligned(16))) uint32_t sT[D][KVB / 4 + 1];   // codes [channel][position/4]
   const int bh = blockIdx.y, b = blockIdx.x;
-  const int p0 = b * kvb;
-  const int32_t* pp = perm + static_cast<size_t>(bh) * N;
-  const uint16_t* vv = V + static_cast<size_t>(bh) * N * D;
-  const float* mean = v_mean + (static_cast<size_t>(bh) * nblk + b) * D;
-  for (int w = threadIdx.x; w < D * kvb / 4; w += 256) {
-    const int c = w % D, p4 = (w / D) * 4;
-    const float am = __uint_as_float(vramax[static_cast<size_t>(bh) * D + c]);
-    const float s = am > 0.0f ? am / 448.0f : 1.0f;
-    if (b == 0 && p4 == 0) v_scale[static_cast<size_t>(bh) * D + c] = s;
-    const float mc = mean[c];
-    uint32_t word = 0;
+  const int p0 = b * KVB;
+  const int cg = threadIdx.x % BR::CG, q = threadIdx.x / BR::CG;
+  if (threadIdx.x < D) {
+    const float am = __uint_as_float(vramax[static_cast<size_t>(bh) * D + threadIdx.x]);
+    const float sc = am > 0.0f ? am / 448.0f : 1.0f;
+    sS[threadIdx.x] = sc;
+    sMean[threadIdx.x] = v_mean[(static_cast<size_t>(bh) * nblk + b) * D + threadIdx.x];
+    if (b == 0) v_scale[static_cast<size_t>(bh) * D + threadIdx.x] = sc;
+  }
+  BR rows;
+  rows.load(V + static_cast<size_t>(bh) * N * D, perm + static_cast<size_t>(bh) * N, p0, N);
+  __syncthreads();
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int pos = p0 + p4 + e;
-      uint32_t code = 0;
-      if (pos < N) {
-        const float r = bf16_to_f32(vv[static_cast<size_t>(pp[pos]) * D + c]) - mc;
-        code = e4m3_encode(r / s);
+  for (int pass = 0; pass < BR::PASS; ++pass) {
+    const int r4 = pass * BR::RQ + q;            // quad index (positions 4r4..4r4+3)
+    if (r4 * 4 < KVB) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int c = cg * 8 + e;
+        uint32_t word = 0u;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int pos = p0 + r4 * 4 + rr;
+          const uint32_t code = pos < N ? e4m3_encode((rows.v[pass][rr][e] - sMean[c]) / sS[c]) : 0u;
+          word |= code << (8 * rr);
+        }
+        sT[c][r4] = word;
       }
-      word |= code << (8 * e);
     }
-    const int gpos = p0 + p4;
-    *reinterpret_cast<uint32_t*>(Vres + ((static_cast<size_t>(bh) * (nblk * kvb / 64) + gpos / 64) * D + c) * 64 +
-                                 (gpos & 63)) = word;
+  }
+  __syncthreads();
+  // output: per 64-position step, D rows of 64 bytes = 16 words per channel
+  uint32_t* out = reinterpret_cast<uint32_t*>(Vres + (static_cast<size_t>(bh) * nblk * KVB + p0) * D);
+  for (int i = threadIdx.x; i < (KVB / 64) * D * 4; i += 256) {   // 16-byte pieces
+    const int step = i / (D * 4), rem = i % (D * 4), c = rem / 4, part = rem % 4;
+    const uint32_t* src = &sT[c][step * 16 + part * 4];
+    *reinterpret_cast<uint4*>(out + (static_cast<size_t>(step) * D + c) * 16 + part * 4) =
+        make_uint4(src[0], src[1], src[2], src[3]);
   }
 }
 
@@ -544,7 +636,7 @@ hipError_t launch_sort(const PrepArgs& a, const int32_t* labels, int32_t* perm, 
 
 template <int D>
 static hipError_t update_t(const PrepArgs& a, const int32_t* perm, hipStream_t st) {
-  hipLaunchKernelGGL(k_kmeans_update<D>, dim3(a.k, a.B * a.H), dim3(D), 0, st, a.V, perm, a.counts, a.starts,
+  hipLaunchKernelGGL((k_kmeans_update<D>), dim3(a.k, a.B * a.H), dim3(D), 0, st, a.V, perm, a.counts, a.starts,
                      a.N, a.k, a.C);
   return hipGetLastError();
 }
@@ -557,28 +649,25 @@ hipError_t launch_iota(int32_t* perm, int N, size_t total, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, int KVB>
 static hipError_t vres_t(const PrepArgs& a, const int32_t* perm, const PrepOut& o, hipStream_t st) {
   const int BH = a.B * a.H;
   const int e4 = a.v_format == 0;
-  hipLaunchKernelGGL(k_vblock_stats<D>, dim3(a.nblk, BH), dim3(D), 0, st, a.V, perm, a.N, a.kvb, a.nblk,
+  hipLaunchKernelGGL((k_vblock_stats<D, KVB>), dim3(a.nblk, BH), dim3(256), 0, st, a.V, perm, a.N, a.nblk,
                      a.vsmooth, e4, o.v_mean, a.vramax);
   if (e4)
-    hipLaunchKernelGGL(k_vres_e4m3<D>, dim3(a.nblk, BH), dim3(256), 0, st, a.V, perm, o.v_mean, a.vramax, a.N,
-                       a.kvb, a.nblk, o.Vres, reinterpret_cast<float*>(o.v_scale));
+    hipLaunchKernelGGL((k_vres_e4m3<D, KVB>), dim3(a.nblk, BH), dim3(256), 0, st, a.V, perm, o.v_mean, a.vramax,
+                       a.N, a.nblk, o.Vres, reinterpret_cast<float*>(o.v_scale));
   else
     hipLaunchKernelGGL(k_vres_mxfp4<D>, dim3(a.nblk, BH), dim3(256), 0, st, a.V, perm, o.v_mean, a.N, a.kvb,
                        a.nblk, o.Vres, reinterpret_cast<uint8_t*>(o.v_scale));
-  if (a.kvb == 64)
-    hipLaunchKernelGGL((k_ksmooth<D, 64>), dim3(a.nblk, BH), dim3(256), 0, st, a.K, perm, a.mu, a.N, a.nblk,
-                       o.Kq, o.k_scale);
-  else
-    hipLaunchKernelGGL((k_ksmooth<D, 128>), dim3(a.nblk, BH), dim3(256), 0, st, a.K, perm, a.mu, a.N, a.nblk,
-                       o.Kq, o.k_scale);
+  hipLaunchKernelGGL((k_ksmooth<D, KVB>), dim3(a.nblk, BH), dim3(256), 0, st, a.K, perm, a.mu, a.N, a.nblk, o.Kq,
+                     o.k_scale);
   return hipGetLastError();
 }
 hipError_t launch_vres_ksmooth(const PrepArgs& a, const int32_t* perm, const PrepOut& o, hipStream_t st) {
-  return a.d == 64 ? vres_t<64>(a, perm, o, st) : vres_t<128>(a, perm, o, st);
+  if (a.d == 64) return a.kvb == 64 ? vres_t<64, 64>(a, perm, o, st) : vres_t<64, 128>(a, perm, o, st);
+  return a.kvb == 64 ? vres_t<128, 64>(a, perm, o, st) : vres_t<128, 128>(a, perm, o, st);
 }
 
 }  // namespace vc
