@@ -1,0 +1,98 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+declared in include/vcattn.h, and rejects invalid arguments with the right
+status before anything is launched (all calls below fail validation, so no
+device work is ever enqueued)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from bit_attention_video_amd import binding as vb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "vcattn.h")
+
+VC_OK, VC_ERR_INVALID_ARG, VC_ERR_UNSUPPORTED, VC_ERR_WORKSPACE = 0, -1, -2, -3
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if n.startswith(("vc", "vsmooth"))))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(vb.LIB_PATH):
+        pytest.skip("libvcattn.so not built")
+    return vb.lib()
+
+
+def test_header_declares_expected_entry_points():
+    names = declared_functions()
+    for want in ("vsmooth_prepare", "vc_attn_fwd", "vc_attention", "vc_prepare_workspace_bytes",
+                 "vc_attention_workspace_bytes", "vc_status_str", "vc_last_error", "vc_dbg_expcast",
+                 "vc_dbg_kmeans_assign", "vc_dbg_sort"):
+        assert want in names, want
+
+
+def test_library_exports_every_declared_symbol(lib):
+    raw = ctypes.CDLL(vb.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(raw, name), f"{name} not exported"
+
+
+def cfg(**kw):
+    base = dict(B=1, H=2, N=1000, d=64, kv_block=64, n_clusters=16, iters=3)
+    base.update(kw)
+    return vb.make_config(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=96), VC_ERR_UNSUPPORTED),
+    (dict(kv_block=32), VC_ERR_UNSUPPORTED),
+    (dict(N=0), VC_ERR_INVALID_ARG),
+    (dict(n_clusters=0), VC_ERR_INVALID_ARG),
+    (dict(n_clusters=1001), VC_ERR_INVALID_ARG),      # k > N
+    (dict(n_clusters=5000, N=10000), VC_ERR_INVALID_ARG),
+    (dict(iters=0), VC_ERR_INVALID_ARG),
+    (dict(beta=0.5), VC_ERR_INVALID_ARG),
+    (dict(beta=-0.6), VC_ERR_INVALID_ARG),
+    (dict(v_format=2), VC_ERR_UNSUPPORTED),
+])
+def test_invalid_config_rejected_before_launch(lib, kw, status):
+    c = cfg(**kw)
+    P = ctypes.c_void_p(16)      # never dereferenced: validation fails first
+    r = lib.vsmooth_prepare(ctypes.byref(c), P, P, P, P, P, P, P, P, P, None, P, 1 << 40, None)
+    assert r == status, (r, lib.vc_last_error())
+    assert lib.vc_last_error().decode()
+    assert lib.vc_prepare_workspace_bytes(ctypes.byref(c)) == 0
+
+
+def test_null_and_misaligned_pointers_rejected(lib):
+    c = cfg()
+    P = ctypes.c_void_p(256)
+    assert lib.vsmooth_prepare(ctypes.byref(c), None, P, P, P, P, P, P, P, P, None, P, 1 << 40, None) == VC_ERR_INVALID_ARG
+    bad = ctypes.c_void_p(258)
+    assert lib.vc_attn_fwd(ctypes.byref(c), bad, P, P, P, P, P, P, None) == VC_ERR_INVALID_ARG
+    assert "aligned" in lib.vc_last_error().decode()
+    assert lib.vc_attention(ctypes.byref(c), P, P, P, None, P, P, 1 << 40, None) == VC_ERR_INVALID_ARG  # no init
+    assert lib.vc_dbg_expcast(None, None, None, -1, None, None) == VC_ERR_INVALID_ARG
+
+
+def test_workspace_too_small_rejected(lib):
+    c = cfg()
+    need = lib.vc_prepare_workspace_bytes(ctypes.byref(c))
+    assert need > 0 and lib.vc_attention_workspace_bytes(ctypes.byref(c)) > need
+    P = ctypes.c_void_p(256)
+    r = lib.vsmooth_prepare(ctypes.byref(c), P, P, P, P, P, P, P, P, P, None, P, need - 1, None)
+    assert r == VC_ERR_WORKSPACE
+    assert lib.vc_status_str(r).decode() == "workspace too small"
+
+
+def test_workspace_sizes_grow_with_problem(lib):
+    small = lib.vc_attention_workspace_bytes(ctypes.byref(cfg()))
+    big = lib.vc_attention_workspace_bytes(ctypes.byref(cfg(N=4000)))
+    assert big > 3 * small
