@@ -14,7 +14,8 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libvcattn.so")
+# VCATTN_LIBRARY selects another build of the library (same ABI)
+LIB_PATH = os.environ.get("VCATTN_LIBRARY") or os.path.join(_HERE, "libvcattn.so")
 
 # ExpCast offset default: fp32(8/ln2 - 12), the value that centres
 # 8z + 56 + beta on the exact E4M3 code of 2^z over fractional z.

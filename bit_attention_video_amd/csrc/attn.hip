@@ -126,17 +126,22 @@ struct LaneOffsets {
 // [16i, 16i+16) after the wave-uniform base); the swizzle is applied on the
 // global side by choosing which chunk each lane fetches.
 template <int D, int KVB, int VF>
-__device__ __forceinline__ void stage_block(uint8_t* st, const uint8_t* kq_blk, const uint8_t* vr_blk,
-                                            const uint8_t* sc_blk, const LaneOffsets<D, KVB, VF>& lo, int wave,
-                                            int lane) {
+__device__ __forceinline__ void stage_block_k(uint8_t* st, const uint8_t* kq_blk, const LaneOffsets<D, KVB, VF>& lo,
+                                              int wave) {
   using T = AttnTile<D, KVB, VF>;
   using L = LaneOffsets<D, KVB, VF>;
-  static_assert((256 / (D / 16)) % 32 == 0 || L::KR == 1, "K rows per round must keep the swizzle");
 #pragma unroll
   for (int r = 0; r < L::KR; ++r)
     __builtin_amdgcn_global_load_lds((glb_ptr_t)(kq_blk + lo.k_src + r * 4096),
                                      (lds_ptr_t)(st + (r * 256 + wave * 64) * 16), 16, 0, 0);
-  uint8_t* sv = st + T::KBYTES;
+  (void)sizeof(T);
+}
+
+template <int D, int KVB, int VF>
+__device__ __forceinline__ void stage_block_v(uint8_t* sv, const uint8_t* vr_blk, const uint8_t* sc_blk,
+                                              const LaneOffsets<D, KVB, VF>& lo, int wave, int lane) {
+  using T = AttnTile<D, KVB, VF>;
+  using L = LaneOffsets<D, KVB, VF>;
 #pragma unroll
   for (int r = 0; r < L::VR; ++r)
     if ((r * 256 + wave * 64) * 16 < T::VBYTES)
@@ -168,30 +173,130 @@ struct SoftmaxState {
   float m_run, l_run;
 };
 
-// One KV block: S^T on FP8 MFMA, row max, ExpCast bytes, row sums (ones.P^T),
-// rescale, PV on FP8 / scaled FP8xFP4 MFMA, and every MSLOT blocks the mean
-// restoration flush.
-template <int D, int KVB, int VF, bool MASK>
-__device__ __forceinline__ void attn_block(
-    SoftmaxState<D / 32, AttnTile<D, KVB, VF>::MSLOT>& st, const uint8_t* sK, const uint16_t* sMhalf,
-    const LaneOffsets<D, KVB, VF>& lo, const v8i* qb, float cb, float kc, int b, int nblk, int nvalid,
-    int g, int col) {
+// S^T = Kq . Qq^T for one block (8 MFMAs at d=128).
+template <int D, int KVB, int VF>
+__device__ __forceinline__ void qk_block(v16f* S, const uint8_t* sK,
+                                         const LaneOffsets<D, KVB, VF>& lo, const v8i* qb) {
   using TT = AttnTile<D, KVB, VF>;
-  constexpr int NDC = TT::NDC, NKT = TT::NKT, NKS = TT::NKS, NDT = TT::NDT, VROW = TT::VROW, MS = TT::MSLOT;
-  const uint8_t* sV = sK + TT::KBYTES;
-  const uint8_t* sS = sV + TT::VBYTES;
-  const v8i ones = {0x22222222, 0x22222222, 0x22222222, 0x22222222, 0, 0, 0, 0};   // E2M1 1.0 (FP4 operand)
-
-  v16f S[NKT];
 #pragma unroll
-  for (int kt = 0; kt < NKT; ++kt) {
+  for (int kt = 0; kt < TT::NKT; ++kt)
 #pragma unroll
-    for (int c = 0; c < NDC; ++c) {
+    for (int c = 0; c < TT::NDC; ++c) {
       const v8i a = join8(*reinterpret_cast<const uint4*>(sK + kt * 32 * D + lo.k_rd[c][0]),
                           *reinterpret_cast<const uint4*>(sK + kt * 32 * D + lo.k_rd[c][1]));
       S[kt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qb[c], c == 0 ? v16f{} : S[kt], 0, 0, 0, 0, 0, 0);
     }
+}
+
+// compile-time loop: f(integral_constant<int, I>) for I = 0..N-1
+template <int N, int I = 0, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, I + 1>(static_cast<F&&>(f));
   }
+}
+
+// IEEE maximum (NaN-propagating, so no operand canonicalisation; gfx950 has a
+// three-input form).  Scores are never NaN; masked keys are -inf.
+__device__ __forceinline__ float fmax_ieee(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
+// running maximum over the 16 scores of one S^T tile register set
+__device__ __forceinline__ float tile_max(const v16f& t, float m) {
+#pragma unroll
+  for (int r = 0; r < 16; r += 2) m = fmax_ieee(fmax_ieee(m, t[r]), t[r + 1]);
+  return m;
+}
+__device__ __forceinline__ float tile_max(const v16f& t) {
+  float m = fmax_ieee(t[0], t[1]);
+#pragma unroll
+  for (int r = 2; r < 16; r += 2) m = fmax_ieee(fmax_ieee(m, t[r]), t[r + 1]);
+  return m;
+}
+
+// Issue order of one block step's matrix instructions.  Per 64-key step s:
+// the S^T MFMAs of the NEXT block for key tiles 2s and 2s+1 (NDC each), the
+// row-sum MFMA of this block's bytes P_s, then its NDT P.V MFMAs.  A score
+// tile is overwritten only after ExpCast has consumed it, so the bytes of
+// tile 0 are made first and the bytes of tiles 1.. are spread over the slots
+// behind the MFMAs (RATE words of four bytes per slot after the first NDC
+// slots, which carry tile 1); the next block's per-tile row maxima follow two
+// slots after the MFMAs that produce the tile.  The wave issues in order, so
+// vector work placed between two 64-cycle MFMAs runs in the matrix core's
+// shadow.
+template <int D, int KVB, int VF>
+struct StepPlan {
+  using TT = AttnTile<D, KVB, VF>;
+  static constexpr int NDC = TT::NDC, NKT = TT::NKT, NKS = TT::NKS, NDT = TT::NDT;
+  static constexpr int PER_S = 2 * NDC + 1 + NDT;
+  static constexpr int M = NKS * PER_S;          // MFMAs per step
+  static constexpr int NW = (NKT - 1) * 4;       // ExpCast words behind the MFMAs
+  static constexpr int RATE = NDC == 1 ? 2 : 1;
+  static constexpr int kind(int i) {             // 0: S^T, 1: row sum, 2: P.V
+    return i % PER_S < 2 * NDC ? 0 : i % PER_S == 2 * NDC ? 1 : 2;
+  }
+  static constexpr int step_of(int i) { return i / PER_S; }
+  static constexpr int qk_kt(int i) { return 2 * step_of(i) + (i % PER_S) / NDC; }
+  static constexpr int qk_c(int i) { return (i % PER_S) % NDC; }
+  static constexpr int pv_T(int i) { return i % PER_S - 2 * NDC - 1; }
+  static constexpr int qk_slot(int kt) { return (kt / 2) * PER_S + (kt % 2) * NDC; }
+  static constexpr int wbeg(int i) {
+    const int w = i < NDC ? i * (4 / NDC) : 4 + (i - NDC) * RATE;
+    return w < NW ? w : NW;
+  }
+  static constexpr int pm_slot(int kt) { return qk_slot(kt) + NDC + 1; }
+  static constexpr bool valid() {
+    for (int kt = 1; kt < NKT; ++kt)
+      if (wbeg(qk_slot(kt)) < 4 * kt) return false;   // tile kt's bytes made before it is overwritten
+    return wbeg(M) == NW;
+  }
+};
+
+// acc += (mean/s_v)^T . rowsums of the last MS blocks on v_mfma_f32_32x32x16_bf16
+// with both factors split into bf16 hi + lo (lane group 0 feeds the hi means,
+// group 1 the lo means); runs after a chunk of MS row sums is complete.
+template <int D, int KVB, int VF>
+__device__ __forceinline__ void mean_flush(SoftmaxState<D / 32, AttnTile<D, KVB, VF>::MSLOT>& st,
+                                           const uint16_t* sMhalf, int g, int col) {
+  using TT = AttnTile<D, KVB, VF>;
+  constexpr int NDT = TT::NDT, MS = TT::MSLOT;
+  v4i bhi, blo;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t h0 = bf16_bits(st.RS[2 * i]), h1 = bf16_bits(st.RS[2 * i + 1]);
+    const uint32_t l0 = bf16_bits(st.RS[2 * i] - bf16_val(h0)), l1 = bf16_bits(st.RS[2 * i + 1] - bf16_val(h1));
+    bhi[i] = static_cast<int>(h0 | (h1 << 16));
+    blo[i] = static_cast<int>(l0 | (l1 << 16));
+  }
+  typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+#pragma unroll
+  for (int T = 0; T < NDT; ++T) {
+    const v4i a = *reinterpret_cast<const v4i*>(sMhalf + (g * D + 32 * T + col) * MS);
+    st.acc[T] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, bhi),
+                                                        st.acc[T], 0, 0, 0);
+    st.acc[T] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, blo),
+                                                        st.acc[T], 0, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < MS; ++i) st.RS[i] = 0.0f;
+}
+
+// Row maximum, ExpCast, row sums and P.V of block b from its scores S, with
+// the next block's S^T (into the same registers, tile by tile) interleaved
+// as planned above.  pmax: per-lane maximum of S (before the cross-lane
+// step); on return it holds the next block's.
+template <int D, int KVB, int VF, bool MASK>
+__device__ __forceinline__ void block_step(
+    SoftmaxState<D / 32, AttnTile<D, KVB, VF>::MSLOT>& st, v16f* S, float& pmax,
+    const uint8_t* sV, const uint8_t* sKn, const LaneOffsets<D, KVB, VF>& lo, const v8i* qb,
+    float cb, float kc, int b, int nvalid, int g, int col) {
+  using TT = AttnTile<D, KVB, VF>;
+  using PL = StepPlan<D, KVB, VF>;
+  static_assert(PL::valid(), "step plan overwrites a score tile before its bytes are made");
+  constexpr int NKT = TT::NKT, NKS = TT::NKS, NDT = TT::NDT, VROW = TT::VROW, MS = TT::MSLOT;
+  const uint8_t* sS = sV + TT::VBYTES;
+  const v8i ones = {0x22222222, 0x22222222, 0x22222222, 0x22222222, 0, 0, 0, 0};   // E2M1 1.0 (FP4 operand)
+
   if constexpr (MASK) {
 #pragma unroll
     for (int kt = 0; kt < NKT; ++kt) {
@@ -200,14 +305,11 @@ __device__ __forceinline__ void attn_block(
       for (int r = 0; r < 16; ++r)
         if (r >= lim) S[kt][r] = -__builtin_inff();
     }
+    pmax = tile_max(S[0]);
+#pragma unroll
+    for (int kt = 1; kt < NKT; ++kt) pmax = tile_max(S[kt], pmax);
   }
-  float mx = -__builtin_inff();
-#pragma unroll
-  for (int kt = 0; kt < NKT; ++kt)
-#pragma unroll
-    for (int r = 0; r < 16; r += 2) mx = fmaxf(fmaxf(mx, S[kt][r]), S[kt][r + 1]);
-  mx = max_xor32(mx);
-
+  const float mx = max_xor32(pmax);
   const float m_new = fmaxf(st.m_run, cb * mx);
   const float Bq = __builtin_fmaf(-8.0f, m_new, kc);
   const float A8 = 8.0f * cb;
@@ -225,80 +327,113 @@ __device__ __forceinline__ void attn_block(
   }
   st.m_run = m_new;
 
-  // per 64-key step: ExpCast bytes straight into the PV B operand, then the
-  // row-sum and P.V MFMAs (the next step's bytes overlap these MFMAs)
+  v8i P[NKS];
   v16f rsum;
-#pragma unroll
-  for (int s = 0; s < NKS; ++s) {
-    v8i P;
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const v16f& sv = S[2 * s + t];
-        P[4 * t + q4] =
-            static_cast<int>(expcast4(sv[4 * q4], sv[4 * q4 + 1], sv[4 * q4 + 2], sv[4 * q4 + 3], A8, Bq));
-      }
-    // row sums of the decoded bytes on the matrix core: ones(FP4) . P^T, exact
-    rsum = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, P, s == 0 ? v16f{} : rsum, 4, 0, 0, 127, 0, 127);
-#pragma unroll
-    for (int T = 0; T < NDT; ++T) {
-      const uint8_t* vb = sV + (s * D + 32 * T) * VROW;
-      if constexpr (VF == 0) {
-        const v8i a = join8(*reinterpret_cast<const uint4*>(vb + lo.v_rd[0]),
-                            *reinterpret_cast<const uint4*>(vb + lo.v_rd[1]));
-        st.acc[T] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, P, st.acc[T], 0, 0, 0, 0, 0, 0);
-      } else {
-        const uint4 q = *reinterpret_cast<const uint4*>(vb + lo.v_rd[0]);
-        const v8i a = {static_cast<int>(q.x), static_cast<int>(q.y), static_cast<int>(q.z), static_cast<int>(q.w),
-                       0, 0, 0, 0};
-        const int sc = sS[(2 * s + g) * D + 32 * T + col];
-        st.acc[T] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, P, st.acc[T], 4, 0, 0, sc, 0, 127);
+  v8i opnd[3];
+  int osc[3];
+  (void)osc;
+  // operand of MFMA j into ring slot j % 3
+  auto load_opnd = [&](auto jc) {
+    constexpr int j = decltype(jc)::value;
+    if constexpr (j < PL::M) {
+      if constexpr (PL::kind(j) == 0) {
+        constexpr int kt = PL::qk_kt(j), c = PL::qk_c(j);
+        opnd[j % 3] = join8(*reinterpret_cast<const uint4*>(sKn + kt * 32 * D + lo.k_rd[c][0]),
+                            *reinterpret_cast<const uint4*>(sKn + kt * 32 * D + lo.k_rd[c][1]));
+      } else if constexpr (PL::kind(j) == 2) {
+        constexpr int sj = PL::step_of(j), T = PL::pv_T(j);
+        const uint8_t* vb = sV + (sj * D + 32 * T) * VROW;
+        if constexpr (VF == 0) {
+          opnd[j % 3] = join8(*reinterpret_cast<const uint4*>(vb + lo.v_rd[0]),
+                              *reinterpret_cast<const uint4*>(vb + lo.v_rd[1]));
+        } else {
+          const uint4 q = *reinterpret_cast<const uint4*>(vb + lo.v_rd[0]);
+          opnd[j % 3] = v8i{static_cast<int>(q.x), static_cast<int>(q.y), static_cast<int>(q.z),
+                            static_cast<int>(q.w), 0, 0, 0, 0};
+          osc[j % 3] = sS[(2 * sj + g) * D + 32 * T + col];
+        }
       }
     }
-  }
+  };
+  // ExpCast word w of the tiles behind tile 0 (tile 1 + w/4, word w%4)
+  auto ecast = [&](auto wc) {
+    constexpr int w = decltype(wc)::value;
+    constexpr int kt = 1 + w / 4, q = w % 4;
+    const v16f& sv = S[kt];
+    P[kt / 2][4 * (kt % 2) + q] =
+        static_cast<int>(expcast4(sv[4 * q], sv[4 * q + 1], sv[4 * q + 2], sv[4 * q + 3], A8, Bq));
+  };
+
+  load_opnd(std::integral_constant<int, 0>{});
+  load_opnd(std::integral_constant<int, 1>{});
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    P[0][q] = static_cast<int>(expcast4(S[0][4 * q], S[0][4 * q + 1], S[0][4 * q + 2], S[0][4 * q + 3], A8, Bq));
+  __builtin_amdgcn_sched_barrier(0);
+
+  static_for<PL::M>([&](auto ic) {
+    constexpr int i = decltype(ic)::value;
+    load_opnd(std::integral_constant<int, i + 2>{});
+    if constexpr (PL::kind(i) == 0) {
+      constexpr int kt = PL::qk_kt(i), c = PL::qk_c(i);
+      S[kt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(opnd[i % 3], qb[c], c == 0 ? v16f{} : S[kt], 0, 0,
+                                                             0, 0, 0, 0);
+    } else if constexpr (PL::kind(i) == 1) {
+      constexpr int sj = PL::step_of(i);
+      // row sums of the decoded bytes on the matrix core: ones(FP4) . P^T, exact
+      rsum = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, P[sj], sj == 0 ? v16f{} : rsum, 4, 0, 0, 127,
+                                                            0, 127);
+    } else {
+      constexpr int sj = PL::step_of(i), T = PL::pv_T(i);
+      if constexpr (VF == 0)
+        st.acc[T] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(opnd[i % 3], P[sj], st.acc[T], 0, 0, 0, 0, 0,
+                                                                   0);
+      else
+        st.acc[T] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(opnd[i % 3], P[sj], st.acc[T], 4, 0, 0,
+                                                                   osc[i % 3], 0, 127);
+    }
+    static_for<PL::wbeg(i + 1) - PL::wbeg(i)>([&](auto kc2) {
+      ecast(std::integral_constant<int, PL::wbeg(i) + decltype(kc2)::value>{});
+    });
+    static_for<NKT>([&](auto ktc) {
+      constexpr int kt = decltype(ktc)::value;
+      if constexpr (PL::pm_slot(kt) == i) pmax = kt == 0 ? tile_max(S[0]) : tile_max(S[kt], pmax);
+    });
+    __builtin_amdgcn_sched_barrier(0);
+  });
+  static_for<NKT>([&](auto ktc) {
+    constexpr int kt = decltype(ktc)::value;
+    if constexpr (PL::pm_slot(kt) >= PL::M) pmax = kt == 0 ? tile_max(S[0]) : tile_max(S[kt], pmax);
+  });
+
   const float rs = rsum[0];
   st.l_run += rs;
   const int slot = b & (MS - 1);
 #pragma unroll
   for (int i = 0; i < MS; ++i) st.RS[i] = i == slot ? rs : st.RS[i];
-
-  if (slot == MS - 1 || b == nblk - 1) {
-    // acc += (mean/s_v)^T . rowsums over the last MS blocks, on
-    // v_mfma_f32_32x32x16_bf16 with both factors split into bf16 hi + lo
-    // (lane group 0 feeds the hi means, group 1 the lo means)
-    v4i bhi, blo;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t h0 = bf16_bits(st.RS[2 * i]), h1 = bf16_bits(st.RS[2 * i + 1]);
-      const uint32_t l0 = bf16_bits(st.RS[2 * i] - bf16_val(h0)), l1 = bf16_bits(st.RS[2 * i + 1] - bf16_val(h1));
-      bhi[i] = static_cast<int>(h0 | (h1 << 16));
-      blo[i] = static_cast<int>(l0 | (l1 << 16));
-    }
-    typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
-#pragma unroll
-    for (int T = 0; T < NDT; ++T) {
-      const v4i a = *reinterpret_cast<const v4i*>(sMhalf + (g * D + 32 * T + col) * MS);
-      st.acc[T] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, bhi),
-                                                          st.acc[T], 0, 0, 0);
-      st.acc[T] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, blo),
-                                                          st.acc[T], 0, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < MS; ++i) st.RS[i] = 0.0f;
-  }
 }
 
+// The fused forward.  Per workgroup one 128-row query tile (4 waves x 32
+// rows).  Block b+1's S^T MFMAs run inside block b's step, so each block
+// starts with its scores ready: K is staged two blocks ahead and V one block
+// ahead, each in a two-slot LDS ring filled by direct global->LDS loads.
 template <int D, int KVB, int VF, int O32>
 __global__ __launch_bounds__(256, 2) void k_attn_fwd(AttnArgs p) {
   using TT = AttnTile<D, KVB, VF>;
-  constexpr int NDC = TT::NDC, NKS = TT::NKS, NDT = TT::NDT, VROW = TT::VROW;
+  constexpr int NDC = TT::NDC, NKT = TT::NKT, NKS = TT::NKS, NDT = TT::NDT, VROW = TT::VROW;
   constexpr int MS = TT::MSLOT;
-  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
-  uint8_t* stages = smem;                                            // 2 x STAGE bytes
-  uint16_t* sM = reinterpret_cast<uint16_t*>(smem + 2 * TT::STAGE); // [2 halves][2 hi/lo][D][MS]
-  float* sCol = reinterpret_cast<float*>(sM + 2 * 2 * D * MS);       // [D]
-  float* sRed = sCol + D;                                            // [4]
+  constexpr int VSTAGE = TT::VBYTES + (TT::SBYTES + 1023) / 1024 * 1024;
+  // Every ring slot is an LDS object of its own and every block step below
+  // names its slots at compile time: the compiler then knows that a step's
+  // operand reads do not touch the slots its direct loads are filling, and
+  // does not make those reads wait for the loads.
+  __shared__ __attribute__((aligned(1024))) uint8_t sK0[TT::KBYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t sK1[TT::KBYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t sV0[VSTAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t sV1[VSTAGE];
+  __shared__ __attribute__((aligned(16))) uint16_t sM[2 * 2 * D * MS];   // [2 halves][2 hi/lo][D][MS]
+  __shared__ __attribute__((aligned(16))) float sCol[D];
+  __shared__ float sRed[4];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 5, col = lane & 31;
   const int N = p.N, nblk = p.nblk;
@@ -315,8 +450,25 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(AttnArgs p) {
   const float* vm = p.v_mean + static_cast<size_t>(bh) * nblk * D;
   const LaneOffsets<D, KVB, VF> lo(lane);
 
-  // block 0 in flight while the query tile is prepared
-  stage_block<D, KVB, VF>(stages, kq, vr, scb, lo, wave, lane);
+  // slot j & 1 of each ring, chosen at compile time
+  auto kslot = [&](auto par) -> uint8_t* {
+    if constexpr (decltype(par)::value) return sK1; else return sK0;
+  };
+  auto vslot = [&](auto par) -> uint8_t* {
+    if constexpr (decltype(par)::value) return sV1; else return sV0;
+  };
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+  auto stage_k = [&](int j, auto par) {   // K_j into slot par = j & 1
+    stage_block_k<D, KVB, VF>(kslot(par), kq + static_cast<size_t>(j) * KVB * D, lo, wave);
+  };
+  auto stage_v = [&](int j, auto par) {   // V_j (and its E8M0 scales) into slot par = j & 1
+    stage_block_v<D, KVB, VF>(vslot(par), vr + static_cast<size_t>(j) * NKS * D * VROW,
+                              VF == 1 ? scb + static_cast<size_t>(j) * (KVB / 32) * D : nullptr, lo, wave, lane);
+  };
+  stage_k(0, P0{});
+  stage_v(0, P0{});
+  if (nblk > 1) stage_k(1, P1{});
 
   for (int i = threadIdx.x; i < 2 * 2 * D * MS; i += 256) sM[i] = 0;
   float colv = 1.0f;
@@ -381,15 +533,43 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(AttnArgs p) {
 #pragma unroll
   for (int i = 0; i < MS; ++i) st.RS[i] = 0.0f;
 
+  // block scales travel one step ahead in a register: a load issued inside a
+  // step would make its first use wait on the block loads issued before it
+  float k_cur = ks[0];
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+
+  v16f S[NKT];
+  qk_block<D, KVB, VF>(S, sK0, lo, qb);
+  float pmax = tile_max(S[0]);
+#pragma unroll
+  for (int kt = 1; kt < NKT; ++kt) pmax = tile_max(S[kt], pmax);
 
   const int ntail = N - (nblk - 1) * KVB;            // real keys of the last block
   const int nfull = ntail < KVB ? nblk - 1 : nblk;   // blocks without padded keys
 
-  // after block b: stage the mean of block b+1 into its ring slot, wait for
-  // block b+1's direct loads, and make both visible to the workgroup
-  auto finish = [&](int b, float mnext) {
+  // one block step: softmax and P.V of block b from S, then (into the same
+  // registers, whose scores ExpCast has consumed) S^T of block b+1, whose K
+  // was staged two blocks ahead; the mean flush and the next loads follow
+  // (par = b & 1 names the slots: V_b and K_{b+2} in slot par, K_{b+1} and
+  // V_{b+1} in the other)
+  auto step = [&](const int b, auto par, auto masked) {
+    constexpr bool MASK = decltype(masked)::value;
+    constexpr int PAR = decltype(par)::value;
+    using Q = std::integral_constant<int, 1 - PAR>;
+    float mnext = 0.0f, k_next = 0.0f;
+    if (b + 2 < nblk) stage_k(b + 2, par);
+    if (b + 1 < nblk) {
+      stage_v(b + 1, Q{});
+      k_next = ks[b + 1];
+      if (threadIdx.x < D) mnext = vm[static_cast<size_t>(b + 1) * D + threadIdx.x];
+    }
+    // softmax and P.V of block b, with block b+1's scores made in between
+    // (for the last block they come from a stale slot and are discarded)
+    block_step<D, KVB, VF, MASK>(st, S, pmax, vslot(par), kslot(Q{}), lo, qb, cq * k_cur, p.kc, b,
+                                 MASK ? ntail : KVB, g, col);
+    if ((b & (MS - 1)) == MS - 1 || b == nblk - 1)
+      mean_flush<D, KVB, VF>(st, sM + ((b >> 3) & 1) * 2 * D * MS, g, col);
     if (b + 1 < nblk && threadIdx.x < D) {
       const int nb = b + 1;
       const float ms = mnext * rcol;
@@ -400,28 +580,18 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(AttnArgs p) {
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    k_cur = k_next;
   };
-  auto prefetch = [&](int b) -> float {
-    float mnext = 0.0f;
-    if (b + 1 < nblk) {
-      stage_block<D, KVB, VF>(stages + ((b + 1) & 1) * TT::STAGE, kq + static_cast<size_t>(b + 1) * KVB * D,
-                              vr + static_cast<size_t>(b + 1) * NKS * D * VROW,
-                              VF == 1 ? scb + static_cast<size_t>(b + 1) * (KVB / 32) * D : nullptr, lo, wave,
-                              lane);
-      if (threadIdx.x < D) mnext = vm[static_cast<size_t>(b + 1) * D + threadIdx.x];
-    }
-    return mnext;
-  };
-  for (int b = 0; b < nfull; ++b) {
-    const float mnext = prefetch(b);
-    attn_block<D, KVB, VF, false>(st, stages + (b & 1) * TT::STAGE, sM + ((b >> 3) & 1) * 2 * D * MS, lo, qb,
-                                  cq * ks[b], p.kc, b, nblk, KVB, g, col);
-    finish(b, mnext);
+
+  int b = 0;
+  for (; b + 2 <= nfull; b += 2) {
+    step(b, P0{}, std::false_type{});
+    step(b + 1, P1{}, std::false_type{});
   }
-  if (nfull < nblk) {
-    const int b = nblk - 1;
-    attn_block<D, KVB, VF, true>(st, stages + (b & 1) * TT::STAGE, sM + ((b >> 3) & 1) * 2 * D * MS, lo, qb,
-                                 cq * ks[b], p.kc, b, nblk, ntail, g, col);
+  if (b < nfull) step(b++, P0{}, std::false_type{});
+  if (nfull < nblk) {      // b == nblk - 1
+    if (b & 1) step(b, P1{}, std::true_type{});
+    else step(b, P0{}, std::true_type{});
   }
 
   // ---- O = s_v * acc / l ----
@@ -449,24 +619,11 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(AttnArgs p) {
   }
 }
 
-template <int D, int KVB, int VF>
-static constexpr size_t attn_smem_bytes() {
-  using TT = AttnTile<D, KVB, VF>;
-  return 2 * TT::STAGE + 2 * 2 * D * TT::MSLOT * 2 + D * 4 + 16;
-}
-
 template <int D, int KVB, int VF, int O32>
 static void launch_attn_o(const AttnArgs& a, hipStream_t st) {
-  constexpr size_t smem = attn_smem_bytes<D, KVB, VF>();
-  static bool attr_set = false;          // raising the limit is idempotent
-  if (!attr_set) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn_fwd<D, KVB, VF, O32>),
-                        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
-    attr_set = true;
-  }
   const int nqt = (a.N + kQTile - 1) / kQTile;
   const dim3 grid(static_cast<unsigned>(a.B * a.H * nqt));
-  hipLaunchKernelGGL((k_attn_fwd<D, KVB, VF, O32>), grid, dim3(256), smem, st, a);
+  hipLaunchKernelGGL((k_attn_fwd<D, KVB, VF, O32>), grid, dim3(256), 0, st, a);
 }
 
 template <int D, int KVB, int VF>
