@@ -1,7 +1,8 @@
 // Fused VC-Attention forward for gfx950.
 //
-// Per 128-row query tile (one workgroup, 4 waves x 32 queries):
-//   * Q tile -> E4M3 codes with one scale s_q = max|Q|/448, kept in registers;
+// Per 256 query rows (one workgroup, 8 waves x 32 queries):
+//   * each 128-row Q tile -> E4M3 codes with one scale s_q = max|Q|/448, kept
+//     in registers;
 //   * for every KV block in ascending order (chooseai.io brief, "V-Smooth":
 //     the mean comes back through the online-softmax row sums; theclarity.today
 //     story: one pass over the values):
@@ -77,6 +78,8 @@ __device__ __forceinline__ float max_xor32(float v) {
   return fmaxf(fmaxf(v, __uint_as_float(r[0])), __uint_as_float(r[1]));
 }
 
+constexpr int kAttnThreads = 512;   // threads per attention workgroup
+
 template <int D, int KVB, int VF>
 struct AttnTile {
   static constexpr int NDC = D / 64;      // 64-deep chunks of the QK^T contraction
@@ -89,6 +92,9 @@ struct AttnTile {
   static constexpr int SBYTES = VF == 1 ? (KVB / 32) * D : 0;
   static constexpr int STAGE = KBYTES + VBYTES + (SBYTES + 1023) / 1024 * 1024;
   static constexpr int MSLOT = 8;         // blocks per mean-restoration flush
+  static constexpr int NTH = kAttnThreads;
+  static constexpr int NWV = NTH / 64;    // waves, 32 query rows each
+  static constexpr int ROWS = NWV * 32;   // query rows per workgroup (NWV / 4 scale tiles)
 };
 
 // Per-lane offsets that stay fixed for the whole kernel.  With the swizzle
@@ -99,8 +105,9 @@ struct AttnTile {
 template <int D, int KVB, int VF>
 struct LaneOffsets {
   using T = AttnTile<D, KVB, VF>;
-  static constexpr int KR = T::KBYTES / 4096;           // direct-load rounds for K
-  static constexpr int VR = (T::VBYTES + 4095) / 4096;  // ... and for the residuals
+  static constexpr int RB = T::NTH * 16;                  // bytes per direct-load round
+  static constexpr int KR = (T::KBYTES + RB - 1) / RB;    // direct-load rounds for K
+  static constexpr int VR = (T::VBYTES + RB - 1) / RB;    // ... and for the residuals
   int k_rd[T::NDC][2];   // K operand: 16-byte halves of the 32-byte chunk (c, h)
   int v_rd[2];           // residual operand chunks (E4M3: g and 2+g; MXFP4: g)
   int k_src, v_src;      // source offsets of this lane's direct loads (round 0)
@@ -112,7 +119,7 @@ struct LaneOffsets {
       for (int h = 0; h < 2; ++h) k_rd[c][h] = col * D + swz<D>(col, 4 * c + 2 * g + h) * 16;
     v_rd[0] = col * T::VROW + swz<T::VROW>(col, g) * 16;
     v_rd[1] = col * T::VROW + swz<T::VROW>(col, VF == 0 ? 2 + g : g) * 16;
-    // round r fetches chunk 256r + tid: its row is 256r/(D/16) rows further
+    // round r fetches chunk NTH*r + tid: its row is NTH*r/(D/16) rows further
     // down, a multiple of 32, so the swizzled chunk is the same as in round 0
     const int t = threadIdx.x;
     const int krow = t / (D / 16), vrow = t / (T::VROW / 16);
@@ -132,9 +139,9 @@ __device__ __forceinline__ void stage_block_k(uint8_t* st, const uint8_t* kq_blk
   using L = LaneOffsets<D, KVB, VF>;
 #pragma unroll
   for (int r = 0; r < L::KR; ++r)
-    __builtin_amdgcn_global_load_lds((glb_ptr_t)(kq_blk + lo.k_src + r * 4096),
-                                     (lds_ptr_t)(st + (r * 256 + wave * 64) * 16), 16, 0, 0);
-  (void)sizeof(T);
+    if ((r * T::NTH + wave * 64) * 16 < T::KBYTES)
+      __builtin_amdgcn_global_load_lds((glb_ptr_t)(kq_blk + lo.k_src + r * L::RB),
+                                       (lds_ptr_t)(st + (r * T::NTH + wave * 64) * 16), 16, 0, 0);
 }
 
 template <int D, int KVB, int VF>
@@ -144,9 +151,9 @@ __device__ __forceinline__ void stage_block_v(uint8_t* sv, const uint8_t* vr_blk
   using L = LaneOffsets<D, KVB, VF>;
 #pragma unroll
   for (int r = 0; r < L::VR; ++r)
-    if ((r * 256 + wave * 64) * 16 < T::VBYTES)
-      __builtin_amdgcn_global_load_lds((glb_ptr_t)(vr_blk + lo.v_src + r * 4096),
-                                       (lds_ptr_t)(sv + (r * 256 + wave * 64) * 16), 16, 0, 0);
+    if ((r * T::NTH + wave * 64) * 16 < T::VBYTES)
+      __builtin_amdgcn_global_load_lds((glb_ptr_t)(vr_blk + lo.v_src + r * L::RB),
+                                       (lds_ptr_t)(sv + (r * T::NTH + wave * 64) * 16), 16, 0, 0);
   if constexpr (VF == 1) {
     if (wave == 0 && lane < T::SBYTES / 16)
       __builtin_amdgcn_global_load_lds((glb_ptr_t)(sc_blk + lane * 16), (lds_ptr_t)(sv + T::VBYTES), 16, 0, 0);
@@ -201,18 +208,24 @@ __device__ __forceinline__ void static_for(F&& f) {
 // three-input form).  Scores are never NaN; masked keys are -inf.
 __device__ __forceinline__ float fmax_ieee(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 
-// running maximum over the 16 scores of one S^T tile register set
+// maximum over the 16 scores of one S^T tile register set (and m), as a
+// depth-3 tree of three-input maxima
 __device__ __forceinline__ float tile_max(const v16f& t, float m) {
-#pragma unroll
-  for (int r = 0; r < 16; r += 2) m = fmax_ieee(fmax_ieee(m, t[r]), t[r + 1]);
-  return m;
+  const float a0 = fmax_ieee(fmax_ieee(t[0], t[1]), t[2]);
+  const float a1 = fmax_ieee(fmax_ieee(t[3], t[4]), t[5]);
+  const float a2 = fmax_ieee(fmax_ieee(t[6], t[7]), t[8]);
+  const float a3 = fmax_ieee(fmax_ieee(t[9], t[10]), t[11]);
+  const float a4 = fmax_ieee(fmax_ieee(t[12], t[13]), t[14]);
+  const float b0 = fmax_ieee(fmax_ieee(a0, a1), a2);
+  const float b1 = fmax_ieee(fmax_ieee(a3, a4), t[15]);
+  return fmax_ieee(fmax_ieee(b0, b1), m);
 }
-__device__ __forceinline__ float tile_max(const v16f& t) {
-  float m = fmax_ieee(t[0], t[1]);
-#pragma unroll
-  for (int r = 2; r < 16; r += 2) m = fmax_ieee(fmax_ieee(m, t[r]), t[r + 1]);
-  return m;
-}
+__device__ __forceinline__ float tile_max(const v16f& t) { return tile_max(t, -__builtin_inff()); }
+
+// Keeps a value computed here: the empty statement consumes it, so the
+// compiler cannot sink the computation past this point (into a later, exposed
+// part of the loop).  Emits no instruction.
+__device__ __forceinline__ void pin(float& v) { asm volatile("" : "+v"(v)); }
 
 // Issue order of one block step's matrix instructions.  Per 64-key step s:
 // the S^T MFMAs of the NEXT block for key tiles 2s and 2s+1 (NDC each), the
@@ -295,7 +308,18 @@ __device__ __forceinline__ void block_step(
   static_assert(PL::valid(), "step plan overwrites a score tile before its bytes are made");
   constexpr int NKT = TT::NKT, NKS = TT::NKS, NDT = TT::NDT, VROW = TT::VROW, MS = TT::MSLOT;
   const uint8_t* sS = sV + TT::VBYTES;
-  const v8i ones = {0x22222222, 0x22222222, 0x22222222, 0x22222222, 0, 0, 0, 0};   // E2M1 1.0 (FP4 operand)
+  // Row sums on a 16x16x128 MFMA with P (E4M3) as its B operand.  Output
+  // column n collects lanes n, n+16, n+32, n+48 of B, whose lane groups G
+  // (of sixteen) hold query n for even G and n+16 for odd G; the FP8 B
+  // operand of lane group G carries contraction indices 16G+s and
+  // 64+16G+s, while the FP4 A operand carries 32G+s in nibble s, so A's
+  // nibbles 0..15 meet even B groups and 16..31 odd ones (measured with a
+  // one-wave probe).  A is 1.0 (E2M1) in the half whose parity matches the
+  // row block of four that lane group receives in the 16x16 result (rows
+  // 4(L/16)+i of lane L), so each lane gets the exact sum of its own query.
+  const int rb = (col >> 2) & 1;     // (lane % 16) / 4, parity
+  const int lo_one = rb ? 0 : 0x22222222, hi_one = rb ? 0x22222222 : 0;
+  const v8i ones = {lo_one, lo_one, hi_one, hi_one, 0, 0, 0, 0};
 
   if constexpr (MASK) {
 #pragma unroll
@@ -328,7 +352,7 @@ __device__ __forceinline__ void block_step(
   st.m_run = m_new;
 
   v8i P[NKS];
-  v16f rsum;
+  v4f rsum;
   v8i opnd[3];
   int osc[3];
   (void)osc;
@@ -380,9 +404,10 @@ __device__ __forceinline__ void block_step(
                                                              0, 0, 0, 0);
     } else if constexpr (PL::kind(i) == 1) {
       constexpr int sj = PL::step_of(i);
-      // row sums of the decoded bytes on the matrix core: ones(FP4) . P^T, exact
-      rsum = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, P[sj], sj == 0 ? v16f{} : rsum, 4, 0, 0, 127,
-                                                            0, 127);
+      // row sums of the decoded bytes on the matrix core (exact: multiples of
+      // 2^-9 below 2^8)
+      rsum = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ones, P[sj], sj == 0 ? v4f{} : rsum, 4, 0, 0, 127, 0,
+                                                              127);
     } else {
       constexpr int sj = PL::step_of(i), T = PL::pv_T(i);
       if constexpr (VF == 0)
@@ -397,7 +422,10 @@ __device__ __forceinline__ void block_step(
     });
     static_for<NKT>([&](auto ktc) {
       constexpr int kt = decltype(ktc)::value;
-      if constexpr (PL::pm_slot(kt) == i) pmax = kt == 0 ? tile_max(S[0]) : tile_max(S[kt], pmax);
+      if constexpr (PL::pm_slot(kt) == i) {
+        pmax = kt == 0 ? tile_max(S[0]) : tile_max(S[kt], pmax);
+        pin(pmax);
+      }
     });
     __builtin_amdgcn_sched_barrier(0);
   });
@@ -413,13 +441,15 @@ __device__ __forceinline__ void block_step(
   for (int i = 0; i < MS; ++i) st.RS[i] = i == slot ? rs : st.RS[i];
 }
 
-// The fused forward.  Per workgroup one 128-row query tile (4 waves x 32
-// rows).  Block b+1's S^T MFMAs run inside block b's step, so each block
+// The fused forward.  Per workgroup 256 query rows (8 waves x 32 rows, two
+// 128-row tiles with a query scale each), so every staged K/V block serves
+// 256 queries.  Block b+1's S^T MFMAs run inside block b's step, so each block
 // starts with its scores ready: K is staged two blocks ahead and V one block
 // ahead, each in a two-slot LDS ring filled by direct global->LDS loads.
 template <int D, int KVB, int VF, int O32>
-__global__ __launch_bounds__(256, 2) void k_attn_fwd(AttnArgs p) {
+__global__ __launch_bounds__(kAttnThreads, 1) void k_attn_fwd(AttnArgs p) {
   using TT = AttnTile<D, KVB, VF>;
+  static_assert(kQTile == 4 * 32 && TT::ROWS % kQTile == 0, "a query scale tile is four waves");
   constexpr int NDC = TT::NDC, NKT = TT::NKT, NKS = TT::NKS, NDT = TT::NDT, VROW = TT::VROW;
   constexpr int MS = TT::MSLOT;
   constexpr int VSTAGE = TT::VBYTES + (TT::SBYTES + 1023) / 1024 * 1024;
@@ -433,13 +463,14 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(AttnArgs p) {
   __shared__ __attribute__((aligned(1024))) uint8_t sV1[VSTAGE];
   __shared__ __attribute__((aligned(16))) uint16_t sM[2 * 2 * D * MS];   // [2 halves][2 hi/lo][D][MS]
   __shared__ __attribute__((aligned(16))) float sCol[D];
-  __shared__ float sRed[4];
+  __shared__ float sRcol[D];      // 1 / column scale: block means enter the accumulator in residual units
+  __shared__ float sRed[TT::NWV];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 5, col = lane & 31;
   const int N = p.N, nblk = p.nblk;
-  const int nqt = (N + kQTile - 1) / kQTile;
+  const int nqt = (N + TT::ROWS - 1) / TT::ROWS;
   const int bh = blockIdx.x / nqt, qt = blockIdx.x % nqt;
-  const int qrow = qt * kQTile + wave * 32 + col;
+  const int qrow = qt * TT::ROWS + wave * 32 + col;
 
   const uint8_t* kq = p.Kq + static_cast<size_t>(bh) * nblk * KVB * D;
   const uint8_t* vr = p.Vres + static_cast<size_t>(bh) * nblk * NKS * D * VROW;
@@ -470,13 +501,14 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(AttnArgs p) {
   stage_v(0, P0{});
   if (nblk > 1) stage_k(1, P1{});
 
-  for (int i = threadIdx.x; i < 2 * 2 * D * MS; i += 256) sM[i] = 0;
+  for (int i = threadIdx.x; i < 2 * 2 * D * MS; i += TT::NTH) sM[i] = 0;
   float colv = 1.0f;
   if (threadIdx.x < D) {
     if (VF == 0) colv = reinterpret_cast<const float*>(p.v_scale)[static_cast<size_t>(bh) * D + threadIdx.x];
     sCol[threadIdx.x] = colv;
+    sRcol[threadIdx.x] = 1.0f / colv;
   }
-  const float rcol = 1.0f / colv;   // block means enter the accumulator in residual units
+  const float rcol = 1.0f / colv;
 
   // ---- query tile: E4M3 codes with one scale per 128 rows ----
   v8i qb[NDC];
@@ -502,7 +534,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(AttnArgs p) {
     am = wave_max(am);
     if (lane == 0) sRed[wave] = am;
     __syncthreads();
-    const float amax = fmaxf(fmaxf(sRed[0], sRed[1]), fmaxf(sRed[2], sRed[3]));
+    const float* tr = sRed + (wave & ~3);      // the four waves of this wave's 128-row scale tile
+    const float amax = fmaxf(fmaxf(tr[0], tr[1]), fmaxf(tr[2], tr[3]));
     const float sq = amax > 0.0f ? amax / 448.0f : 1.0f;
 #pragma unroll
     for (int c = 0; c < NDC; ++c)
@@ -572,7 +605,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(AttnArgs p) {
       mean_flush<D, KVB, VF>(st, sM + ((b >> 3) & 1) * 2 * D * MS, g, col);
     if (b + 1 < nblk && threadIdx.x < D) {
       const int nb = b + 1;
-      const float ms = mnext * rcol;
+      const float ms = mnext * sRcol[threadIdx.x];
       const uint32_t hi = bf16_bits(ms);
       uint16_t* mh = sM + ((nb >> 3) & 1) * 2 * D * MS;
       mh[(0 * D + threadIdx.x) * MS + (nb & (MS - 1))] = static_cast<uint16_t>(hi);
@@ -621,9 +654,10 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(AttnArgs p) {
 
 template <int D, int KVB, int VF, int O32>
 static void launch_attn_o(const AttnArgs& a, hipStream_t st) {
-  const int nqt = (a.N + kQTile - 1) / kQTile;
+  using TT = AttnTile<D, KVB, VF>;
+  const int nqt = (a.N + TT::ROWS - 1) / TT::ROWS;
   const dim3 grid(static_cast<unsigned>(a.B * a.H * nqt));
-  hipLaunchKernelGGL((k_attn_fwd<D, KVB, VF, O32>), grid, dim3(256), 0, st, a);
+  hipLaunchKernelGGL((k_attn_fwd<D, KVB, VF, O32>), grid, dim3(TT::NTH), 0, st, a);
 }
 
 template <int D, int KVB, int VF>
