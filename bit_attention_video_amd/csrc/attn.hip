@@ -577,6 +577,8 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_fwd(AttnArgs p) {
   float pmax = tile_max(S[0]);
 #pragma unroll
   for (int kt = 1; kt < NKT; ++kt) pmax = tile_max(S[kt], pmax);
+  // every wave has read K_0 before the first step refills its slot
+  __syncthreads();
 
   const int ntail = N - (nblk - 1) * KVB;            // real keys of the last block
   const int nfull = ntail < KVB ? nblk - 1 : nblk;   // blocks without padded keys
