@@ -171,6 +171,22 @@ def main():
     t_prep = float(np.mean(prep_ms)) * 1e-3
     log(f"step {ms_step:.2f} ms (prep {t_prep * 1e3:.2f} ms, attention {t_fwd * 1e3:.2f} ms)")
 
+    # the FP8 MFMA rate this GPU sustains (pure MFMA loop, same launch shape
+    # class): the clock drops under full matrix load, so this is the
+    # attainable ceiling next to the 5.0 PF specification
+    loop_ms = []
+    chk, loop_flops = vb.mfma_loop(2048, 200)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        chk, loop_flops = vb.mfma_loop(2048, 2000, chk)
+        e1.record()
+        torch.cuda.synchronize()
+        loop_ms.append(e0.elapsed_time(e1))
+    loop_tflops = loop_flops / (min(loop_ms) * 1e-3) / 1e12
+    log(f"fp8 mfma loop {loop_tflops:.1f} TFLOP/s")
+
     if args.calib_copy_mib:
         a = torch.empty(args.calib_copy_mib << 20, dtype=torch.uint8, device="cuda")
         b = torch.empty_like(a)
@@ -214,6 +230,8 @@ def main():
         "t_prep_ms": round(t_prep * 1e3, 3),
         "t_attn_ms": round(t_fwd * 1e3, 3),
         "prep_over_attn": round(t_prep / t_fwd, 4),
+        "fp8_mfma_loop_tflops": round(loop_tflops, 1),
+        "pct_mfma_loop_attn": round(100 * achieved / loop_tflops, 2),
         "roofline": {"bound": "mfma", "kernel": "k_attn_fwd", "achieved": round(achieved, 2),
                      "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4),
                      "traffic": traffic},

@@ -62,6 +62,8 @@ def lib() -> ctypes.CDLL:
         L.vc_dbg_kmeans_assign.restype = ctypes.c_int
         L.vc_dbg_sort.argtypes = [cfgp, _P, _P, _P, ctypes.c_size_t, _P]
         L.vc_dbg_sort.restype = ctypes.c_int
+        L.vc_mfma_loop.argtypes = [ctypes.c_int32, ctypes.c_int32, _P, _P]
+        L.vc_mfma_loop.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -222,3 +224,16 @@ def dbg_sort(cfg: VcConfig, labels: torch.Tensor) -> torch.Tensor:
     _check(lib().vc_dbg_sort(ctypes.byref(cfg), _ptr(labels), _ptr(perm), _ptr(ws), ws.numel(), _stream()),
            "vc_dbg_sort")
     return perm
+
+
+MFMA_LOOP_THREADS = 512
+MFMA_LOOP_FLOPS_PER_ITER_WAVE = 8 * 2 * 32 * 32 * 64
+
+
+def mfma_loop(blocks: int, iters: int, out: torch.Tensor | None = None) -> tuple[torch.Tensor, float]:
+    """Runs the FP8 MFMA loop kernel; returns (checksum buffer, flops launched)."""
+    n = blocks * MFMA_LOOP_THREADS
+    out = torch.empty(n, dtype=torch.float32, device="cuda") if out is None else out
+    _need(out, torch.float32, (n,), "out")
+    _check(lib().vc_mfma_loop(blocks, iters, _ptr(out), _stream()), "vc_mfma_loop")
+    return out, float(blocks) * (MFMA_LOOP_THREADS // 64) * iters * MFMA_LOOP_FLOPS_PER_ITER_WAVE

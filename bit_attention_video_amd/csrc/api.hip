@@ -279,6 +279,14 @@ vc_status vc_dbg_expcast(const float* S, const float* A, const float* B, int64_t
   return VC_OK;
 }
 
+vc_status vc_mfma_loop(int32_t blocks, int32_t iters, float* out, hipStream_t stream) {
+  g_err.clear();
+  if (blocks < 1 || iters < 1) return fail(VC_ERR_INVALID_ARG, "blocks and iters must be >= 1");
+  if (!out) return fail(VC_ERR_INVALID_ARG, "out is NULL");
+  VC_TRY(vc::launch_mfma_loop(blocks, iters, out, stream), "mfma_loop");
+  return VC_OK;
+}
+
 vc_status vc_dbg_kmeans_assign(const vc_config* cfg, const void* V, const float* C, int32_t* labels, void* ws,
                                size_t ws_bytes, hipStream_t stream) {
   g_err.clear();

@@ -685,6 +685,35 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+// Eight independent FP8 32x32x64 MFMA chains per wave: the matrix core's
+// sustained rate at the clock the part holds under full MFMA load.
+__global__ __launch_bounds__(512) void k_mfma_loop(int iters, float* __restrict__ out) {
+  v16f acc[8];
+#pragma unroll
+  for (int m = 0; m < 8; ++m) acc[m] = v16f{};
+  v8i a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = static_cast<int>(0x30303030u + threadIdx.x);
+    b[i] = static_cast<int>(0x28282828u + i);
+  }
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int m = 0; m < 8; ++m) acc[m] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[m], 0, 0, 0, 0, 0, 0);
+  }
+  float r = 0.0f;
+#pragma unroll
+  for (int m = 0; m < 8; ++m)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) r += acc[m][i];
+  out[static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x] = r;
+}
+
+hipError_t launch_mfma_loop(int blocks, int iters, float* out, hipStream_t st) {
+  hipLaunchKernelGGL(k_mfma_loop, dim3(static_cast<unsigned>(blocks)), dim3(512), 0, st, iters, out);
+  return hipGetLastError();
+}
+
 hipError_t launch_dbg_expcast(const float* S, const float* A, const float* B, int64_t n, uint8_t* out,
                               hipStream_t st) {
   if (n <= 0) return hipSuccess;

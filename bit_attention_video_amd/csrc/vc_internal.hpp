@@ -65,5 +65,6 @@ hipError_t launch_vres_ksmooth(const PrepArgs& a, const int32_t* perm, const Pre
 hipError_t launch_attn(const AttnArgs& a, hipStream_t st);
 hipError_t launch_dbg_expcast(const float* S, const float* A, const float* B, int64_t n, uint8_t* out,
                               hipStream_t st);
+hipError_t launch_mfma_loop(int blocks, int iters, float* out, hipStream_t st);
 
 }  // namespace vc

@@ -143,6 +143,16 @@ vc_status vc_dbg_kmeans_assign(const vc_config* cfg, const void* V, const float*
 vc_status vc_dbg_sort(const vc_config* cfg, const int32_t* labels, int32_t* perm,
                       void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* ---- measurement entry point ------------------------------------------------
+ * vc_mfma_loop: the attainable FP8 MFMA rate on this GPU at its sustained
+ *   clock.  Launches `blocks` workgroups of 512 threads; every wave issues
+ *   `iters` rounds of 8 independent v_mfma 32x32x64 FP8 instructions (131072
+ *   flops each, so the launch does blocks*8*iters*8*131072 flops).  out:
+ *   float[blocks*512] device buffer that receives a checksum per thread (keeps
+ *   the results live).  Errors: INVALID_ARG for blocks < 1, iters < 1 or NULL
+ *   out. */
+vc_status vc_mfma_loop(int32_t blocks, int32_t iters, float* out, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

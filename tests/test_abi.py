@@ -34,7 +34,7 @@ def test_header_declares_expected_entry_points():
     names = declared_functions()
     for want in ("vsmooth_prepare", "vc_attn_fwd", "vc_attention", "vc_prepare_workspace_bytes",
                  "vc_attention_workspace_bytes", "vc_status_str", "vc_last_error", "vc_dbg_expcast",
-                 "vc_dbg_kmeans_assign", "vc_dbg_sort"):
+                 "vc_dbg_kmeans_assign", "vc_dbg_sort", "vc_mfma_loop"):
         assert want in names, want
 
 
@@ -80,6 +80,8 @@ def test_null_and_misaligned_pointers_rejected(lib):
     assert "aligned" in lib.vc_last_error().decode()
     assert lib.vc_attention(ctypes.byref(c), P, P, P, None, P, P, 1 << 40, None) == VC_ERR_INVALID_ARG  # no init
     assert lib.vc_dbg_expcast(None, None, None, -1, None, None) == VC_ERR_INVALID_ARG
+    assert lib.vc_mfma_loop(0, 10, P, None) == VC_ERR_INVALID_ARG
+    assert lib.vc_mfma_loop(4, 10, None, None) == VC_ERR_INVALID_ARG
 
 
 def test_workspace_too_small_rejected(lib):
