@@ -43,8 +43,9 @@ def prepare_head(K: np.ndarray, V: np.ndarray, init_idx: np.ndarray, k: int, ite
 
 
 def attend_rows(Q: np.ndarray, prep: dict, tiles, scale: float = 0.0, beta: float = DEFAULT_BETA,
-                trace: dict | None = None) -> dict:
-    """Returns {tile index: O rows (fp64)} for the requested 128-row tiles."""
+                trace: dict | None = None, mode: str = "expcast") -> dict:
+    """Returns {tile index: O rows (fp64)} for the requested 128-row tiles.
+    mode: "expcast" or "exp2" (ExpCast off), see attention.attend_tile."""
     N, d = Q.shape
     sc = softmax_scale(d, scale)
     out = {}
@@ -53,7 +54,7 @@ def attend_rows(Q: np.ndarray, prep: dict, tiles, scale: float = 0.0, beta: floa
         out[t] = attention.attend_tile(
             Q[lo:hi], prep["k"]["kdec"], prep["k"]["k_scale"], prep["v"]["vres"],
             prep["v"]["col_scale"], prep["v"]["means"], prep["N"], prep["kv_block"], sc,
-            beta, prep["quantize"], trace)
+            beta, prep["quantize"], trace, mode)
     return out
 
 

@@ -28,6 +28,12 @@ online softmax keeps; [clarity]: one pass over the values):
   O = (col_scale * acc + accM) / l.
 Accumulators are fp64 here.
 
+ExpCast off (mode="exp2"): the path ExpCast replaces ([rw] "ExpCast-FP8
+goes after the other end": an fp32 exponential, then a conversion to the
+8-bit format).  Reading: the same log2-domain argument in one binary32 FMA,
+x = fma(S_j, c, -m), then p = E4M3(2^x) rounded to nearest even from the
+exact power; masked keys give byte 0.  Everything else is unchanged.
+
 ``quantize=False`` (self-check): no rounding anywhere and p = 2^(t - m)
 exactly, with blocking, permutation, K smoothing and mean restoration kept.
 """
@@ -52,6 +58,14 @@ def expcast_bytes(S32: np.ndarray, A: float, B: np.ndarray) -> np.ndarray:
     return c.astype(np.uint8)
 
 
+def exp2cast_bytes(S32: np.ndarray, A: float, B: np.ndarray) -> np.ndarray:
+    """Bytes = E4M3_rne(2^fma_f32(S32, A, B)) (ExpCast off).  B broadcasts per row."""
+    x = fma_f32(S32, A, B)
+    with np.errstate(invalid="ignore", over="ignore"):
+        p = np.where(np.isnan(x) | np.isneginf(x), 0.0, np.exp2(x))
+    return e4m3_encode(p).astype(np.uint8)
+
+
 def softmax_scale(d: int, scale: float = 0.0) -> float:
     return float(f32(1.0 / math.sqrt(d))) if scale == 0.0 else float(f32(scale))
 
@@ -68,9 +82,12 @@ def quantize_q_tile(Q: np.ndarray):
 def attend_tile(Q: np.ndarray, kdec: np.ndarray, k_scale: np.ndarray, vres: np.ndarray,
                 col_scale: np.ndarray, means: np.ndarray, N: int, kv_block: int,
                 scale: float, beta: float = DEFAULT_BETA, quantize: bool = True,
-                trace: dict | None = None) -> np.ndarray:
+                trace: dict | None = None, mode: str = "expcast") -> np.ndarray:
     """One query tile (rows of Q, fp64 bf16 values) against all KV blocks.
-    kdec / vres: decoded permuted keys and residuals [nblk*kv_block, d]."""
+    kdec / vres: decoded permuted keys and residuals [nblk*kv_block, d].
+    mode: "expcast" (probability bytes from one FMA) or "exp2" (ExpCast off)."""
+    if mode not in ("expcast", "exp2"):
+        raise ValueError(mode)
     nblk = k_scale.shape[0]
     n, d = Q.shape
     dv = vres.shape[1]
@@ -96,13 +113,19 @@ def attend_tile(Q: np.ndarray, kdec: np.ndarray, k_scale: np.ndarray, vres: np.n
             S32[:, nvalid:] = -np.inf
             t_max = f32(c * np.max(S32, axis=1))
             m_new = np.maximum(m, t_max)
-            Brow = f32(Kc - 8.0 * m_new)
-            codes = expcast_bytes(S32, 8.0 * c, Brow[:, None])
+            if mode == "expcast":
+                A = 8.0 * c
+                Brow = f32(Kc - 8.0 * m_new)
+                codes = expcast_bytes(S32, A, Brow[:, None])
+            else:
+                A = c
+                Brow = -m_new
+                codes = exp2cast_bytes(S32, A, Brow[:, None])
             p = e4m3_decode(codes)
             if trace is not None:
                 trace.setdefault("codes", []).append(codes)
                 trace.setdefault("S32", []).append(S32)
-                trace.setdefault("A", []).append(8.0 * c)
+                trace.setdefault("A", []).append(A)
                 trace.setdefault("B", []).append(Brow)
         else:
             t = S * cq

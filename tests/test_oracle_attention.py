@@ -132,3 +132,62 @@ def test_vsmooth_and_expcast_fidelity_direction():
     on = _all_rows(Q, oracle.prepare_head(K, V, init, 16, 3, 64, fmt="mxfp4", vsmooth_on=True))
     off = _all_rows(Q, oracle.prepare_head(K, V, init, 16, 3, 64, fmt="mxfp4", vsmooth_on=False))
     assert oracle.psnr(on, ref) > oracle.psnr(off, ref)
+
+
+# ---- ExpCast off: p = E4M3(2^x), x = fma(S, c, -m) ----
+
+def test_exp2cast_bytes_at_integer_exponents():
+    # 2^-k for integer k is an E4M3 value down to 2^-9 (normals to 2^-6, then
+    # subnormal multiples of 2^-9); 2^-10 is the tie between 0 and 2^-9 and
+    # goes to the even code 0; -inf (a padded key) gives 0
+    from oracle.attention import exp2cast_bytes
+    z = np.array([0, -1, -2, -3, -4, -5, -6, -7, -8, -9, -10, -11, -40, -np.inf], np.float32)
+    got = exp2cast_bytes(z, 1.0, np.zeros(1, np.float32))
+    want = [0x38, 0x30, 0x28, 0x20, 0x18, 0x10, 0x08, 0x04, 0x02, 0x01, 0x00, 0x00, 0x00, 0x00]
+    assert got.tolist() == want
+
+
+def test_exp2cast_is_nearest_e4m3_of_the_power():
+    # brute force over every non-negative E4M3 code: the byte is the code
+    # nearest to 2^x (ties to even), checked against a scan of all 127 values
+    from oracle.attention import exp2cast_bytes
+    rng = np.random.default_rng(3)
+    x = rng.uniform(-12.0, 0.0, 4000).astype(np.float32)
+    got = exp2cast_bytes(x, 1.0, np.zeros(1, np.float32)).astype(np.int64)
+    codes = np.arange(0, 127)
+    vals = F.e4m3_decode(codes.astype(np.uint8))
+    p = np.exp2(x.astype(np.float64))
+    dist = np.abs(p[:, None] - vals[None, :])
+    best = np.min(dist, axis=1)
+    for i in range(x.size):
+        cand = codes[dist[i] == best[i]]
+        want = cand[0] if cand.size == 1 else cand[cand % 2 == 0][0]
+        assert got[i] == want
+
+
+def test_exp2cast_uses_the_same_argument_as_expcast():
+    # both modes see the same scores, maxima and block order: on one block the
+    # ExpCast bytes equal round(8x + 56 + beta) of the exp2 argument x up to
+    # the two single roundings, so their decoded values agree within one
+    # ExpCast step (a factor 2^(1/8) per code, plus the offset beta/8)
+    w, Q, K, V, init = _head(64, 64, 64)
+    prep = oracle.prepare_head(K, V, init, w.k, w.iters, 64)
+    te, tx = {}, {}
+    oracle.attend_rows(Q, prep, [0], trace=te, mode="expcast")
+    oracle.attend_rows(Q, prep, [0], trace=tx, mode="exp2")
+    assert np.array_equal(te["S32"][0], tx["S32"][0])
+    pe = F.e4m3_decode(te["codes"][0])
+    px = F.e4m3_decode(tx["codes"][0])
+    big = px >= 2.0 ** -6            # normal range of both encodings
+    ratio = pe[big] / px[big]
+    assert np.all(ratio <= 2.0 ** (1.0 / 8 + 1.0 / 16 + 0.06)) and np.all(ratio >= 2.0 ** -(1.0 / 8 + 1.0 / 16 + 0.06))
+
+
+def test_exp2cast_is_closer_to_exact_than_expcast():
+    # the fidelity direction the pages report for ExpCast (it costs PSNR)
+    w, Q, K, V, init = _head(1024, 64, 64, k=16)
+    ref = exact_attention(Q, K, V, softmax_scale(64))
+    prep = oracle.prepare_head(K, V, init, 16, 3, 64)
+    on = np.concatenate([o for _, o in sorted(oracle.attend_rows(Q, prep, range(8), mode="expcast").items())])
+    off = np.concatenate([o for _, o in sorted(oracle.attend_rows(Q, prep, range(8), mode="exp2").items())])
+    assert oracle.psnr(off, ref) > oracle.psnr(on, ref)
