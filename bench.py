@@ -85,11 +85,11 @@ def cpu_baseline(w, host, n_tiles=6):
             "seconds_measured": round(t_prep + t_tiles, 2)}
 
 
-def psnr_report(w, host, O_on, O_off, heads, n_tiles=3):
+def psnr_report(w, host, outputs, heads, n_tiles=3):
     import oracle
     q, k, v, init = host
     out = {}
-    for name, O in (("vsmooth_on", O_on), ("vsmooth_off", O_off)):
+    for name, O in outputs.items():
         errs, refs = [], []
         for h in heads:
             Q, K, V = (oracle.bf16_to_f64(a[0, h]) for a in (q, k, v))
@@ -187,6 +187,24 @@ def main():
     loop_tflops = loop_flops / (min(loop_ms) * 1e-3) / 1e12
     log(f"fp8 mfma loop {loop_tflops:.1f} TFLOP/s")
 
+    # ExpCast off (fp32 exp2 + E4M3 cast) on the same prepared blocks: the
+    # pages' ablation of ExpCast
+    cfg_x = vb.make_config(w.B, w.H, w.N, w.d, w.kv_block, w.k, w.iters, True, fmt, False,
+                           p_mode=vb.EXP2_CAST)
+    O_x = vb.alloc_out(cfg_x)
+    vb.vc_attn_fwd(cfg_x, Q, prep, out=O_x)
+    torch.cuda.synchronize()
+    x_ms = []
+    for _ in range(max(3, args.steps // 2)):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        vb.vc_attn_fwd(cfg_x, Q, prep, out=O_x)
+        e1.record()
+        torch.cuda.synchronize()
+        x_ms.append(e0.elapsed_time(e1))
+    t_x = float(np.mean(x_ms)) * 1e-3
+    log(f"expcast off: attention {t_x * 1e3:.2f} ms")
+
     if args.calib_copy_mib:
         a = torch.empty(args.calib_copy_mib << 20, dtype=torch.uint8, device="cuda")
         b = torch.empty_like(a)
@@ -198,7 +216,9 @@ def main():
         O_on = O.float().cpu().numpy()
         cfg_off = vb.make_config(w.B, w.H, w.N, w.d, w.kv_block, w.k, w.iters, False, fmt, False)
         O_off = vb.vc_attention(cfg_off, Q, K, V, None).float().cpu().numpy()
-        extra["psnr_db_vs_fp64_exact"] = psnr_report(w, host, O_on, O_off, [0, w.H - 1])
+        extra["psnr_db_vs_fp64_exact"] = psnr_report(
+            w, host, {"vsmooth_on": O_on, "vsmooth_off": O_off, "vsmooth_on_expcast_off": O_x.float().cpu().numpy()},
+            [0, w.H - 1])
         log(f"psnr {extra['psnr_db_vs_fp64_exact']}")
 
     cpu = None
@@ -231,6 +251,8 @@ def main():
         "t_attn_ms": round(t_fwd * 1e3, 3),
         "prep_over_attn": round(t_prep / t_fwd, 4),
         "fp8_mfma_loop_tflops": round(loop_tflops, 1),
+        "expcast_off": {"t_attn_ms": round(t_x * 1e3, 3), "attn_tflops": round(flops / t_x / 1e12, 2),
+                        "expcast_speedup": round(t_x / t_fwd, 3)},
         "pct_mfma_loop_attn": round(100 * achieved / loop_tflops, 2),
         "roofline": {"bound": "mfma", "kernel": "k_attn_fwd", "achieved": round(achieved, 2),
                      "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4),

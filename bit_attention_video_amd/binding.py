@@ -22,13 +22,14 @@ LIB_PATH = os.environ.get("VCATTN_LIBRARY") or os.path.join(_HERE, "libvcattn.so
 DEFAULT_BETA = 8.0 / math.log(2.0) - 12.0
 
 E4M3, MXFP4 = 0, 1
+EXPCAST, EXP2_CAST = 0, 1      # p_mode: ExpCast-FP8 bytes, or exp2 then E4M3 cast
 
 
 class VcConfig(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("N", ctypes.c_int32), ("d", ctypes.c_int32),
                 ("kv_block", ctypes.c_int32), ("n_clusters", ctypes.c_int32), ("iters", ctypes.c_int32),
                 ("vsmooth", ctypes.c_int32), ("v_format", ctypes.c_int32), ("out_fp32", ctypes.c_int32),
-                ("softmax_scale", ctypes.c_float), ("beta", ctypes.c_float)]
+                ("softmax_scale", ctypes.c_float), ("beta", ctypes.c_float), ("p_mode", ctypes.c_int32)]
 
 
 _lib = None
@@ -58,6 +59,8 @@ def lib() -> ctypes.CDLL:
         L.vc_last_error.restype = ctypes.c_char_p
         L.vc_dbg_expcast.argtypes = [_P, _P, _P, ctypes.c_int64, _P, _P]
         L.vc_dbg_expcast.restype = ctypes.c_int
+        L.vc_dbg_exp2cast.argtypes = [_P, _P, _P, ctypes.c_int64, _P, _P]
+        L.vc_dbg_exp2cast.restype = ctypes.c_int
         L.vc_dbg_kmeans_assign.argtypes = [cfgp, _P, _P, _P, _P, ctypes.c_size_t, _P]
         L.vc_dbg_kmeans_assign.restype = ctypes.c_int
         L.vc_dbg_sort.argtypes = [cfgp, _P, _P, _P, ctypes.c_size_t, _P]
@@ -82,9 +85,9 @@ def _check(status: int, what: str):
 
 def make_config(B: int, H: int, N: int, d: int, kv_block: int, n_clusters: int = 1, iters: int = 1,
                 vsmooth: bool = True, v_format: int = E4M3, out_fp32: bool = False,
-                softmax_scale: float = 0.0, beta: float = DEFAULT_BETA) -> VcConfig:
+                softmax_scale: float = 0.0, beta: float = DEFAULT_BETA, p_mode: int = EXPCAST) -> VcConfig:
     return VcConfig(B, H, N, d, kv_block, n_clusters, iters, int(bool(vsmooth)), int(v_format),
-                    int(bool(out_fp32)), softmax_scale, beta)
+                    int(bool(out_fp32)), softmax_scale, beta, int(p_mode))
 
 
 def _stream():
@@ -200,6 +203,14 @@ def dbg_expcast(S: torch.Tensor, A: torch.Tensor, B: torch.Tensor) -> torch.Tens
         _need(t, torch.float32, S.shape, n)
     out = torch.empty(S.shape, dtype=torch.uint8, device=S.device)
     _check(lib().vc_dbg_expcast(_ptr(S), _ptr(A), _ptr(B), S.numel(), _ptr(out), _stream()), "vc_dbg_expcast")
+    return out
+
+
+def dbg_exp2cast(S: torch.Tensor, A: torch.Tensor, B: torch.Tensor) -> torch.Tensor:
+    for t, n in ((S, "S"), (A, "A"), (B, "B")):
+        _need(t, torch.float32, S.shape, n)
+    out = torch.empty(S.shape, dtype=torch.uint8, device=S.device)
+    _check(lib().vc_dbg_exp2cast(_ptr(S), _ptr(A), _ptr(B), S.numel(), _ptr(out), _stream()), "vc_dbg_exp2cast")
     return out
 
 

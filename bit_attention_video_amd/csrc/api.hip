@@ -43,6 +43,7 @@ vc_status validate(const vc_config* c, bool need_kmeans, Dims* out) {
   if (!(std::isfinite(c->softmax_scale) && c->softmax_scale >= 0.0f))
     return fail(VC_ERR_INVALID_ARG, "softmax_scale must be finite and >= 0");
   if (!(c->beta >= -0.5f && c->beta <= 0.45f)) return fail(VC_ERR_INVALID_ARG, "beta must lie in [-0.5, 0.45]");
+  if (c->p_mode != 0 && c->p_mode != 1) return fail(VC_ERR_UNSUPPORTED, "p_mode must be 0 (ExpCast) or 1 (exp2 + cast)");
   if (need_kmeans) {
     if (c->n_clusters < 1 || c->n_clusters > c->N || c->n_clusters > vc::kMaxClusters)
       return fail(VC_ERR_INVALID_ARG, "n_clusters must lie in [1, min(N, 4096)]");
@@ -155,6 +156,7 @@ void fill_attn_args(const vc_config* c, const Dims& D, vc::AttnArgs& a) {
   a.scale = c->softmax_scale == 0.0f ? static_cast<float>(1.0 / std::sqrt(static_cast<double>(D.d)))
                                      : c->softmax_scale;
   a.kc = 56.0f + c->beta;
+  a.p_mode = c->p_mode;
 }
 
 }  // namespace
@@ -276,6 +278,15 @@ vc_status vc_dbg_expcast(const float* S, const float* A, const float* B, int64_t
   if (n < 0) return fail(VC_ERR_INVALID_ARG, "n must be >= 0");
   if (n > 0 && (!S || !A || !B || !out)) return fail(VC_ERR_INVALID_ARG, "required pointer is NULL");
   VC_TRY(vc::launch_dbg_expcast(S, A, B, n, out, stream), "dbg_expcast");
+  return VC_OK;
+}
+
+vc_status vc_dbg_exp2cast(const float* S, const float* A, const float* B, int64_t n, uint8_t* out,
+                          hipStream_t stream) {
+  g_err.clear();
+  if (n < 0) return fail(VC_ERR_INVALID_ARG, "n must be >= 0");
+  if (n > 0 && (!S || !A || !B || !out)) return fail(VC_ERR_INVALID_ARG, "required pointer is NULL");
+  VC_TRY(vc::launch_dbg_exp2cast(S, A, B, n, out, stream), "dbg_exp2cast");
   return VC_OK;
 }
 

@@ -43,6 +43,24 @@ __device__ __forceinline__ uint32_t expcast4(float s0, float s1, float s2, float
   return w;
 }
 
+// ExpCast off: four E4M3 bytes of exp2(fma(s, A, B)) (fp32 exponential, then
+// the packed FP8 conversion, round to nearest even; -inf scores give 0)
+__device__ __forceinline__ uint32_t exp2cast4(float s0, float s1, float s2, float s3, float A, float B) {
+  const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0, A, B));
+  const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1, A, B));
+  const float e2 = __builtin_amdgcn_exp2f(__builtin_fmaf(s2, A, B));
+  const float e3 = __builtin_amdgcn_exp2f(__builtin_fmaf(s3, A, B));
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, 0, false);
+  return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(e2, e3, lo, true));
+}
+
+// the probability word of one of the two modes (0: ExpCast, 1: exp2 + cast)
+template <int PM>
+__device__ __forceinline__ uint32_t pword4(float s0, float s1, float s2, float s3, float A, float B) {
+  if constexpr (PM == 0) return expcast4(s0, s1, s2, s3, A, B);
+  else return exp2cast4(s0, s1, s2, s3, A, B);
+}
+
 __device__ __forceinline__ float fp8x4_sum(uint32_t w) {
   const v2f lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), false);
   const v2f hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), true);
@@ -53,6 +71,12 @@ __global__ void k_dbg_expcast(const float* __restrict__ S, const float* __restri
                               const float* __restrict__ B, int64_t n, uint8_t* __restrict__ out) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i < n) out[i] = static_cast<uint8_t>(expcast4(S[i], 0.f, 0.f, 0.f, A[i], B[i]) & 0xffu);
+}
+
+__global__ void k_dbg_exp2cast(const float* __restrict__ S, const float* __restrict__ A,
+                               const float* __restrict__ B, int64_t n, uint8_t* __restrict__ out) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n) out[i] = static_cast<uint8_t>(exp2cast4(S[i], 0.f, 0.f, 0.f, A[i], B[i]) & 0xffu);
 }
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -298,7 +322,7 @@ __device__ __forceinline__ void mean_flush(SoftmaxState<D / 32, AttnTile<D, KVB,
 // the next block's S^T (into the same registers, tile by tile) interleaved
 // as planned above.  pmax: per-lane maximum of S (before the cross-lane
 // step); on return it holds the next block's.
-template <int D, int KVB, int VF, bool MASK>
+template <int D, int KVB, int VF, int PM, bool MASK>
 __device__ __forceinline__ void block_step(
     SoftmaxState<D / 32, AttnTile<D, KVB, VF>::MSLOT>& st, v16f* S, float& pmax,
     const uint8_t* sV, const uint8_t* sKn, const LaneOffsets<D, KVB, VF>& lo, const v8i* qb,
@@ -335,8 +359,10 @@ __device__ __forceinline__ void block_step(
   }
   const float mx = max_xor32(pmax);
   const float m_new = fmaxf(st.m_run, cb * mx);
-  const float Bq = __builtin_fmaf(-8.0f, m_new, kc);
-  const float A8 = 8.0f * cb;
+  // word arguments: ExpCast x = fma(S, 8c, 56 + beta - 8m); ExpCast off
+  // x = fma(S, c, -m), then exp2
+  const float Bq = PM == 0 ? __builtin_fmaf(-8.0f, m_new, kc) : -m_new;
+  const float A8 = PM == 0 ? 8.0f * cb : cb;
 
   // the accumulator moves to the new maximum before this block's P.V lands
   if (__builtin_amdgcn_ballot_w64(m_new > st.m_run)) {
@@ -385,14 +411,14 @@ __device__ __forceinline__ void block_step(
     constexpr int kt = 1 + w / 4, q = w % 4;
     const v16f& sv = S[kt];
     P[kt / 2][4 * (kt % 2) + q] =
-        static_cast<int>(expcast4(sv[4 * q], sv[4 * q + 1], sv[4 * q + 2], sv[4 * q + 3], A8, Bq));
+        static_cast<int>(pword4<PM>(sv[4 * q], sv[4 * q + 1], sv[4 * q + 2], sv[4 * q + 3], A8, Bq));
   };
 
   load_opnd(std::integral_constant<int, 0>{});
   load_opnd(std::integral_constant<int, 1>{});
 #pragma unroll
   for (int q = 0; q < 4; ++q)
-    P[0][q] = static_cast<int>(expcast4(S[0][4 * q], S[0][4 * q + 1], S[0][4 * q + 2], S[0][4 * q + 3], A8, Bq));
+    P[0][q] = static_cast<int>(pword4<PM>(S[0][4 * q], S[0][4 * q + 1], S[0][4 * q + 2], S[0][4 * q + 3], A8, Bq));
   __builtin_amdgcn_sched_barrier(0);
 
   static_for<PL::M>([&](auto ic) {
@@ -446,7 +472,7 @@ __device__ __forceinline__ void block_step(
 // 256 queries.  Block b+1's S^T MFMAs run inside block b's step, so each block
 // starts with its scores ready: K is staged two blocks ahead and V one block
 // ahead, each in a two-slot LDS ring filled by direct global->LDS loads.
-template <int D, int KVB, int VF, int O32>
+template <int D, int KVB, int VF, int O32, int PM>
 __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_fwd(AttnArgs p) {
   using TT = AttnTile<D, KVB, VF>;
   static_assert(kQTile == 4 * 32 && TT::ROWS % kQTile == 0, "a query scale tile is four waves");
@@ -601,7 +627,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_fwd(AttnArgs p) {
     }
     // softmax and P.V of block b, with block b+1's scores made in between
     // (for the last block they come from a stale slot and are discarded)
-    block_step<D, KVB, VF, MASK>(st, S, pmax, vslot(par), kslot(Q{}), lo, qb, cq * k_cur, p.kc, b,
+    block_step<D, KVB, VF, PM, MASK>(st, S, pmax, vslot(par), kslot(Q{}), lo, qb, cq * k_cur, p.kc, b,
                                  MASK ? ntail : KVB, g, col);
     if ((b & (MS - 1)) == MS - 1 || b == nblk - 1)
       mean_flush<D, KVB, VF>(st, sM + ((b >> 3) & 1) * 2 * D * MS, g, col);
@@ -659,7 +685,8 @@ static void launch_attn_o(const AttnArgs& a, hipStream_t st) {
   using TT = AttnTile<D, KVB, VF>;
   const int nqt = (a.N + TT::ROWS - 1) / TT::ROWS;
   const dim3 grid(static_cast<unsigned>(a.B * a.H * nqt));
-  hipLaunchKernelGGL((k_attn_fwd<D, KVB, VF, O32>), grid, dim3(TT::NTH), 0, st, a);
+  if (a.p_mode == 0) hipLaunchKernelGGL((k_attn_fwd<D, KVB, VF, O32, 0>), grid, dim3(TT::NTH), 0, st, a);
+  else hipLaunchKernelGGL((k_attn_fwd<D, KVB, VF, O32, 1>), grid, dim3(TT::NTH), 0, st, a);
 }
 
 template <int D, int KVB, int VF>
@@ -711,6 +738,14 @@ __global__ __launch_bounds__(512) void k_mfma_loop(int iters, float* __restrict_
 
 hipError_t launch_mfma_loop(int blocks, int iters, float* out, hipStream_t st) {
   hipLaunchKernelGGL(k_mfma_loop, dim3(static_cast<unsigned>(blocks)), dim3(512), 0, st, iters, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_dbg_exp2cast(const float* S, const float* A, const float* B, int64_t n, uint8_t* out,
+                               hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_dbg_exp2cast, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, st, S, A, B, n,
+                     out);
   return hipGetLastError();
 }
 

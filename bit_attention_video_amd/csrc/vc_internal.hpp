@@ -42,7 +42,7 @@ struct PrepOut {
 };
 
 struct AttnArgs {
-  int B, H, N, d, kvb, nblk, v_format, out_fp32;
+  int B, H, N, d, kvb, nblk, v_format, out_fp32, p_mode;
   float scale, kc;     // softmax scale, fp32(56 + beta)
   const uint16_t* Q;
   const uint8_t* Kq;
@@ -65,6 +65,8 @@ hipError_t launch_vres_ksmooth(const PrepArgs& a, const int32_t* perm, const Pre
 hipError_t launch_attn(const AttnArgs& a, hipStream_t st);
 hipError_t launch_dbg_expcast(const float* S, const float* A, const float* B, int64_t n, uint8_t* out,
                               hipStream_t st);
+hipError_t launch_dbg_exp2cast(const float* S, const float* A, const float* B, int64_t n, uint8_t* out,
+                               hipStream_t st);
 hipError_t launch_mfma_loop(int blocks, int iters, float* out, hipStream_t st);
 
 }  // namespace vc

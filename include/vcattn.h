@@ -79,6 +79,8 @@ typedef struct {
   int32_t out_fp32;         /* 0: O is bf16; 1: O is fp32                          */
   float softmax_scale;      /* 0 selects fp32(1/sqrt(d))                           */
   float beta;               /* ExpCast offset, -0.5 <= beta <= 0.45                */
+  int32_t p_mode;           /* 0: ExpCast-FP8 probability bytes; 1: ExpCast off,   */
+                            /*    p = E4M3(exp2(x)) (see below)                    */
 } vc_config;
 
 /* Bytes of workspace vsmooth_prepare needs (k-means and sort scratch). */
@@ -138,6 +140,10 @@ const char* vc_last_error(void);
  *   k = cfg->n_clusters. */
 vc_status vc_dbg_expcast(const float* S, const float* A, const float* B, int64_t n,
                          uint8_t* out, hipStream_t stream);
+/* vc_dbg_exp2cast: out[i] = the p_mode 1 byte: E4M3 (round to nearest even)
+ *   of the fp32 exp2 of x = fma(S[i], A[i], B[i]) (A = c, B = -m). */
+vc_status vc_dbg_exp2cast(const float* S, const float* A, const float* B, int64_t n,
+                          uint8_t* out, hipStream_t stream);
 vc_status vc_dbg_kmeans_assign(const vc_config* cfg, const void* V, const float* C,
                                int32_t* labels, void* ws, size_t ws_bytes, hipStream_t stream);
 vc_status vc_dbg_sort(const vc_config* cfg, const int32_t* labels, int32_t* perm,

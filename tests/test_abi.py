@@ -34,7 +34,7 @@ def test_header_declares_expected_entry_points():
     names = declared_functions()
     for want in ("vsmooth_prepare", "vc_attn_fwd", "vc_attention", "vc_prepare_workspace_bytes",
                  "vc_attention_workspace_bytes", "vc_status_str", "vc_last_error", "vc_dbg_expcast",
-                 "vc_dbg_kmeans_assign", "vc_dbg_sort", "vc_mfma_loop"):
+                 "vc_dbg_kmeans_assign", "vc_dbg_sort", "vc_mfma_loop", "vc_dbg_exp2cast"):
         assert want in names, want
 
 
@@ -61,6 +61,7 @@ def cfg(**kw):
     (dict(beta=0.5), VC_ERR_INVALID_ARG),
     (dict(beta=-0.6), VC_ERR_INVALID_ARG),
     (dict(v_format=2), VC_ERR_UNSUPPORTED),
+    (dict(p_mode=2), VC_ERR_UNSUPPORTED),
 ])
 def test_invalid_config_rejected_before_launch(lib, kw, status):
     c = cfg(**kw)

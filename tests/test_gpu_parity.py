@@ -17,7 +17,7 @@ import torch
 
 import oracle
 from oracle import formats as F
-from oracle.attention import DEFAULT_BETA, exact_attention, expcast_bytes, softmax_scale
+from oracle.attention import DEFAULT_BETA, exact_attention, exp2cast_bytes, expcast_bytes, softmax_scale
 from bit_attention_video_amd import binding as vb
 from bit_attention_video_amd import inputs
 from layouts import kq_natural, vres_natural, to_device_bf16
@@ -44,11 +44,11 @@ def fmt_id(fmt):
     return vb.E4M3 if fmt == "e4m3" else vb.MXFP4
 
 
-def cfg_for(w, H=None, N=None, vsmooth=True, fmt=None, out_fp32=True, beta=DEFAULT_BETA):
+def cfg_for(w, H=None, N=None, vsmooth=True, fmt=None, out_fp32=True, beta=DEFAULT_BETA, mode="expcast"):
     fmt = fmt or w.v_format
     N = N or w.N
     return vb.make_config(w.B, H or w.H, N, w.d, w.kv_block, min(w.k, N), w.iters, vsmooth, fmt_id(fmt),
-                          out_fp32, 0.0, beta)
+                          out_fp32, 0.0, beta, vb.EXPCAST if mode == "expcast" else vb.EXP2_CAST)
 
 
 def gen(w, H=None, N=None):
@@ -123,6 +123,41 @@ def test_expcast_bytes_bit_exact():
     assert list(got[-61:-5]) == [int(k) + (int(k) & 1) for k in range(56)]
 
 
+def test_exp2cast_bytes_match_oracle():
+    # ExpCast off: the fma argument is bit-exact; exp2 on the GPU is within
+    # one fp32 ulp, so a byte may differ from the oracle's (rounded from the
+    # exact power) only where 2^x lies within 2^-21 (relative) of an E4M3
+    # rounding midpoint, and then only by one code
+    rng = np.random.default_rng(101)
+    rows, cols = 512, 256
+    S = (rng.standard_normal((rows, cols)) * rng.uniform(1, 3e4, (rows, 1))).astype(np.float32)
+    S[:, -3:] = -np.inf
+    c = F.f32(rng.uniform(1e-6, 1e-3, rows))
+    m = F.f32(c * np.max(np.where(np.isfinite(S), S, -np.inf), axis=1))
+    A = c.astype(np.float32)
+    B = (-m).astype(np.float32)
+    want = exp2cast_bytes(S.astype(np.float64), A[:, None].astype(np.float64), B[:, None].astype(np.float64))
+    ints = np.arange(-12, 1).astype(np.float32)            # exact powers of two, including the 2^-10 tie
+    St = np.concatenate([S.ravel(), ints])
+    At = np.concatenate([np.repeat(A, cols), np.ones_like(ints)])
+    Bt = np.concatenate([np.repeat(B, cols), np.zeros_like(ints)])
+    wantt = np.concatenate([want.ravel(), exp2cast_bytes(ints.astype(np.float64), 1.0, np.zeros(ints.size))])
+    got = vb.dbg_exp2cast(torch.from_numpy(St).cuda(), torch.from_numpy(At).cuda(), torch.from_numpy(Bt).cuda())
+    got = got.cpu().numpy().astype(np.int64)
+    x = F.fma_f32(St.astype(np.float64), At.astype(np.float64), Bt.astype(np.float64))
+    with np.errstate(invalid="ignore", over="ignore"):
+        p = np.where(np.isnan(x) | np.isneginf(x), 0.0, np.exp2(x))
+    w = wantt.astype(np.int64)
+    lo = F.e4m3_decode(np.clip(w - 1, 0, 126).astype(np.uint8))
+    here = F.e4m3_decode(w.astype(np.uint8))
+    hi = F.e4m3_decode(np.clip(w + 1, 0, 126).astype(np.uint8))
+    near = (np.abs(p - (lo + here) / 2) <= 2.0 ** -21 * p) | (np.abs(p - (here + hi) / 2) <= 2.0 ** -21 * p)
+    bad = (got != w) & ~(near & (np.abs(got - w) == 1))
+    assert not bad.any(), f"{np.count_nonzero(bad)} bytes differ away from a rounding midpoint"
+    log(f"  exp2cast: {np.count_nonzero(got != w)} of {w.size} bytes at near-midpoints differ by one code")
+    assert np.array_equal(got[-13:], w[-13:])
+
+
 # ------------------------------------------------------------------ sort
 @pytest.mark.parametrize("N,k", [(1, 1), (1000, 16), (77777, 1024), (20000, 4096), (5000, 1)])
 def test_sort_bit_exact(N, k):
@@ -174,28 +209,31 @@ def test_prepare_bit_exact(name, H, N, vsmooth, fmt):
 
 
 # ------------------------------------------------------------------ attention
-def oracle_rows(w, host, b, h, prep_o, tiles, beta=DEFAULT_BETA):
+def oracle_rows(w, host, b, h, prep_o, tiles, beta=DEFAULT_BETA, mode="expcast"):
     Q = oracle.bf16_to_f64(host[0][b, h])
-    return oracle.attend_rows(Q, prep_o, tiles, 0.0, beta)
+    return oracle.attend_rows(Q, prep_o, tiles, 0.0, beta, mode=mode)
 
 
-@pytest.mark.parametrize("name,H,N,vsmooth,fmt,kvb,d", [
-    ("tiny", 2, None, True, "e4m3", None, None),
-    ("tiny", 2, None, False, "e4m3", None, None),
-    ("tiny", 2, None, True, "mxfp4", None, None),
-    ("tiny", 1, 1000, True, "e4m3", 128, None),     # ragged query tile and KV block
-    ("tiny", 1, 77, True, "e4m3", 64, None),        # one partial block
-    ("tiny", 1, 1, True, "e4m3", 64, None),         # a single token
-    ("tiny", 1, 700, True, "mxfp4", 128, 128),
-    ("mid", 2, None, True, "e4m3", None, None),
+@pytest.mark.parametrize("name,H,N,vsmooth,fmt,kvb,d,mode", [
+    ("tiny", 2, None, True, "e4m3", None, None, "expcast"),
+    ("tiny", 2, None, False, "e4m3", None, None, "expcast"),
+    ("tiny", 2, None, True, "mxfp4", None, None, "expcast"),
+    ("tiny", 1, 1000, True, "e4m3", 128, None, "expcast"),     # ragged query tile and KV block
+    ("tiny", 1, 77, True, "e4m3", 64, None, "expcast"),        # one partial block
+    ("tiny", 1, 1, True, "e4m3", 64, None, "expcast"),         # a single token
+    ("tiny", 1, 700, True, "mxfp4", 128, 128, "expcast"),
+    ("mid", 2, None, True, "e4m3", None, None, "expcast"),
+    ("tiny", 2, None, True, "e4m3", None, None, "exp2"),       # ExpCast off
+    ("tiny", 1, 1000, False, "mxfp4", 128, 128, "exp2"),
+    ("mid", 2, None, True, "e4m3", None, None, "exp2"),
 ])
-def test_attention_parity(name, H, N, vsmooth, fmt, kvb, d):
+def test_attention_parity(name, H, N, vsmooth, fmt, kvb, d, mode):
     import dataclasses
     w = inputs.WORKLOADS[name]
     w = dataclasses.replace(w, kv_block=kvb or w.kv_block, d=d or w.d)
     host, dev = gen(w, H=H, N=N)
     N = N or w.N
-    cfg = cfg_for(w, H=H, N=N, vsmooth=vsmooth, fmt=fmt)
+    cfg = cfg_for(w, H=H, N=N, vsmooth=vsmooth, fmt=fmt, mode=mode)
     prep = vb.vsmooth_prepare(cfg, dev["K"], dev["V"], dev["init"])
     O = vb.vc_attn_fwd(cfg, dev["Q"], prep).cpu().numpy()
     O2 = vb.vc_attention(cfg, dev["Q"], dev["K"], dev["V"], dev["init"]).cpu().numpy()
@@ -204,11 +242,11 @@ def test_attention_parity(name, H, N, vsmooth, fmt, kvb, d):
     tiles = list(range(ntile)) if N <= 4096 else sorted({0, 1, ntile // 2, ntile - 1})
     for h in range(H):
         po = oracle_head(w, host, 0, h, vsmooth, fmt)
-        rows = oracle_rows(w, host, 0, h, po, tiles)
+        rows = oracle_rows(w, host, 0, h, po, tiles, mode=mode)
         Oref = np.concatenate([rows[t] for t in tiles])
         Og = np.concatenate([O[0, h, t * 128:min((t + 1) * 128, N)] for t in tiles])
         vmax = float(np.max(np.abs(oracle.bf16_to_f64(host[2][0, h]))))
-        check_close(Og, Oref, vmax, f"{name} N={N} h{h} vs={vsmooth} {fmt}")
+        check_close(Og, Oref, vmax, f"{name} N={N} h{h} vs={vsmooth} {fmt} {mode}")
 
 
 def test_bf16_output_and_determinism():
