@@ -25,20 +25,28 @@ def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
     return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
-def prepare_head(K: np.ndarray, V: np.ndarray, init_idx: np.ndarray, k: int, iters: int,
+def prepare_head(K: np.ndarray, V: np.ndarray, init_idx: np.ndarray | None, k: int, iters: int,
                  kv_block: int, fmt: str = "e4m3", vsmooth_on: bool = True,
-                 quantize: bool = True) -> dict:
-    """K, V: [N, d] fp64 bf16 values of one head."""
+                 quantize: bool = True, init_centroids: np.ndarray | None = None,
+                 perm: np.ndarray | None = None) -> dict:
+    """K, V: [N, d] fp64 bf16 values of one head.  With V-Smooth on, the
+    clustering starts from V[init_idx] or, warm-started, from init_centroids
+    (fp32 [k, d]); a given perm is reused as is (no clustering, no sort).
+    "final_centroids" are the member means of the final clusters."""
     N = V.shape[0]
-    if vsmooth_on:
-        labels, cents = kmeans.kmeans(V, init_idx, iters)
-        perm = vsmooth.stable_sort_perm(labels, init_idx.shape[0])
+    final = None
+    if perm is not None:
+        labels, cents = None, []
+        perm = np.asarray(perm, np.int32)
+    elif vsmooth_on:
+        labels, cents, final = kmeans.kmeans(V, init_idx, iters, init_centroids)
+        perm = vsmooth.stable_sort_perm(labels, k)
     else:
         labels, cents = None, []
         perm = np.arange(N, dtype=np.int32)
     vs = vsmooth.vsmooth_values(V, perm, kv_block, fmt, vsmooth_on, quantize)
     ks = vsmooth.ksmooth(K, perm, kv_block, vsmooth_on, quantize)
-    return {"labels": labels, "centroids": cents, "perm": perm, "v": vs, "k": ks,
+    return {"labels": labels, "centroids": cents, "final_centroids": final, "perm": perm, "v": vs, "k": ks,
             "N": N, "kv_block": kv_block, "fmt": fmt, "quantize": quantize}
 
 

@@ -11,7 +11,11 @@ iteration count.  The readings used here (all stated as readings):
   tokens and centroids, as D = |c|^2 - 2 v.c in exact integers.  "Lightweight"
   is read as: cheap enough to run inside the attention call.
 * Initial centroids are the value rows at k distinct token indices that the
-  caller supplies (drawn at random by the input generator).
+  caller supplies (drawn at random by the input generator), or, warm-started
+  across denoising steps (the pages run the clustering step by step and call
+  its cost a scheduling trade), the centroids the previous call ended with.
+* The centroids a call ends with are the member means of its final clusters
+  (one more update after the last assignment pass).
 * ``iters`` assignment passes, with a centroid update between consecutive
   passes; the final labels are those of the last pass.
 * Ties go to the lowest cluster index.
@@ -52,13 +56,17 @@ def update(V: np.ndarray, labels: np.ndarray, C_old: np.ndarray) -> np.ndarray:
     return np.where(counts[:, None] > 0, mean, C_old)
 
 
-def kmeans(V: np.ndarray, init_idx: np.ndarray, iters: int):
-    """V: [N, d] float64 holding the bf16 values of one head.
-    Returns (labels int32 [N], centroids_per_pass list of [k, d] arrays: the
-    centroids each assignment pass used)."""
+def kmeans(V: np.ndarray, init_idx: np.ndarray | None, iters: int, init_centroids: np.ndarray | None = None):
+    """V: [N, d] float64 holding the bf16 values of one head.  Starts from the
+    rows V[init_idx], or from init_centroids (fp32 [k, d]) when given.
+    Returns (labels int32 [N], centroids_per_pass: the centroids each
+    assignment pass used, final: the member means of the final clusters)."""
     sV = int8_scale(V)
     Vq = quant_i8(V, sV)
-    C = V[np.asarray(init_idx, dtype=np.int64)].astype(np.float64)
+    if init_centroids is not None:
+        C = f32(np.asarray(init_centroids, np.float64)).astype(np.float64)
+    else:
+        C = V[np.asarray(init_idx, dtype=np.int64)].astype(np.float64)
     used = []
     labels = None
     for it in range(iters):
@@ -66,4 +74,4 @@ def kmeans(V: np.ndarray, init_idx: np.ndarray, iters: int):
         labels = assign(Vq, quant_i8(C, sV))
         if it + 1 < iters:
             C = update(V, labels, C)
-    return labels, used
+    return labels, used, update(V, labels, C)

@@ -179,7 +179,7 @@ def test_kmeans_assign_given_oracle_centroids(name, H, N):
     cfg = cfg_for(w, H=H, N=N)
     for h in range(H):
         V = oracle.bf16_to_f64(host[2][0, h])
-        labels, cents = oracle.kmeans.kmeans(V, host[3][0, h], w.iters)
+        labels, cents, _ = oracle.kmeans.kmeans(V, host[3][0, h], w.iters)
         sV = oracle.kmeans.int8_scale(V)
         Vq = oracle.kmeans.quant_i8(V, sV)
         for it, C in enumerate(cents):

@@ -9,6 +9,8 @@ import numpy as np
 from oracle import kmeans as KM
 from oracle import vsmooth as VS
 from oracle import formats as F
+import oracle
+from bit_attention_video_amd import inputs
 
 
 def brute_assign(Vq, Cq):
@@ -84,7 +86,7 @@ def test_kmeans_recovers_sse_optimum_on_separated_tiny_instances():
         own = np.concatenate([np.arange(k), rng.integers(0, k, N - k)])
         V = F.f32(centers[own] + rng.standard_normal((N, d)) * 0.5)
         init = np.array([np.flatnonzero(own == c)[0] for c in range(k)], np.int32)
-        labels, _ = KM.kmeans(V, init, iters=4)
+        labels, _, _ = KM.kmeans(V, init, iters=4)
         best = min(sse(V, np.array(lab), k) for lab in itertools.product(range(k), repeat=N))
         assert abs(sse(V, labels, k) - best) <= 1e-9 * max(1.0, best)
 
@@ -93,7 +95,7 @@ def test_kmeans_pass_count_and_used_centroids():
     rng = np.random.default_rng(13)
     V = F.f32(rng.standard_normal((50, 4)))
     init = rng.choice(50, 5, replace=False).astype(np.int32)
-    labels, used = KM.kmeans(V, init, iters=3)
+    labels, used, _ = KM.kmeans(V, init, iters=3)
     assert len(used) == 3
     assert np.array_equal(used[0], V[init])
     # the labels are the assignment made with the last centroids
@@ -187,3 +189,64 @@ def test_ksmooth_per_block_scale_and_shift():
         s = ks["k_scale"][b]
         assert s == float(F.f32(np.max(np.abs(Kp[lo:hi])) / 448))
         assert np.max(np.abs(ks["kdec"][lo:hi])) == 448.0
+
+
+# ---- carrying the clustering across denoising steps ----
+
+def test_final_centroids_are_exact_member_means():
+    # final = member means of the last pass's clusters, each the fp32
+    # rounding of the exact rational mean; empty clusters keep the centroid
+    rng = np.random.default_rng(21)
+    V = F.f32(rng.standard_normal((60, 3)) * 4)
+    init = np.array([0, 1, 2, 3, 4, 4 + 50], np.int32)
+    labels, used, final = KM.kmeans(V, init, iters=2)
+    for c in range(init.size):
+        mem = V[labels == c]
+        for j in range(3):
+            if len(mem) == 0:
+                assert final[c, j] == used[-1][c, j]
+            else:
+                exact = sum(Fraction(float(x)) for x in mem[:, j]) / len(mem)
+                assert final[c, j] == float(np.float32(float(exact)))
+
+
+def test_warm_start_from_converged_centroids_is_a_fixed_point():
+    # Lloyd's fixed point: once the labels stop changing, one warm-started
+    # pass from the final centroids reproduces the labels and the centroids
+    rng = np.random.default_rng(22)
+    centers = rng.standard_normal((6, 8)) * 10
+    V = F.f32(centers[rng.integers(0, 6, 400)] + rng.standard_normal((400, 8)) * 0.3)
+    init = rng.choice(400, 6, replace=False).astype(np.int32)
+    labels, _, final = KM.kmeans(V, init, iters=12)
+    l2, used2, f2 = KM.kmeans(V, None, 1, init_centroids=final)
+    assert np.array_equal(used2[0], final)
+    assert np.array_equal(l2, labels)
+    assert np.array_equal(f2, final)
+
+
+def test_warm_start_equals_continuing_the_passes():
+    # I passes from V[init] then J passes from its final centroids equal
+    # I + J passes: the carried state is exactly the centroids of pass I + 1
+    rng = np.random.default_rng(23)
+    V = F.f32(rng.standard_normal((300, 6)) * 3)
+    init = rng.choice(300, 9, replace=False).astype(np.int32)
+    l5, u5, f5 = KM.kmeans(V, init, iters=5)
+    l2, u2, f2 = KM.kmeans(V, init, iters=2)
+    l3, u3, f3 = KM.kmeans(V, None, 3, init_centroids=f2)
+    assert np.array_equal(l3, l5) and np.array_equal(f3, f5)
+    for a, b in zip(u2 + u3, u5):
+        assert np.array_equal(a, b)
+
+
+def test_prepare_with_given_perm_reproduces_the_clustered_prepare():
+    # the residuals, means, scales and K codes depend on the clustering only
+    # through the permutation
+    w = inputs.small(inputs.WORKLOADS["tiny"], N=700, seed=31)
+    q, k, v, init = inputs.gen_head(w, 0, 0)
+    K, V = oracle.bf16_to_f64(k), oracle.bf16_to_f64(v)
+    full = oracle.prepare_head(K, V, init, w.k, w.iters, w.kv_block)
+    again = oracle.prepare_head(K, V, None, w.k, w.iters, w.kv_block, perm=full["perm"])
+    assert np.array_equal(again["perm"], full["perm"])
+    for part in ("v", "k"):
+        for key, val in full[part].items():
+            assert np.array_equal(np.asarray(again[part][key]), np.asarray(val)), (part, key)
