@@ -49,6 +49,9 @@ def lib() -> ctypes.CDLL:
         L.vc_attention_workspace_bytes.restype = ctypes.c_size_t
         L.vsmooth_prepare.argtypes = [cfgp, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
         L.vsmooth_prepare.restype = ctypes.c_int
+        L.vsmooth_prepare_warm.argtypes = [cfgp, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                           ctypes.c_size_t, _P]
+        L.vsmooth_prepare_warm.restype = ctypes.c_int
         L.vc_attn_fwd.argtypes = [cfgp, _P, _P, _P, _P, _P, _P, _P, _P]
         L.vc_attn_fwd.restype = ctypes.c_int
         L.vc_attention.argtypes = [cfgp, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
@@ -166,6 +169,36 @@ def vsmooth_prepare(cfg: VcConfig, K: torch.Tensor, V: torch.Tensor, init_idx: t
                                  _ptr(out.Kq), _ptr(out.k_scale), _ptr(out.Vres), _ptr(out.v_scale),
                                  _ptr(out.v_mean), _ptr(out.perm), _ptr(out.labels), _ptr(ws), ws.numel(),
                                  _stream()), "vsmooth_prepare")
+    return out
+
+
+def vsmooth_prepare_warm(cfg: VcConfig, K: torch.Tensor, V: torch.Tensor, *,
+                         init_idx: torch.Tensor | None = None, init_centroids: torch.Tensor | None = None,
+                         perm_in: torch.Tensor | None = None, centroids_out: torch.Tensor | None = None,
+                         out: Prepared | None = None, ws: torch.Tensor | None = None,
+                         with_labels: bool = True) -> Prepared:
+    """vsmooth_prepare carried across calls (include/vcattn.h): exactly one of
+    init_idx (cold start), init_centroids (warm start) or perm_in (reuse)."""
+    shp = (cfg.B, cfg.H, cfg.N, cfg.d)
+    _need(K, torch.bfloat16, shp, "K")
+    _need(V, torch.bfloat16, shp, "V")
+    cshape = (cfg.B, cfg.H, cfg.n_clusters, cfg.d)
+    if init_idx is not None:
+        _need(init_idx, torch.int32, (cfg.B, cfg.H, cfg.n_clusters), "init_idx")
+    if init_centroids is not None:
+        _need(init_centroids, torch.float32, cshape, "init_centroids")
+    if perm_in is not None:
+        _need(perm_in, torch.int32, (cfg.B, cfg.H, cfg.N), "perm_in")
+    if centroids_out is not None:
+        _need(centroids_out, torch.float32, cshape, "centroids_out")
+    out = out or alloc_prepared(cfg, K.device, with_labels)
+    nbytes = workspace_bytes(cfg)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=K.device)
+    _check(lib().vsmooth_prepare_warm(ctypes.byref(cfg), _ptr(K), _ptr(V), _ptr(init_idx), _ptr(init_centroids),
+                                      _ptr(perm_in), _ptr(centroids_out), _ptr(out.Kq), _ptr(out.k_scale),
+                                      _ptr(out.Vres), _ptr(out.v_scale), _ptr(out.v_mean), _ptr(out.perm),
+                                      _ptr(out.labels), _ptr(ws), ws.numel(), _stream()), "vsmooth_prepare_warm")
     return out
 
 

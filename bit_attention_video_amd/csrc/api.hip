@@ -124,14 +124,26 @@ void fill_prep_args(const vc_config* c, const Dims& D, const void* K, const void
     if (e_ != hipSuccess) return hip_fail(e_, where); \
   } while (0)
 
+// Clustering starts from V[init] or from init_centroids; perm_in skips it.
+// centroids_out receives the member means of the final clusters.
 vc_status run_prepare(const vc_config* c, const Dims& D, vc::PrepArgs& a, const int32_t* init,
-                      const vc::PrepOut& o, int32_t* user_labels, hipStream_t st) {
+                      const vc::PrepOut& o, int32_t* user_labels, hipStream_t st,
+                      const float* init_centroids = nullptr, const int32_t* perm_in = nullptr,
+                      float* centroids_out = nullptr) {
   VC_TRY(vc::launch_fill(a.vamax, 0u, D.BH, st), "fill");
   VC_TRY(vc::launch_fill(a.vramax, 0u, D.BH * D.d, st), "fill");
   VC_TRY(vc::launch_stats(a, st), "stats");
-  if (c->vsmooth) {
+  if (perm_in) {
+    if (perm_in != o.perm)
+      VC_TRY(hipMemcpyAsync(o.perm, perm_in, D.BH * D.N * sizeof(int32_t), hipMemcpyDeviceToDevice, st),
+             "copy perm");
+  } else if (c->vsmooth) {
     VC_TRY(vc::launch_quant_v_i8(a, st), "quant_v_i8");
-    VC_TRY(vc::launch_init_centroids(a, init, st), "init_centroids");
+    if (init_centroids)
+      VC_TRY(hipMemcpyAsync(a.C, init_centroids, D.BH * D.k * D.d * sizeof(float), hipMemcpyDeviceToDevice, st),
+             "copy centroids");
+    else
+      VC_TRY(vc::launch_init_centroids(a, init, st), "init_centroids");
     for (int it = 0; it < D.iters; ++it) {
       const bool last = it + 1 == D.iters;
       int32_t* lab = (last && user_labels) ? user_labels : a.labels;
@@ -142,6 +154,11 @@ vc_status run_prepare(const vc_config* c, const Dims& D, vc::PrepArgs& a, const 
       } else {
         VC_TRY(vc::launch_sort(a, lab, o.perm, st), "sort");
       }
+    }
+    if (centroids_out) {
+      VC_TRY(vc::launch_update(a, o.perm, st), "kmeans_update");
+      VC_TRY(hipMemcpyAsync(centroids_out, a.C, D.BH * D.k * D.d * sizeof(float), hipMemcpyDeviceToDevice, st),
+             "copy centroids");
     }
   } else {
     VC_TRY(vc::launch_iota(o.perm, D.N, D.BH * D.N, st), "iota");
@@ -220,6 +237,31 @@ vc_status vsmooth_prepare(const vc_config* cfg, const void* K, const void* V, co
   carve_prep(cv, D, a);
   vc::PrepOut o{Kq, k_scale, Vres, v_scale, v_mean, perm};
   return run_prepare(cfg, D, a, init_idx, o, labels, stream);
+}
+
+vc_status vsmooth_prepare_warm(const vc_config* cfg, const void* K, const void* V, const int32_t* init_idx,
+                               const float* init_centroids, const int32_t* perm_in, float* centroids_out,
+                               uint8_t* Kq, float* k_scale, uint8_t* Vres, void* v_scale, float* v_mean,
+                               int32_t* perm, int32_t* labels, void* ws, size_t ws_bytes, hipStream_t stream) {
+  g_err.clear();
+  Dims D;
+  if (vc_status s = validate(cfg, true, &D)) return s;
+  if (!cfg->vsmooth) return fail(VC_ERR_INVALID_ARG, "vsmooth_prepare_warm needs vsmooth on");
+  if (!K || !V || !Kq || !k_scale || !Vres || !v_scale || !v_mean || !perm || !ws)
+    return fail(VC_ERR_INVALID_ARG, "required pointer is NULL");
+  if ((init_idx != nullptr) + (init_centroids != nullptr) + (perm_in != nullptr) != 1)
+    return fail(VC_ERR_INVALID_ARG, "exactly one of init_idx, init_centroids, perm_in must be given");
+  if (misaligned(K) || misaligned(V) || misaligned(Kq) || misaligned(Vres) || misaligned(v_scale) ||
+      misaligned(v_mean) || misaligned(ws))
+    return fail(VC_ERR_INVALID_ARG, "tensors and workspace must be 16-byte aligned");
+  if (ws_bytes < vc_prepare_workspace_bytes(cfg)) return fail(VC_ERR_WORKSPACE, "workspace too small");
+  vc::PrepArgs a{};
+  fill_prep_args(cfg, D, K, V, a);
+  Carver cv(reinterpret_cast<void*>((reinterpret_cast<uintptr_t>(ws) + 255) & ~static_cast<uintptr_t>(255)));
+  carve_prep(cv, D, a);
+  vc::PrepOut o{Kq, k_scale, Vres, v_scale, v_mean, perm};
+  return run_prepare(cfg, D, a, init_idx, o, perm_in ? nullptr : labels, stream, init_centroids, perm_in,
+                     perm_in ? nullptr : centroids_out);
 }
 
 vc_status vc_attn_fwd(const vc_config* cfg, const void* Q, const uint8_t* Kq, const float* k_scale,

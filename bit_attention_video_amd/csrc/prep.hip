@@ -344,6 +344,10 @@ __global__ void k_iota(int32_t* __restrict__ perm, int N, size_t total) {
   if (i < total) perm[i] = static_cast<int32_t>(i % N);
 }
 
+// A permutation entry as a row index: a caller-supplied permutation with an
+// entry outside [0, N) reads row 0 instead of memory outside the head.
+__device__ __forceinline__ int clamp_tok(int t, int N) { return static_cast<unsigned>(t) < static_cast<unsigned>(N) ? t : 0; }
+
 // ---- V-Smooth residuals -----------------------------------------------------------
 // A workgroup owns one block.  Thread (cg, q) holds channels 8cg..8cg+7 of
 // the sorted positions 4q..4q+3 (+ 4*RQ per pass), read as whole 16-byte
@@ -363,7 +367,7 @@ struct BlockRows {
         const int r = (ps * RQ + q) * 4 + rr;
         const int pos = p0 + r;
         uint4 raw = make_uint4(0u, 0u, 0u, 0u);
-        if (r < KVB && pos < N) raw = *reinterpret_cast<const uint4*>(vv + static_cast<size_t>(pp[pos]) * D + cg * 8);
+        if (r < KVB && pos < N) raw = *reinterpret_cast<const uint4*>(vv + static_cast<size_t>(clamp_tok(pp[pos], N)) * D + cg * 8);
         const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[ps][rr][e] = bf16_to_f32(static_cast<uint16_t>(w[e >> 1] >> ((e & 1) * 16)));
@@ -506,7 +510,7 @@ __global__ __launch_bounds__(256) void k_vres_mxfp4(const uint16_t* __restrict__
 #pragma unroll
     for (int e = 0; e < 32; ++e) {
       const int pos = p0 + grp * 32 + e;
-      r[e] = pos < N ? bf16_to_f32(vv[static_cast<size_t>(pp[pos]) * D + c]) - mc : 0.0f;
+      r[e] = pos < N ? bf16_to_f32(vv[static_cast<size_t>(clamp_tok(pp[pos], N)) * D + c]) - mc : 0.0f;
       am = fmaxf(am, fabsf(r[e]));
     }
     int ex = 0;
@@ -541,7 +545,7 @@ __global__ __launch_bounds__(256) void k_ksmooth(const uint16_t* __restrict__ K,
   float x[CPT];
   float am = 0.0f;
   if (pos < N) {
-    const int tok = perm[static_cast<size_t>(bh) * N + pos];
+    const int tok = clamp_tok(perm[static_cast<size_t>(bh) * N + pos], N);
     const uint16_t* kr = K + (static_cast<size_t>(bh) * N + tok) * D + part * CPT;
     const float* m = mu + static_cast<size_t>(bh) * D + part * CPT;
 #pragma unroll

@@ -147,3 +147,18 @@ def small(w: Workload, N: int, H: int = 1, k: int | None = None, d: int | None =
         seed=seed if seed is not None else w.seed,
         iters=iters if iters is not None else w.iters,
         v_format=v_format if v_format is not None else w.v_format)
+
+
+def next_step(w: Workload, bits: np.ndarray, step: int, sigma: float, tag: int) -> np.ndarray:
+    """A following denoising step's tensor: bf16 values plus N(0, sigma^2)
+    noise, drawn per head from default_rng([seed, 7919, step, tag, b, h]) and
+    rounded back to bf16.  bits: uint16 [B,H,N,d] (Q, K or V; tag tells them
+    apart).  Stands in for the slowly changing activations of consecutive
+    diffusion steps."""
+    out = np.empty_like(bits)
+    for b in range(bits.shape[0]):
+        for h in range(bits.shape[1]):
+            rng = np.random.default_rng([w.seed, 7919, step, tag, b, h])
+            x = bf16_bits_to_f32(bits[b, h]) + rng.standard_normal(bits.shape[2:], dtype=np.float32) * np.float32(sigma)
+            out[b, h] = _bf16_round(x.astype(np.float32))
+    return out

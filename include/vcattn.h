@@ -108,6 +108,31 @@ vc_status vsmooth_prepare(const vc_config* cfg, const void* K, const void* V,
                           int32_t* labels, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * vsmooth_prepare_warm: vsmooth_prepare that carries the clustering across
+ * calls (denoising steps: the runtimewire article and the chooseai.io brief
+ * describe running V-Smooth step by step and treating its cost as a
+ * scheduling trade).  cfg->vsmooth must be 1.  Exactly one of
+ *   init_idx        int32 [B,H,k]   cold start, as in vsmooth_prepare;
+ *   init_centroids  fp32 [B,H,k,d]  warm start, e.g. the centroids_out of the
+ *                   previous step; cfg->iters passes (1 is the usual choice);
+ *   perm_in         int32 [B,H,N]   reuse a permutation: no clustering and no
+ *                   sort.  It must be a permutation of 0..N-1 per head;
+ *                   entries outside [0, N) are clamped, so a bad perm_in
+ *                   gives meaningless output but reads nothing outside K, V.
+ *                   perm may equal perm_in.
+ * is non-NULL.  centroids_out (nullable, fp32 [B,H,k,d]) receives the member
+ * means of the final clusters (a cluster with no members keeps its
+ * centroid); it is left untouched when perm_in is given, and labels too.
+ * Other arguments as vsmooth_prepare.
+ */
+vc_status vsmooth_prepare_warm(const vc_config* cfg, const void* K, const void* V,
+                               const int32_t* init_idx, const float* init_centroids,
+                               const int32_t* perm_in, float* centroids_out, uint8_t* Kq,
+                               float* k_scale, uint8_t* Vres, void* v_scale, float* v_mean,
+                               int32_t* perm, int32_t* labels, void* ws, size_t ws_bytes,
+                               hipStream_t stream);
+
+/*
  * vc_attn_fwd: fused forward (chooseai.io brief, "ExpCast-FP8" and the last
  * sentences of "V-Smooth").  Q bf16 [B,H,N,d] in natural order; Kq..v_mean as
  * written by vsmooth_prepare; O [B,H,N,d] bf16 or fp32 (cfg->out_fp32), rows in

@@ -34,7 +34,8 @@ def test_header_declares_expected_entry_points():
     names = declared_functions()
     for want in ("vsmooth_prepare", "vc_attn_fwd", "vc_attention", "vc_prepare_workspace_bytes",
                  "vc_attention_workspace_bytes", "vc_status_str", "vc_last_error", "vc_dbg_expcast",
-                 "vc_dbg_kmeans_assign", "vc_dbg_sort", "vc_mfma_loop", "vc_dbg_exp2cast"):
+                 "vc_dbg_kmeans_assign", "vc_dbg_sort", "vc_mfma_loop", "vc_dbg_exp2cast",
+                 "vsmooth_prepare_warm"):
         assert want in names, want
 
 
@@ -99,3 +100,16 @@ def test_workspace_sizes_grow_with_problem(lib):
     small = lib.vc_attention_workspace_bytes(ctypes.byref(cfg()))
     big = lib.vc_attention_workspace_bytes(ctypes.byref(cfg(N=4000)))
     assert big > 3 * small
+
+
+def test_warm_prepare_needs_exactly_one_start(lib):
+    c = cfg()
+    P = ctypes.c_void_p(256)
+    args = lambda init, cent, perm_in: (ctypes.byref(c), P, P, init, cent, perm_in, None, P, P, P, P, P, P, None, P,
+                                         1 << 40, None)
+    assert lib.vsmooth_prepare_warm(*args(None, None, None)) == VC_ERR_INVALID_ARG
+    assert "exactly one" in lib.vc_last_error().decode()
+    assert lib.vsmooth_prepare_warm(*args(P, P, None)) == VC_ERR_INVALID_ARG
+    assert lib.vsmooth_prepare_warm(*args(P, P, P)) == VC_ERR_INVALID_ARG
+    c.vsmooth = 0
+    assert lib.vsmooth_prepare_warm(*args(P, None, None)) == VC_ERR_INVALID_ARG

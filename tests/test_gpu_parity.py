@@ -261,6 +261,106 @@ def test_bf16_output_and_determinism():
     assert torch.equal(Oa, O32.to(torch.bfloat16)), "bf16 output is not the RNE of the fp32 output"
 
 
+# ------------------------------------------------------------------ prep carried across steps
+def _prep_np(prep, fmt):
+    return prep_to_numpy(prep, fmt)
+
+
+@pytest.mark.parametrize("name,H,N", [("tiny", 2, None), ("mid", 1, 5000)])
+def test_warm_start_and_perm_reuse_bit_exact(name, H, N):
+    # step 0: cold start with centroids_out; step 1 (perturbed K, V): one
+    # warm-started pass from those centroids; step 2: reuse step 1's perm.
+    # Every output is compared with the oracle bit for bit.
+    w = inputs.WORKLOADS[name]
+    host, dev = gen(w, H=H, N=N)
+    N = N or w.N
+    fmt = w.v_format
+    cfg = cfg_for(w, H=H, N=N)
+    k = cfg.n_clusters
+    C0 = torch.empty((1, H, k, w.d), dtype=torch.float32, device="cuda")
+    p0 = vb.vsmooth_prepare_warm(cfg, dev["K"], dev["V"], init_idx=dev["init"], centroids_out=C0)
+    g0 = _prep_np(p0, fmt)
+    C0n = C0.cpu().numpy()
+    q, kb, vb_, init = host
+    k1 = inputs.next_step(w, kb, 1, 0.05, 1)
+    v1 = inputs.next_step(w, vb_, 1, 0.05, 2)
+    cfg1 = cfg_for(w, H=H, N=N)
+    cfg1.iters = 1
+    C1 = torch.empty_like(C0)
+    p1 = vb.vsmooth_prepare_warm(cfg1, to_device_bf16(k1), to_device_bf16(v1), init_centroids=C0, centroids_out=C1)
+    g1 = _prep_np(p1, fmt)
+    C1n = C1.cpu().numpy()
+    k2 = inputs.next_step(w, k1, 2, 0.05, 1)
+    v2 = inputs.next_step(w, v1, 2, 0.05, 2)
+    p2 = vb.vsmooth_prepare_warm(cfg1, to_device_bf16(k2), to_device_bf16(v2), perm_in=p1.perm)
+    g2 = _prep_np(p2, fmt)
+    p2b = vb.alloc_prepared(cfg1)
+    p2b.perm.copy_(p1.perm)
+    vb.vsmooth_prepare_warm(cfg1, to_device_bf16(k2), to_device_bf16(v2), perm_in=p2b.perm, out=p2b)
+    for part in ("Kq", "Vres", "v_mean", "k_scale"):
+        assert torch.equal(getattr(p2b, part), getattr(p2, part)), f"in-place perm reuse differs in {part}"
+    for h in range(H):
+        K0, V0 = oracle.bf16_to_f64(kb[0, h]), oracle.bf16_to_f64(vb_[0, h])
+        o0 = oracle.prepare_head(K0, V0, init[0, h], k, w.iters, w.kv_block, fmt)
+        compare_prep(g0, o0, 0, h, fmt)
+        assert np.array_equal(C0n[0, h], o0["final_centroids"].astype(np.float32)), "cold centroids_out differ"
+        K1, V1 = oracle.bf16_to_f64(k1[0, h]), oracle.bf16_to_f64(v1[0, h])
+        o1 = oracle.prepare_head(K1, V1, None, k, 1, w.kv_block, fmt, init_centroids=C0n[0, h])
+        compare_prep(g1, o1, 0, h, fmt)
+        assert np.array_equal(C1n[0, h], o1["final_centroids"].astype(np.float32)), "warm centroids_out differ"
+        K2, V2 = oracle.bf16_to_f64(k2[0, h]), oracle.bf16_to_f64(v2[0, h])
+        o2 = oracle.prepare_head(K2, V2, None, k, 1, w.kv_block, fmt, perm=o1["perm"])
+        compare_prep(g2, o2, 0, h, fmt, vsmooth=False)
+        moved = np.count_nonzero(g1["labels"][0, h] != g0["labels"][0, h])
+        log(f"  {name} h{h}: {moved} of {N} labels moved between steps")
+
+
+def test_stepper_follows_schedule_bit_exact():
+    # six denoising steps (cold, warm, warm, reuse x3) through the stepper,
+    # each preparation checked against the oracle chain
+    from bit_attention_video_amd.schedule import VSmoothSchedule, VSmoothStepper
+    w = inputs.WORKLOADS["tiny"]
+    host, dev = gen(w, H=1)
+    cfg = cfg_for(w, H=1)
+    st = VSmoothStepper(cfg, VSmoothSchedule(6, vsmooth_frac=0.5, after="reuse"))
+    q, kb, vb_, init = host
+    cents, perm = None, None
+    for step in range(6):
+        if step:
+            kb = inputs.next_step(w, kb, step, 0.05, 1)
+            vb_ = inputs.next_step(w, vb_, step, 0.05, 2)
+        prep = st.prepare(step, to_device_bf16(kb), to_device_bf16(vb_), dev["init"])
+        g = prep_to_numpy(prep, w.v_format)
+        K, V = oracle.bf16_to_f64(kb[0, 0]), oracle.bf16_to_f64(vb_[0, 0])
+        act = st.last_action
+        if act == "cold":
+            o = oracle.prepare_head(K, V, init[0, 0], cfg.n_clusters, w.iters, w.kv_block, w.v_format)
+        elif act == "warm":
+            o = oracle.prepare_head(K, V, None, cfg.n_clusters, 1, w.kv_block, w.v_format, init_centroids=cents)
+        else:
+            o = oracle.prepare_head(K, V, None, cfg.n_clusters, 1, w.kv_block, w.v_format, perm=perm)
+        compare_prep(g, o, 0, 0, w.v_format, vsmooth=act != "reuse")
+        if act != "reuse":
+            cents, perm = o["final_centroids"], o["perm"]
+            assert np.array_equal(st.centroids.cpu().numpy()[0, 0], cents.astype(np.float32))
+    assert [st.schedule.action(i) for i in range(6)] == ["cold", "warm", "warm", "reuse", "reuse", "reuse"]
+
+
+def test_perm_reuse_clamps_entries_outside_the_head():
+    w = inputs.WORKLOADS["tiny"]
+    host, dev = gen(w, H=1, N=700)
+    cfg = cfg_for(w, H=1, N=700)
+    bad = np.random.default_rng(5).permutation(700).astype(np.int32)
+    bad[[3, 100, 699]] = [700, -1, 1 << 30]
+    p = vb.vsmooth_prepare_warm(cfg, dev["K"], dev["V"], perm_in=torch.from_numpy(bad).view(1, 1, 700).cuda())
+    g = _prep_np(p, w.v_format)
+    clamped = np.where((bad >= 0) & (bad < 700), bad, 0).astype(np.int32)
+    o = oracle.prepare_head(oracle.bf16_to_f64(host[1][0, 0]), oracle.bf16_to_f64(host[2][0, 0]), None, cfg.n_clusters,
+                            1, w.kv_block, w.v_format, perm=clamped)
+    g["perm"] = np.where((g["perm"] >= 0) & (g["perm"] < 700), g["perm"], 0)
+    compare_prep(g, o, 0, 0, w.v_format, vsmooth=False)
+
+
 # ------------------------------------------------------------------ full-size workloads, sampled
 @pytest.mark.parametrize("name", ["video", "mxfp4"])
 def test_full_size_sampled(name):
