@@ -84,13 +84,14 @@ __global__ void k_quant_v_i8(const uint16_t* __restrict__ V, const float* __rest
   const size_t i8 = (static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x) * 8;
   if (i8 >= total) return;
   const float s = sV[i8 / per_head];
+  const float y = 1.0f / s;
   const uint4 raw = *reinterpret_cast<const uint4*>(V + i8);
   const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
   uint32_t out[2] = {0u, 0u};
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const uint16_t b = static_cast<uint16_t>(w[e >> 1] >> ((e & 1) * 16));
-    const uint32_t q = static_cast<uint32_t>(i8_code(bf16_to_f32(b), s)) & 0xffu;
+    const uint32_t q = static_cast<uint32_t>(i8_code(bf16_to_f32(b), s, y)) & 0xffu;
     out[e >> 2] |= q << ((e & 3) * 8);
   }
   *reinterpret_cast<uint2*>(Vq + i8) = make_uint2(out[0], out[1]);
@@ -444,6 +445,7 @@ __global__ __launch_bounds__(256) void k_vres_e4m3(const uint16_t* __restrict__ 
   using BR = BlockRows<D, KVB>;
   __shared__ float sMean[D];
   __shared__ float sS[D];
+  __shared__ float sY[D];           // fp32(1 / scale)
   __shared__ __attribute__((aligned(16))) uint32_t sT[D][KVB / 4 + 1];   // codes [channel][position/4]
   const int bh = blockIdx.y, b = blockIdx.x;
   const int p0 = b * KVB;
@@ -452,6 +454,7 @@ __global__ __launch_bounds__(256) void k_vres_e4m3(const uint16_t* __restrict__ 
     const float am = __uint_as_float(vramax[static_cast<size_t>(bh) * D + threadIdx.x]);
     const float sc = am > 0.0f ? am / 448.0f : 1.0f;
     sS[threadIdx.x] = sc;
+    sY[threadIdx.x] = 1.0f / sc;
     sMean[threadIdx.x] = v_mean[(static_cast<size_t>(bh) * nblk + b) * D + threadIdx.x];
     if (b == 0) v_scale[static_cast<size_t>(bh) * D + threadIdx.x] = sc;
   }
@@ -465,14 +468,14 @@ __global__ __launch_bounds__(256) void k_vres_e4m3(const uint16_t* __restrict__ 
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int c = cg * 8 + e;
-        uint32_t word = 0u;
+        const float mc = sMean[c], sc = sS[c], yc = sY[c];
+        float qv[4];
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
           const int pos = p0 + r4 * 4 + rr;
-          const uint32_t code = pos < N ? e4m3_encode((rows.v[pass][rr][e] - sMean[c]) / sS[c]) : 0u;
-          word |= code << (8 * rr);
+          qv[rr] = pos < N ? div_rn(rows.v[pass][rr][e] - mc, sc, yc) : 0.0f;
         }
-        sT[c][r4] = word;
+        sT[c][r4] = e4m3x4(qv[0], qv[1], qv[2], qv[3]);
       }
     }
   }
@@ -562,16 +565,19 @@ __global__ __launch_bounds__(256) void k_ksmooth(const uint16_t* __restrict__ K,
   __syncthreads();
   const float bm = fmaxf(fmaxf(sMax[0], sMax[1]), fmaxf(sMax[2], sMax[3]));
   const float s = bm > 0.0f ? bm / 448.0f : 1.0f;
+  const float y = 1.0f / s;
   if (threadIdx.x == 0) k_scale[static_cast<size_t>(bh) * nblk + b] = s;
   const int prow = (row & ~63) | kstep_row_of_pos(row & 63);
   uint8_t* dst = Kq + (static_cast<size_t>(bh) * nblk * KVB + b * KVB + prow) * D + part * CPT;
 #pragma unroll
   for (int q = 0; q < CPT / 16; ++q) {
-    uint32_t w[4] = {0u, 0u, 0u, 0u};
+    uint32_t w[4];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const uint32_t code = pos < N ? e4m3_encode(x[q * 16 + e] / s) : 0u;
-      w[e >> 2] |= code << (8 * (e & 3));
+    for (int j = 0; j < 4; ++j) {
+      float qv[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) qv[e] = pos < N ? div_rn(x[q * 16 + 4 * j + e], s, y) : 0.0f;
+      w[j] = e4m3x4(qv[0], qv[1], qv[2], qv[3]);
     }
     *reinterpret_cast<uint4*>(dst + q * 16) = make_uint4(w[0], w[1], w[2], w[3]);
   }

@@ -68,9 +68,33 @@ __device__ __forceinline__ uint32_t e2m1_encode(float x) {
   return code | sign;
 }
 
+// x / s rounded once to binary32, given y = fp32(1 / s) rounded once:
+// q = x*y, then one correction from the exact residual x - q*s (Markstein's
+// division with a correctly rounded reciprocal; s > 0 normal, x finite).
+// The sign copy keeps -0 / s = -0.
+__device__ __forceinline__ float div_rn(float x, float s, float y) {
+  const float q = x * y;
+  const float r = __builtin_fmaf(-q, s, x);
+  return __builtin_copysignf(__builtin_fmaf(r, y, q), x);
+}
+
+// E4M3 codes (round to nearest even, sign kept) of four values with
+// |x| < 464, packed little-endian; v_cvt_pk_fp8_f32 converts two per
+// instruction.
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true));
+}
+
 // int8 code of x / s for the k-means distances: clamp(rne(fp32(x / s)), -127, 127)
 __device__ __forceinline__ int32_t i8_code(float x, float s) {
   float r = rintf(x / s);
+  r = fminf(fmaxf(r, -127.0f), 127.0f);
+  return static_cast<int32_t>(r);
+}
+// the same with y = fp32(1 / s) given (see div_rn)
+__device__ __forceinline__ int32_t i8_code(float x, float s, float y) {
+  float r = rintf(div_rn(x, s, y));
   r = fminf(fmaxf(r, -127.0f), 127.0f);
   return static_cast<int32_t>(r);
 }
