@@ -8,6 +8,8 @@
 // facts (per-channel E4M3/NVFP4 residuals after block-mean subtraction).
 // Every sum that feeds a stored value is formed in fp64 in a fixed order, so
 // runs are deterministic.
+#include <climits>
+
 #include "vc_internal.hpp"
 
 namespace vc {
@@ -106,7 +108,7 @@ __global__ void k_init_centroids(const uint16_t* __restrict__ V, const int32_t* 
       bf16_to_f32(V[(static_cast<size_t>(bh) * N + tok) * D + c]);
 }
 
-// int8 centroid codes and the packed distance offsets cn32 = 32*|c|^2 + (row % 32);
+// int8 centroid codes and the packed score offsets cn32 = (31 - row % 32) - 32*|c|^2;
 // rows k..kpad-1 are padding (codes 0, offset INT_MAX: never the minimum).
 template <int D>
 __global__ __launch_bounds__(256) void k_quant_centroids(const float* __restrict__ C,
@@ -130,19 +132,21 @@ __global__ __launch_bounds__(256) void k_quant_centroids(const float* __restrict
   }
   for (int o = 32; o > 0; o >>= 1) sq += __shfl_xor(sq, o, 64);
   if (lane == 0)
-    cn32[static_cast<size_t>(bh) * kpad + i] = i < k ? sq * 32 + (i & 31) : 0x7fffffff;
+    cn32[static_cast<size_t>(bh) * kpad + i] = i < k ? (31 - (i & 31)) - sq * 32 : INT_MIN;
 }
 
 // One assignment pass: label = argmin_c (|c_q|^2 - 2 v_q.c_q), lowest index on
 // ties.  C^T = Cq . Vq^T runs on v_mfma_i32_32x32x32_i8 (exact int32); each
 // lane folds its 16 accumulator rows of a 32-centroid tile into keys
-// 32*D + row-in-tile (min = lowest distance, then lowest row), keeps a tile's
-// minimum only if its distance is strictly lower than the best so far, and
-// the two lane halves that share a token column are merged on (D, index).
+// 32*(2 v.c - |c|^2) + (31 - row-in-tile) = (acc << 6) + cn32 (one shift-add;
+// max = lowest distance, then lowest row; key >> 5 is the score exactly),
+// keeps a tile's maximum only if its score is strictly higher than the best
+// so far, and the two lane halves that share a token column are merged on
+// (score, index).
 // A workgroup covers 256 tokens (4 waves x 2 column tiles of 32); centroids
 // stream through LDS in chunks of 128.
 template <int D>
-__global__ __launch_bounds__(256) void k_kmeans_assign(const int8_t* __restrict__ Vq,
+__global__ __launch_bounds__(256, 2) void k_kmeans_assign(const int8_t* __restrict__ Vq,
                                                        const int8_t* __restrict__ Cq,
                                                        const int32_t* __restrict__ cn32, int N,
                                                        int kpad, int32_t* __restrict__ labels) {
@@ -170,7 +174,7 @@ __global__ __launch_bounds__(256) void k_kmeans_assign(const int8_t* __restrict_
         bop[j][c] = v4i{0, 0, 0, 0};
     }
   }
-  int best[2] = {0x7fffffff, 0x7fffffff};
+  int best[2] = {INT_MIN, INT_MIN};
   int btile[2] = {0, 0};
   for (int c0 = 0; c0 < kpad; c0 += CCH) {
     const int rows = min(CCH, kpad - c0);
@@ -200,22 +204,25 @@ __global__ __launch_bounds__(256) void k_kmeans_assign(const int8_t* __restrict_
 #pragma unroll
         for (int c = 0; c < NDC; ++c)
           acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[c], bop[j][c], acc, 0, 0, 0);
-        int tmin = 0x7fffffff;
+        int key[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) tmin = min(tmin, off[r] - 64 * acc[r]);
+        for (int r = 0; r < 16; ++r) key[r] = static_cast<int>((static_cast<uint32_t>(acc[r]) << 6) + off[r]);
+        int tmax = max(key[0], key[1]);
+#pragma unroll
+        for (int r = 2; r < 16; r += 2) tmax = max(max(tmax, key[r]), key[r + 1]);
         // tiles arrive in increasing index order: a later tile must win on
-        // distance alone (the packed row only orders rows inside one tile)
-        if ((tmin >> 5) < (best[j] >> 5)) { best[j] = tmin; btile[j] = gt; }
+        // score alone (the packed row only orders rows inside one tile)
+        if ((tmax >> 5) > (best[j] >> 5)) { best[j] = tmax; btile[j] = gt; }
       }
     }
   }
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const int dist = best[j] >> 5;
-    const int idx = btile[j] * 32 + (best[j] & 31);
-    const int pd = __shfl_xor(dist, 32, 64);
+    const int score = best[j] >> 5;
+    const int idx = btile[j] * 32 + (31 - (best[j] & 31));
+    const int ps = __shfl_xor(score, 32, 64);
     const int pi = __shfl_xor(idx, 32, 64);
-    const int lab = (pd < dist || (pd == dist && pi < idx)) ? pi : idx;
+    const int lab = (ps > score || (ps == score && pi < idx)) ? pi : idx;
     const int tok = tok0 + j * 32 + col;
     if (g == 0 && tok < N) labels[static_cast<size_t>(bh) * N + tok] = lab;
   }
@@ -532,34 +539,42 @@ __global__ __launch_bounds__(256) void k_vres_mxfp4(const uint16_t* __restrict__
   }
 }
 
-// K smoothing: K' = fp32(K - mu_K) gathered in sorted order; per block
-// s_k = fp32(max|K'| / 448); codes stored in k-step row order.
+// K smoothing and per-block E4M3: K' = K - mean_K (per channel over the
+// head's tokens), gathered in sorted order; s_k = max|K'_block| / 448;
+// Kq = E4M3(K' / s_k) in k-step row order.  Rows are read as whole 16-byte
+// pieces (BlockRows), four rows per wave instruction.
 template <int D, int KVB>
 __global__ __launch_bounds__(256) void k_ksmooth(const uint16_t* __restrict__ K,
                                                  const int32_t* __restrict__ perm,
                                                  const float* __restrict__ mu, int N, int nblk,
                                                  uint8_t* __restrict__ Kq, float* __restrict__ k_scale) {
-  constexpr int TPR = 256 / KVB;      // threads per row
-  constexpr int CPT = D / TPR;        // channels per thread (16, 32 or 64)
+  using BR = BlockRows<D, KVB>;
   __shared__ float sMax[4];
   const int bh = blockIdx.y, b = blockIdx.x;
-  const int row = threadIdx.x / TPR, part = threadIdx.x % TPR;
-  const int pos = b * KVB + row;
-  float x[CPT];
-  float am = 0.0f;
-  if (pos < N) {
-    const int tok = clamp_tok(perm[static_cast<size_t>(bh) * N + pos], N);
-    const uint16_t* kr = K + (static_cast<size_t>(bh) * N + tok) * D + part * CPT;
-    const float* m = mu + static_cast<size_t>(bh) * D + part * CPT;
-#pragma unroll
-    for (int e = 0; e < CPT; ++e) {
-      x[e] = bf16_to_f32(kr[e]) - m[e];
-      am = fmaxf(am, fabsf(x[e]));
-    }
-  } else {
-#pragma unroll
-    for (int e = 0; e < CPT; ++e) x[e] = 0.0f;
+  const int p0 = b * KVB;
+  const int cg = threadIdx.x % BR::CG, q = threadIdx.x / BR::CG;
+  BR rows;
+  rows.load(K + static_cast<size_t>(bh) * N * D, perm + static_cast<size_t>(bh) * N, p0, N);
+  float m[8];
+  {
+    const float4 m0 = *reinterpret_cast<const float4*>(mu + static_cast<size_t>(bh) * D + cg * 8);
+    const float4 m1 = *reinterpret_cast<const float4*>(mu + static_cast<size_t>(bh) * D + cg * 8 + 4);
+    m[0] = m0.x; m[1] = m0.y; m[2] = m0.z; m[3] = m0.w; m[4] = m1.x; m[5] = m1.y; m[6] = m1.z; m[7] = m1.w;
   }
+  float am = 0.0f;
+#pragma unroll
+  for (int ps = 0; ps < BR::PASS; ++ps)
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int r = (ps * BR::RQ + q) * 4 + rr;
+      const bool live = r < KVB && p0 + r < N;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = live ? rows.v[ps][rr][e] - m[e] : 0.0f;
+        rows.v[ps][rr][e] = x;
+        am = fmaxf(am, fabsf(x));
+      }
+    }
   am = wave_max(am);
   if ((threadIdx.x & 63) == 0) sMax[threadIdx.x >> 6] = am;
   __syncthreads();
@@ -567,20 +582,20 @@ __global__ __launch_bounds__(256) void k_ksmooth(const uint16_t* __restrict__ K,
   const float s = bm > 0.0f ? bm / 448.0f : 1.0f;
   const float y = 1.0f / s;
   if (threadIdx.x == 0) k_scale[static_cast<size_t>(bh) * nblk + b] = s;
-  const int prow = (row & ~63) | kstep_row_of_pos(row & 63);
-  uint8_t* dst = Kq + (static_cast<size_t>(bh) * nblk * KVB + b * KVB + prow) * D + part * CPT;
+  uint8_t* dst = Kq + (static_cast<size_t>(bh) * nblk * KVB + p0) * D + cg * 8;
 #pragma unroll
-  for (int q = 0; q < CPT / 16; ++q) {
-    uint32_t w[4];
+  for (int ps = 0; ps < BR::PASS; ++ps)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      float qv[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) qv[e] = pos < N ? div_rn(x[q * 16 + 4 * j + e], s, y) : 0.0f;
-      w[j] = e4m3x4(qv[0], qv[1], qv[2], qv[3]);
+    for (int rr = 0; rr < 4; ++rr) {
+      const int r = (ps * BR::RQ + q) * 4 + rr;
+      if (r < KVB) {
+        const float* x = rows.v[ps][rr];
+        const uint32_t lo = e4m3x4(div_rn(x[0], s, y), div_rn(x[1], s, y), div_rn(x[2], s, y), div_rn(x[3], s, y));
+        const uint32_t hi = e4m3x4(div_rn(x[4], s, y), div_rn(x[5], s, y), div_rn(x[6], s, y), div_rn(x[7], s, y));
+        const int prow = (r & ~63) | kstep_row_of_pos(r & 63);
+        *reinterpret_cast<uint2*>(dst + static_cast<size_t>(prow) * D) = make_uint2(lo, hi);
+      }
     }
-    *reinterpret_cast<uint4*>(dst + q * 16) = make_uint4(w[0], w[1], w[2], w[3]);
-  }
 }
 
 // ---- host launchers ---------------------------------------------------------------
