@@ -291,32 +291,58 @@ __global__ __launch_bounds__(1024) void k_sort_scan(int32_t* __restrict__ hist, 
   }
 }
 
-// Tokens of a chunk are placed in token order: each round of 256 tokens ranks
-// every token among equal labels of the round, then advances the per-label base.
+// Tokens of a chunk are placed in token order.  Each of the 4 waves owns a
+// contiguous quarter of the chunk: per-wave label counts (LDS) prefixed
+// across the waves give each wave its own base per label, and the wave then
+// walks its quarter 64 tokens at a time, ranking a token among the round's
+// equal labels by matching label bits with ballots (the lanes whose label
+// equals this lane's, below it) and advancing its bases.
 __global__ __launch_bounds__(256) void k_sort_scatter(const int32_t* __restrict__ labels,
                                                       const int32_t* __restrict__ hist, int N,
                                                       int k, int nch, int32_t* __restrict__ perm) {
-  __shared__ int32_t base[kMaxClusters];
-  __shared__ int32_t lab[256];
+  constexpr int QW = kSortChunk / 4;            // tokens per wave
+  __shared__ int32_t base[4][kMaxClusters];
   const int bh = blockIdx.y, ch = blockIdx.x;
-  for (int i = threadIdx.x; i < k; i += 256)
-    base[i] = hist[(static_cast<size_t>(bh) * nch + ch) * k + i];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int t0 = ch * kSortChunk, t1 = min(N, t0 + kSortChunk);
-  for (int r0 = t0; r0 < t1; r0 += 256) {
-    const int t = r0 + threadIdx.x;
-    int L = t < t1 ? labels[static_cast<size_t>(bh) * N + t] : -1;
-    if (static_cast<unsigned>(L) >= static_cast<unsigned>(k)) L = -1;   // out-of-range labels are dropped
-    __syncthreads();
-    lab[threadIdx.x] = L;
-    __syncthreads();
-    int before = 0, total = 0;
-    for (int j = 0; j < 256; ++j) {
-      const int lj = lab[j];
-      if (lj == L) { ++total; before += j < static_cast<int>(threadIdx.x) ? 1 : 0; }
+  const int w0 = t0 + wave * QW, w1 = min(t1, w0 + QW);
+  const int32_t* lab = labels + static_cast<size_t>(bh) * N;
+  for (int i = threadIdx.x; i < 4 * kMaxClusters; i += 256) (&base[0][0])[i] = 0;
+  __syncthreads();
+  for (int t = w0 + lane; t < w1; t += 64) {
+    const int L = lab[t];
+    if (static_cast<unsigned>(L) < static_cast<unsigned>(k)) atomicAdd(&base[wave][L], 1);
+  }
+  __syncthreads();
+  for (int L = threadIdx.x; L < k; L += 256) {
+    int run = hist[(static_cast<size_t>(bh) * nch + ch) * k + L];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int c = base[w][L];
+      base[w][L] = run;
+      run += c;
     }
-    if (L >= 0) perm[static_cast<size_t>(bh) * N + base[L] + before] = t;
-    __syncthreads();
-    if (L >= 0 && before == total - 1) base[L] += total;
+  }
+  __syncthreads();
+  int nbits = 1;
+  while ((1 << nbits) < k) ++nbits;
+  const uint64_t below = (1ull << lane) - 1ull;
+  for (int r0 = w0; r0 < w1; r0 += 64) {
+    const int t = r0 + lane;
+    int L = t < w1 ? lab[t] : -1;
+    if (static_cast<unsigned>(L) >= static_cast<unsigned>(k)) L = -1;   // out-of-range labels are dropped
+    uint64_t same = __ballot(L >= 0);
+    for (int bit = 0; bit < nbits; ++bit) {
+      const bool on = (L >> bit) & 1;
+      const uint64_t m = __ballot(on);
+      same &= on ? m : ~m;
+    }
+    const int before = __popcll(same & below);
+    const int total = __popcll(same);
+    int pos = 0;
+    if (L >= 0) pos = base[wave][L];
+    if (L >= 0) perm[static_cast<size_t>(bh) * N + pos + before] = t;
+    if (L >= 0 && before == total - 1) base[wave][L] = pos + total;
   }
 }
 
