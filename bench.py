@@ -57,7 +57,7 @@ def traffic_from_profile(workload: str):
         return None
 
 
-def cpu_baseline(w, host, n_tiles=6):
+def cpu_baseline(w, host, n_tiles=32):
     """The oracle as it stands on one head: full V-Smooth prep plus n_tiles
     query tiles, scaled to the whole job's effective TFLOPS."""
     import oracle
