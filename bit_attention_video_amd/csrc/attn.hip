@@ -80,7 +80,6 @@ __global__ void k_dbg_exp2cast(const float* __restrict__ S, const float* __restr
 }
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
-typedef __attribute__((address_space(1))) void* glb_ptr_t;
 
 // Swizzled 16-byte chunk inside an LDS row of RB bytes.  A 16-byte operand
 // read is served 8 lanes per cycle from 32 banks or 16 lanes per cycle from
@@ -153,34 +152,48 @@ struct LaneOffsets {
 };
 
 // Stage one block (K rows, residual rows, E8M0 scales) into LDS with direct
-// global->LDS loads (global_load_lds_dwordx4: lane i of a wave writes bytes
-// [16i, 16i+16) after the wave-uniform base); the swizzle is applied on the
-// global side by choosing which chunk each lane fetches.
+// buffer->LDS loads (buffer_load_dwordx4 ... lds: lane i of a wave writes
+// bytes [16i, 16i+16) after the wave-uniform LDS base in M0); the swizzle is
+// applied on the global side by choosing which chunk each lane fetches.  The
+// buffer form takes the block offset in an SGPR and the lane offset in a
+// loop-invariant VGPR, so issuing a load costs no vector instructions.  (The
+// FLAT form, global_load_lds, also works, but while one is in flight the
+// compiler's wait-count pass can only drain LDS reads completely, which
+// undoes the operand prefetch below.)
+// raw buffer descriptor over [base, base + bytes) (stride 0, no swizzle)
+#define VC_BUFFER_RSRC(base, bytes) \
+  __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(static_cast<const void*>(base)), 0, static_cast<int>(bytes), 0x00020000)
+
 template <int D, int KVB, int VF>
-__device__ __forceinline__ void stage_block_k(uint8_t* st, const uint8_t* kq_blk, const LaneOffsets<D, KVB, VF>& lo,
-                                              int wave) {
+__device__ __forceinline__ void stage_block_k(uint8_t* st, const uint8_t* kq, uint32_t kq_bytes, uint32_t blk_off,
+                                              const LaneOffsets<D, KVB, VF>& lo, int wave) {
   using T = AttnTile<D, KVB, VF>;
   using L = LaneOffsets<D, KVB, VF>;
+  const auto rs = VC_BUFFER_RSRC(kq, kq_bytes);
 #pragma unroll
   for (int r = 0; r < L::KR; ++r)
     if ((r * T::NTH + wave * 64) * 16 < T::KBYTES)
-      __builtin_amdgcn_global_load_lds((glb_ptr_t)(kq_blk + lo.k_src + r * L::RB),
-                                       (lds_ptr_t)(st + (r * T::NTH + wave * 64) * 16), 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(st + (r * T::NTH + wave * 64) * 16), 16,
+                                               static_cast<uint32_t>(lo.k_src), blk_off + static_cast<uint32_t>(r * L::RB), 0, 0);
 }
 
 template <int D, int KVB, int VF>
-__device__ __forceinline__ void stage_block_v(uint8_t* sv, const uint8_t* vr_blk, const uint8_t* sc_blk,
+__device__ __forceinline__ void stage_block_v(uint8_t* sv, const uint8_t* vr, uint32_t vr_bytes, uint32_t blk_off,
+                                              const uint8_t* sc, uint32_t sc_bytes, uint32_t sc_off,
                                               const LaneOffsets<D, KVB, VF>& lo, int wave, int lane) {
   using T = AttnTile<D, KVB, VF>;
   using L = LaneOffsets<D, KVB, VF>;
+  const auto rs = VC_BUFFER_RSRC(vr, vr_bytes);
 #pragma unroll
   for (int r = 0; r < L::VR; ++r)
     if ((r * T::NTH + wave * 64) * 16 < T::VBYTES)
-      __builtin_amdgcn_global_load_lds((glb_ptr_t)(vr_blk + lo.v_src + r * L::RB),
-                                       (lds_ptr_t)(sv + (r * T::NTH + wave * 64) * 16), 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(sv + (r * T::NTH + wave * 64) * 16), 16,
+                                               static_cast<uint32_t>(lo.v_src), blk_off + static_cast<uint32_t>(r * L::RB), 0, 0);
   if constexpr (VF == 1) {
+    const auto rsc = VC_BUFFER_RSRC(sc, sc_bytes);
     if (wave == 0 && lane < T::SBYTES / 16)
-      __builtin_amdgcn_global_load_lds((glb_ptr_t)(sc_blk + lane * 16), (lds_ptr_t)(sv + T::VBYTES), 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsc, (lds_ptr_t)(sv + T::VBYTES), 16, static_cast<uint32_t>(lane * 16),
+                                               sc_off, 0, 0);
   }
 }
 
@@ -493,6 +506,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_fwd(AttnArgs p) {
   __shared__ float sRed[TT::NWV];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 5, col = lane & 31;
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);   // the wave index in a scalar register
   const int N = p.N, nblk = p.nblk;
   const int nqt = (N + TT::ROWS - 1) / TT::ROWS;
   const int bh = blockIdx.x / nqt, qt = blockIdx.x % nqt;
@@ -516,12 +530,17 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_fwd(AttnArgs p) {
   };
   using P0 = std::integral_constant<int, 0>;
   using P1 = std::integral_constant<int, 1>;
+  // direct loads address this head's Kq, residual rows and E8M0 scales
+  // through buffer descriptors: block offset in a scalar, lane offset fixed
+  const uint32_t kq_bytes = static_cast<uint32_t>(nblk) * TT::KBYTES;
+  const uint32_t vr_bytes = static_cast<uint32_t>(nblk) * TT::VBYTES;
+  const uint32_t sc_bytes = VF == 1 ? static_cast<uint32_t>(nblk) * TT::SBYTES : 0u;
   auto stage_k = [&](int j, auto par) {   // K_j into slot par = j & 1
-    stage_block_k<D, KVB, VF>(kslot(par), kq + static_cast<size_t>(j) * KVB * D, lo, wave);
+    stage_block_k<D, KVB, VF>(kslot(par), kq, kq_bytes, static_cast<uint32_t>(j) * TT::KBYTES, lo, wave_s);
   };
   auto stage_v = [&](int j, auto par) {   // V_j (and its E8M0 scales) into slot par = j & 1
-    stage_block_v<D, KVB, VF>(vslot(par), vr + static_cast<size_t>(j) * NKS * D * VROW,
-                              VF == 1 ? scb + static_cast<size_t>(j) * (KVB / 32) * D : nullptr, lo, wave, lane);
+    stage_block_v<D, KVB, VF>(vslot(par), vr, vr_bytes, static_cast<uint32_t>(j) * TT::VBYTES, scb, sc_bytes,
+                              static_cast<uint32_t>(j) * TT::SBYTES, lo, wave_s, lane);
   };
   stage_k(0, P0{});
   stage_v(0, P0{});
