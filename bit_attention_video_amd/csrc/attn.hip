@@ -334,10 +334,11 @@ __device__ __forceinline__ void mean_flush(SoftmaxState<D / 32, AttnTile<D, KVB,
 // Row maximum, ExpCast, row sums and P.V of block b from its scores S, with
 // the next block's S^T (into the same registers, tile by tile) interleaved
 // as planned above.  pmax: per-lane maximum of S (before the cross-lane
-// step); on return it holds the next block's.
-template <int D, int KVB, int VF, int PM, bool MASK>
+// step); on return it holds the next block's.  hook(i) runs right after
+// matrix instruction i is issued (the caller puts its direct loads there).
+template <int D, int KVB, int VF, int PM, bool MASK, typename Hook>
 __device__ __forceinline__ void block_step(
-    SoftmaxState<D / 32, AttnTile<D, KVB, VF>::MSLOT>& st, v16f* S, float& pmax,
+    Hook&& hook, SoftmaxState<D / 32, AttnTile<D, KVB, VF>::MSLOT>& st, v16f* S, float& pmax,
     const uint8_t* sV, const uint8_t* sKn, const LaneOffsets<D, KVB, VF>& lo, const v8i* qb,
     float cb, float kc, int b, int nvalid, int g, int col) {
   using TT = AttnTile<D, KVB, VF>;
@@ -466,6 +467,7 @@ __device__ __forceinline__ void block_step(
         pin(pmax);
       }
     });
+    hook(ic);
     __builtin_amdgcn_sched_barrier(0);
   });
   static_for<NKT>([&](auto ktc) {
@@ -630,24 +632,35 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_fwd(AttnArgs p) {
 
   // one block step: softmax and P.V of block b from S, then (into the same
   // registers, whose scores ExpCast has consumed) S^T of block b+1, whose K
-  // was staged two blocks ahead; the mean flush and the next loads follow
-  // (par = b & 1 names the slots: V_b and K_{b+2} in slot par, K_{b+1} and
-  // V_{b+1} in the other)
+  // was staged two blocks ahead; the mean flush follows (par = b & 1 names
+  // the slots: V_b and K_{b+2} in slot par, K_{b+1} and V_{b+1} in the
+  // other).  The direct loads of K_{b+2} and V_{b+1} go behind the first
+  // and the fifth matrix instruction of the step: issued together at the
+  // step's start, the eight waves' loads queue up and hold the waves back.
   auto step = [&](const int b, auto par, auto masked) {
     constexpr bool MASK = decltype(masked)::value;
     constexpr int PAR = decltype(par)::value;
     using Q = std::integral_constant<int, 1 - PAR>;
+    using PL = StepPlan<D, KVB, VF>;
+    constexpr int SK = 0, SV = PL::M > 4 ? 4 : PL::M - 1;
     float mnext = 0.0f, k_next = 0.0f;
-    if (b + 2 < nblk) stage_k(b + 2, par);
     if (b + 1 < nblk) {
-      stage_v(b + 1, Q{});
       k_next = ks[b + 1];
       if (threadIdx.x < D) mnext = vm[static_cast<size_t>(b + 1) * D + threadIdx.x];
     }
+    auto hook = [&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      if constexpr (i == SK) {
+        if (b + 2 < nblk) stage_k(b + 2, par);
+      }
+      if constexpr (i == SV) {
+        if (b + 1 < nblk) stage_v(b + 1, Q{});
+      }
+    };
     // softmax and P.V of block b, with block b+1's scores made in between
     // (for the last block they come from a stale slot and are discarded)
-    block_step<D, KVB, VF, PM, MASK>(st, S, pmax, vslot(par), kslot(Q{}), lo, qb, cq * k_cur, p.kc, b,
-                                 MASK ? ntail : KVB, g, col);
+    block_step<D, KVB, VF, PM, MASK>(hook, st, S, pmax, vslot(par), kslot(Q{}), lo, qb, cq * k_cur, p.kc, b,
+                                     MASK ? ntail : KVB, g, col);
     if ((b & (MS - 1)) == MS - 1 || b == nblk - 1)
       mean_flush<D, KVB, VF>(st, sM + ((b >> 3) & 1) * 2 * D * MS, g, col);
     if (b + 1 < nblk && threadIdx.x < D) {
