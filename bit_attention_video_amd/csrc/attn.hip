@@ -164,20 +164,21 @@ struct LaneOffsets {
 #define VC_BUFFER_RSRC(base, bytes) \
   __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(static_cast<const void*>(base)), 0, static_cast<int>(bytes), 0x00020000)
 
-template <int D, int KVB, int VF>
+// (R0, R1): the direct-load rounds to issue, [R0, R1)
+template <int D, int KVB, int VF, int R0 = 0, int R1 = 64>
 __device__ __forceinline__ void stage_block_k(uint8_t* st, const uint8_t* kq, uint32_t kq_bytes, uint32_t blk_off,
                                               const LaneOffsets<D, KVB, VF>& lo, int wave) {
   using T = AttnTile<D, KVB, VF>;
   using L = LaneOffsets<D, KVB, VF>;
   const auto rs = VC_BUFFER_RSRC(kq, kq_bytes);
 #pragma unroll
-  for (int r = 0; r < L::KR; ++r)
+  for (int r = R0; r < (R1 < L::KR ? R1 : L::KR); ++r)
     if ((r * T::NTH + wave * 64) * 16 < T::KBYTES)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(st + (r * T::NTH + wave * 64) * 16), 16,
                                                static_cast<uint32_t>(lo.k_src), blk_off + static_cast<uint32_t>(r * L::RB), 0, 0);
 }
 
-template <int D, int KVB, int VF>
+template <int D, int KVB, int VF, int R0 = 0, int R1 = 64>
 __device__ __forceinline__ void stage_block_v(uint8_t* sv, const uint8_t* vr, uint32_t vr_bytes, uint32_t blk_off,
                                               const uint8_t* sc, uint32_t sc_bytes, uint32_t sc_off,
                                               const LaneOffsets<D, KVB, VF>& lo, int wave, int lane) {
@@ -185,11 +186,11 @@ __device__ __forceinline__ void stage_block_v(uint8_t* sv, const uint8_t* vr, ui
   using L = LaneOffsets<D, KVB, VF>;
   const auto rs = VC_BUFFER_RSRC(vr, vr_bytes);
 #pragma unroll
-  for (int r = 0; r < L::VR; ++r)
+  for (int r = R0; r < (R1 < L::VR ? R1 : L::VR); ++r)
     if ((r * T::NTH + wave * 64) * 16 < T::VBYTES)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(sv + (r * T::NTH + wave * 64) * 16), 16,
                                                static_cast<uint32_t>(lo.v_src), blk_off + static_cast<uint32_t>(r * L::RB), 0, 0);
-  if constexpr (VF == 1) {
+  if constexpr (VF == 1 && R0 == 0) {
     const auto rsc = VC_BUFFER_RSRC(sc, sc_bytes);
     if (wave == 0 && lane < T::SBYTES / 16)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsc, (lds_ptr_t)(sv + T::VBYTES), 16, static_cast<uint32_t>(lane * 16),
@@ -537,16 +538,22 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_fwd(AttnArgs p) {
   const uint32_t kq_bytes = static_cast<uint32_t>(nblk) * TT::KBYTES;
   const uint32_t vr_bytes = static_cast<uint32_t>(nblk) * TT::VBYTES;
   const uint32_t sc_bytes = VF == 1 ? static_cast<uint32_t>(nblk) * TT::SBYTES : 0u;
-  auto stage_k = [&](int j, auto par) {   // K_j into slot par = j & 1
-    stage_block_k<D, KVB, VF>(kslot(par), kq, kq_bytes, static_cast<uint32_t>(j) * TT::KBYTES, lo, wave_s);
+  // K_j into slot par = j & 1 (direct-load rounds [R0, R1))
+  auto stage_k = [&](int j, auto par, auto r0, auto r1) {
+    stage_block_k<D, KVB, VF, decltype(r0)::value, decltype(r1)::value>(
+        kslot(par), kq, kq_bytes, static_cast<uint32_t>(j) * TT::KBYTES, lo, wave_s);
   };
-  auto stage_v = [&](int j, auto par) {   // V_j (and its E8M0 scales) into slot par = j & 1
-    stage_block_v<D, KVB, VF>(vslot(par), vr, vr_bytes, static_cast<uint32_t>(j) * TT::VBYTES, scb, sc_bytes,
-                              static_cast<uint32_t>(j) * TT::SBYTES, lo, wave_s, lane);
+  // V_j (and its E8M0 scales) into slot par = j & 1 (rounds [R0, R1))
+  auto stage_v = [&](int j, auto par, auto r0, auto r1) {
+    stage_block_v<D, KVB, VF, decltype(r0)::value, decltype(r1)::value>(
+        vslot(par), vr, vr_bytes, static_cast<uint32_t>(j) * TT::VBYTES, scb, sc_bytes,
+        static_cast<uint32_t>(j) * TT::SBYTES, lo, wave_s, lane);
   };
-  stage_k(0, P0{});
-  stage_v(0, P0{});
-  if (nblk > 1) stage_k(1, P1{});
+  using RA = std::integral_constant<int, 0>;    // all rounds: [0, 64)
+  using RB = std::integral_constant<int, 64>;
+  stage_k(0, P0{}, RA{}, RB{});
+  stage_v(0, P0{}, RA{}, RB{});
+  if (nblk > 1) stage_k(1, P1{}, RA{}, RB{});
 
   for (int i = threadIdx.x; i < 2 * 2 * D * MS; i += TT::NTH) sM[i] = 0;
   float colv = 1.0f;
@@ -634,28 +641,41 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_fwd(AttnArgs p) {
   // registers, whose scores ExpCast has consumed) S^T of block b+1, whose K
   // was staged two blocks ahead; the mean flush follows (par = b & 1 names
   // the slots: V_b and K_{b+2} in slot par, K_{b+1} and V_{b+1} in the
-  // other).  The direct loads of K_{b+2} and V_{b+1} go behind the first
-  // and the fifth matrix instruction of the step: issued together at the
-  // step's start, the eight waves' loads queue up and hold the waves back.
+  // other).  The direct loads of K_{b+2} and V_{b+1} are spread over the
+  // step, one round (one instruction per wave) behind every second matrix
+  // instruction: issued together at the step's start, the eight waves' loads
+  // queue up and hold the waves back.
   auto step = [&](const int b, auto par, auto masked) {
     constexpr bool MASK = decltype(masked)::value;
     constexpr int PAR = decltype(par)::value;
     using Q = std::integral_constant<int, 1 - PAR>;
     using PL = StepPlan<D, KVB, VF>;
-    constexpr int SK = 0, SV = PL::M > 4 ? 4 : PL::M - 1;
+    using LO = LaneOffsets<D, KVB, VF>;
     float mnext = 0.0f, k_next = 0.0f;
     if (b + 1 < nblk) {
       k_next = ks[b + 1];
       if (threadIdx.x < D) mnext = vm[static_cast<size_t>(b + 1) * D + threadIdx.x];
     }
+    // K round r behind matrix instruction 4r, V round r behind 4r+2 (with
+    // ExpCast off, whose exponentials need more registers, all K rounds go
+    // behind instruction 0 and all V rounds behind 4: spreading them further
+    // makes that variant spill inside the loop)
     auto hook = [&](auto ic) {
       constexpr int i = decltype(ic)::value;
-      if constexpr (i == SK) {
-        if (b + 2 < nblk) stage_k(b + 2, par);
-      }
-      if constexpr (i == SV) {
-        if (b + 1 < nblk) stage_v(b + 1, Q{});
-      }
+      static_for<LO::KR>([&](auto rc) {
+        constexpr int r = decltype(rc)::value;
+        constexpr int at = PM == 0 ? 4 * r : 0;
+        if constexpr (i == (at < PL::M ? at : PL::M - 1)) {
+          if (b + 2 < nblk) stage_k(b + 2, par, rc, std::integral_constant<int, r + 1>{});
+        }
+      });
+      static_for<LO::VR>([&](auto rc) {
+        constexpr int r = decltype(rc)::value;
+        constexpr int at = PM == 0 ? 4 * r + 2 : 4;
+        if constexpr (i == (at < PL::M ? at : PL::M - 1)) {
+          if (b + 1 < nblk) stage_v(b + 1, Q{}, rc, std::integral_constant<int, r + 1>{});
+        }
+      });
     };
     // softmax and P.V of block b, with block b+1's scores made in between
     // (for the last block they come from a stale slot and are discarded)
