@@ -232,6 +232,21 @@ def main():
     t_x = float(np.mean(x_ms)) * 1e-3
     log(f"expcast off: attention {t_x * 1e3:.2f} ms")
 
+    # 4-bit residuals (MXFP4, E8M0 scales per 32 sorted tokens and channel) on
+    # the same inputs: preparation and attention time, and below the PSNR
+    # with V-Smooth on and off
+    mx = None
+    if fmt == vb.E4M3:
+        cfg_m = vb.make_config(w.B, w.H, w.N, w.d, w.kv_block, w.k, w.iters, True, vb.MXFP4, False)
+        prep_m = vb.alloc_prepared(cfg_m, "cuda", with_labels=False)
+        ws_m = torch.empty(vb.workspace_bytes(cfg_m), dtype=torch.uint8, device="cuda")
+        O_m = vb.alloc_out(cfg_m)
+        t_mp = timed(lambda: vb.vsmooth_prepare(cfg_m, K, V, I, out=prep_m, ws=ws_m))
+        t_ma = timed(lambda: vb.vc_attn_fwd(cfg_m, Q, prep_m, out=O_m))
+        mx = {"t_prep_ms": round(t_mp, 3), "t_attn_ms": round(t_ma, 3),
+              "attn_tflops": round(w.flops / (t_ma * 1e-3) / 1e12, 2)}
+        log(f"mxfp4 residuals: prep {t_mp:.2f} ms, attention {t_ma:.2f} ms")
+
     if args.calib_copy_mib:
         a = torch.empty(args.calib_copy_mib << 20, dtype=torch.uint8, device="cuda")
         b = torch.empty_like(a)
@@ -243,9 +258,12 @@ def main():
         O_on = O.float().cpu().numpy()
         cfg_off = vb.make_config(w.B, w.H, w.N, w.d, w.kv_block, w.k, w.iters, False, fmt, False)
         O_off = vb.vc_attention(cfg_off, Q, K, V, None).float().cpu().numpy()
-        extra["psnr_db_vs_fp64_exact"] = psnr_report(
-            w, host, {"vsmooth_on": O_on, "vsmooth_off": O_off, "vsmooth_on_expcast_off": O_x.float().cpu().numpy()},
-            [0, w.H - 1])
+        outs = {"vsmooth_on": O_on, "vsmooth_off": O_off, "vsmooth_on_expcast_off": O_x.float().cpu().numpy()}
+        if mx is not None:
+            cfg_moff = vb.make_config(w.B, w.H, w.N, w.d, w.kv_block, w.k, w.iters, False, vb.MXFP4, False)
+            outs["mxfp4_vsmooth_on"] = O_m.float().cpu().numpy()
+            outs["mxfp4_vsmooth_off"] = vb.vc_attention(cfg_moff, Q, K, V, None).float().cpu().numpy()
+        extra["psnr_db_vs_fp64_exact"] = psnr_report(w, host, outs, [0, w.H - 1])
         log(f"psnr {extra['psnr_db_vs_fp64_exact']}")
 
     cpu = None
@@ -283,6 +301,7 @@ def main():
         "expcast_off": {"t_attn_ms": round(t_x * 1e3, 3), "attn_tflops": round(flops / t_x / 1e12, 2),
                         "expcast_speedup": round(t_x / t_fwd, 3)},
         "pct_mfma_loop_attn": round(100 * achieved / loop_tflops, 2),
+        "mxfp4_residuals": mx,
         "roofline": {"bound": "mfma", "kernel": "k_attn_fwd", "achieved": round(achieved, 2),
                      "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4),
                      "traffic": traffic},

@@ -362,7 +362,7 @@ def test_perm_reuse_clamps_entries_outside_the_head():
 
 
 # ------------------------------------------------------------------ full-size workloads, sampled
-@pytest.mark.parametrize("name", ["video", "mxfp4"])
+@pytest.mark.parametrize("name", ["video", "mxfp4", "long"])
 def test_full_size_sampled(name):
     w = inputs.WORKLOADS[name]
     t0 = time.time()
