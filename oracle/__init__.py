@@ -28,10 +28,12 @@ def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
 def prepare_head(K: np.ndarray, V: np.ndarray, init_idx: np.ndarray | None, k: int, iters: int,
                  kv_block: int, fmt: str = "e4m3", vsmooth_on: bool = True,
                  quantize: bool = True, init_centroids: np.ndarray | None = None,
-                 perm: np.ndarray | None = None) -> dict:
+                 perm: np.ndarray | None = None, cluster_order: bool = False) -> dict:
     """K, V: [N, d] fp64 bf16 values of one head.  With V-Smooth on, the
     clustering starts from V[init_idx] or, warm-started, from init_centroids
     (fp32 [k, d]); a given perm is reused as is (no clustering, no sort).
+    cluster_order renumbers the clusters along their principal axis before
+    the final pass (kmeans.order_clusters), so the blocks follow that order.
     "final_centroids" are the member means of the final clusters."""
     N = V.shape[0]
     final = None
@@ -39,7 +41,7 @@ def prepare_head(K: np.ndarray, V: np.ndarray, init_idx: np.ndarray | None, k: i
         labels, cents = None, []
         perm = np.asarray(perm, np.int32)
     elif vsmooth_on:
-        labels, cents, final = kmeans.kmeans(V, init_idx, iters, init_centroids)
+        labels, cents, final = kmeans.kmeans(V, init_idx, iters, init_centroids, cluster_order)
         perm = vsmooth.stable_sort_perm(labels, k)
     else:
         labels, cents = None, []

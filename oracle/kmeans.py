@@ -21,6 +21,21 @@ iteration count.  The readings used here (all stated as readings):
 * Ties go to the lowest cluster index.
 * Update: the fp32 rounding of the fp64 mean of the members' original values;
   a cluster with no members keeps its centroid.
+
+Optional cluster ordering (a blocking variant; [brief] "V-Smooth" asks that
+similar tokens share a hardware block but says nothing of the order of the
+clusters): before the final assignment pass the centroids are renumbered by
+their position along the principal axis of their int8 codes, so that blocks
+which straddle two clusters join similar ones.  Everything is exact integer
+arithmetic, so the order is reproducible bit for bit:
+
+* s = column sums of the codes q [k, d]; S = k * q^T q - s s^T (k^2 times the
+  covariance of the codes);
+* A = S shifted right (floor) by max(0, bitlen(max|S|) - 24);
+* start vector: the column of A with the largest diagonal entry (lowest
+  index on ties); 16 power steps u = A v, each followed by v = u shifted right
+  by max(0, bitlen(max|u|) - 24);
+* projection p_c = q_c . v; rank = position in ascending (p_c, c) order.
 """
 from __future__ import annotations
 
@@ -56,10 +71,49 @@ def update(V: np.ndarray, labels: np.ndarray, C_old: np.ndarray) -> np.ndarray:
     return np.where(counts[:, None] > 0, mean, C_old)
 
 
-def kmeans(V: np.ndarray, init_idx: np.ndarray | None, iters: int, init_centroids: np.ndarray | None = None):
+POWER_STEPS = 16
+AXIS_BITS = 24
+
+
+def _bitlen(x: int) -> int:
+    return int(x).bit_length()
+
+
+def principal_axis_int(q: np.ndarray) -> np.ndarray:
+    """Integer power iteration on k^2 times the covariance of the codes q
+    ([k, d] integers); returns the integer axis v [d] (see the module notes)."""
+    q = np.asarray(q, dtype=np.int64)
+    k, d = q.shape
+    s = q.sum(axis=0)
+    S = k * (q.T @ q) - np.outer(s, s)              # exact: |entries| < 2^40
+    sh = max(0, _bitlen(int(np.max(np.abs(S)))) - AXIS_BITS)
+    A = S >> sh
+    v = A[:, int(np.argmax(np.diag(A)))].copy()
+    for _ in range(POWER_STEPS):
+        u = A @ v                                   # |u| < 2^24 * 2^24 * d
+        m = int(np.max(np.abs(u)))
+        if m == 0:
+            break
+        v = u >> max(0, _bitlen(m) - AXIS_BITS)
+    return v
+
+
+def order_clusters(q: np.ndarray) -> np.ndarray:
+    """rank [k]: position of cluster c in ascending (q_c . axis, c) order."""
+    q = np.asarray(q, dtype=np.int64)
+    p = q @ principal_axis_int(q)
+    order = np.lexsort((np.arange(q.shape[0]), p))  # by p, then by index
+    rank = np.empty(q.shape[0], dtype=np.int32)
+    rank[order] = np.arange(q.shape[0], dtype=np.int32)
+    return rank
+
+
+def kmeans(V: np.ndarray, init_idx: np.ndarray | None, iters: int, init_centroids: np.ndarray | None = None,
+           order: bool = False):
     """V: [N, d] float64 holding the bf16 values of one head.  Starts from the
     rows V[init_idx], or from init_centroids (fp32 [k, d]) when given.
-    Returns (labels int32 [N], centroids_per_pass: the centroids each
+    order: renumber the centroids along their principal axis before the final
+    pass.  Returns (labels int32 [N], centroids_per_pass: the centroids each
     assignment pass used, final: the member means of the final clusters)."""
     sV = int8_scale(V)
     Vq = quant_i8(V, sV)
@@ -70,6 +124,11 @@ def kmeans(V: np.ndarray, init_idx: np.ndarray | None, iters: int, init_centroid
     used = []
     labels = None
     for it in range(iters):
+        if order and it + 1 == iters:
+            rank = order_clusters(quant_i8(C, sV))
+            Cn = np.empty_like(C)
+            Cn[rank] = C
+            C = Cn
         used.append(C.copy())
         labels = assign(Vq, quant_i8(C, sV))
         if it + 1 < iters:

@@ -250,3 +250,77 @@ def test_prepare_with_given_perm_reproduces_the_clustered_prepare():
     for part in ("v", "k"):
         for key, val in full[part].items():
             assert np.array_equal(np.asarray(again[part][key]), np.asarray(val)), (part, key)
+
+
+# ---------------------------------------------------------------- cluster ordering
+def test_order_of_collinear_centroids_is_monotone():
+    # q_c = a_c * u: the principal axis is +-u, so the order follows a_c
+    rng = np.random.default_rng(31)
+    for _ in range(20):
+        u = rng.integers(-4, 5, 16)
+        u[0] = 3
+        a = rng.permutation(np.arange(-25, 26))[:40]
+        q = a[:, None] * u[None, :]
+        rank = KM.order_clusters(q)
+        seq = a[np.argsort(rank)]
+        assert np.all(np.diff(seq) > 0) or np.all(np.diff(seq) < 0)
+
+
+def test_integer_axis_matches_the_top_eigenvector():
+    # a dominant direction plus noise: the integer power iteration lands on
+    # the top eigenvector of the fp64 covariance (numpy.linalg.eigh)
+    rng = np.random.default_rng(32)
+    for d, k in ((16, 64), (64, 256), (128, 1024)):
+        w = rng.standard_normal(d)
+        w /= np.linalg.norm(w)
+        t = rng.standard_normal(k) * 30.0
+        q = np.clip(np.rint(t[:, None] * w[None, :] + rng.standard_normal((k, d)) * 3.0), -127, 127).astype(np.int64)
+        v = KM.principal_axis_int(q).astype(np.float64)
+        ev = np.linalg.eigh(np.cov(q.T.astype(np.float64)))[1][:, -1]
+        cos = abs(v @ ev) / np.linalg.norm(v)
+        assert cos > 0.9999, (d, k, cos)
+
+
+def test_order_is_equivariant_under_relabelling():
+    rng = np.random.default_rng(33)
+    q = rng.integers(-127, 128, (200, 32))
+    rank = KM.order_clusters(q)
+    p = q @ KM.principal_axis_int(q)
+    assert len(np.unique(p)) == len(p)          # no ties: the order is the projection order
+    pi = rng.permutation(200)
+    rank2 = KM.order_clusters(q[pi])
+    assert np.array_equal(rank2, rank[pi])
+
+
+def test_order_ties_and_degenerate_sets():
+    rng = np.random.default_rng(34)
+    q = rng.integers(-50, 51, (30, 8))
+    q[17] = q[4]                                # duplicate: adjacent, lower index first
+    rank = KM.order_clusters(q)
+    assert rank[17] == rank[4] + 1
+    same = np.tile(rng.integers(-9, 10, 8), (12, 1))
+    assert np.array_equal(KM.order_clusters(same), np.arange(12))
+    assert sorted(KM.order_clusters(q)) == list(range(30))
+
+
+def test_ordered_kmeans_renumbers_the_unordered_result():
+    # the final pass with renumbered centroids assigns every token without a
+    # distance tie to the renumbered cluster; the final member means follow
+    w = inputs.WORKLOADS["tiny"]
+    q, k, v, init = inputs.gen_all(w, H=1)
+    V = oracle.bf16_to_f64(v[0, 0])
+    lab0, used0, fin0 = KM.kmeans(V, init[0, 0], w.iters)
+    lab1, used1, fin1 = KM.kmeans(V, init[0, 0], w.iters, order=True)
+    sV = KM.int8_scale(V)
+    Cq = KM.quant_i8(used0[-1], sV)
+    rank = KM.order_clusters(Cq)
+    assert np.array_equal(used1[-1][rank], used0[-1])
+    Vq = KM.quant_i8(V, sV)
+    D = np.sum(Cq * Cq, axis=1)[None, :] - 2.0 * (Vq @ Cq.T)
+    tie = np.sum(D == D.min(axis=1, keepdims=True), axis=1) > 1
+    assert np.array_equal(lab1[~tie], rank[lab0[~tie]])
+    if not tie.any():
+        assert np.array_equal(fin1[rank], fin0)
+    perm1 = oracle.prepare_head(oracle.bf16_to_f64(k[0, 0]), V, init[0, 0], w.k, w.iters, w.kv_block,
+                                cluster_order=True)["perm"]
+    assert np.all(np.diff(lab1[perm1]) >= 0)
