@@ -29,7 +29,8 @@ class VcConfig(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("N", ctypes.c_int32), ("d", ctypes.c_int32),
                 ("kv_block", ctypes.c_int32), ("n_clusters", ctypes.c_int32), ("iters", ctypes.c_int32),
                 ("vsmooth", ctypes.c_int32), ("v_format", ctypes.c_int32), ("out_fp32", ctypes.c_int32),
-                ("softmax_scale", ctypes.c_float), ("beta", ctypes.c_float), ("p_mode", ctypes.c_int32)]
+                ("softmax_scale", ctypes.c_float), ("beta", ctypes.c_float), ("p_mode", ctypes.c_int32),
+                ("cluster_order", ctypes.c_int32)]
 
 
 _lib = None
@@ -88,9 +89,10 @@ def _check(status: int, what: str):
 
 def make_config(B: int, H: int, N: int, d: int, kv_block: int, n_clusters: int = 1, iters: int = 1,
                 vsmooth: bool = True, v_format: int = E4M3, out_fp32: bool = False,
-                softmax_scale: float = 0.0, beta: float = DEFAULT_BETA, p_mode: int = EXPCAST) -> VcConfig:
+                softmax_scale: float = 0.0, beta: float = DEFAULT_BETA, p_mode: int = EXPCAST,
+                cluster_order: bool = False) -> VcConfig:
     return VcConfig(B, H, N, d, kv_block, n_clusters, iters, int(bool(vsmooth)), int(v_format),
-                    int(bool(out_fp32)), softmax_scale, beta, int(p_mode))
+                    int(bool(out_fp32)), softmax_scale, beta, int(p_mode), int(bool(cluster_order)))
 
 
 def _stream():

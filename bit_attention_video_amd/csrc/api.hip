@@ -44,6 +44,8 @@ vc_status validate(const vc_config* c, bool need_kmeans, Dims* out) {
     return fail(VC_ERR_INVALID_ARG, "softmax_scale must be finite and >= 0");
   if (!(c->beta >= -0.5f && c->beta <= 0.45f)) return fail(VC_ERR_INVALID_ARG, "beta must lie in [-0.5, 0.45]");
   if (c->p_mode != 0 && c->p_mode != 1) return fail(VC_ERR_UNSUPPORTED, "p_mode must be 0 (ExpCast) or 1 (exp2 + cast)");
+  if (c->cluster_order != 0 && c->cluster_order != 1)
+    return fail(VC_ERR_UNSUPPORTED, "cluster_order must be 0 (label order) or 1 (principal-axis order)");
   if (need_kmeans) {
     if (c->n_clusters < 1 || c->n_clusters > c->N || c->n_clusters > vc::kMaxClusters)
       return fail(VC_ERR_INVALID_ARG, "n_clusters must lie in [1, min(N, 4096)]");
@@ -92,6 +94,8 @@ void carve_prep(Carver& cv, const Dims& D, vc::PrepArgs& a) {
   a.hist = cv.take<int32_t>(BH * D.nsort * D.k);
   a.counts = cv.take<int32_t>(BH * D.k);
   a.starts = cv.take<int32_t>(BH * D.k);
+  a.rank = cv.take<int32_t>(BH * D.k);
+  a.Ctmp = cv.take<float>(BH * D.k * D.d);
 }
 
 struct OutSizes {
@@ -147,6 +151,7 @@ vc_status run_prepare(const vc_config* c, const Dims& D, vc::PrepArgs& a, const 
     for (int it = 0; it < D.iters; ++it) {
       const bool last = it + 1 == D.iters;
       int32_t* lab = (last && user_labels) ? user_labels : a.labels;
+      if (last && c->cluster_order) VC_TRY(vc::launch_cluster_order(a, st), "cluster_order");
       VC_TRY(vc::launch_assign(a, lab, st), "kmeans_assign");
       if (!last) {
         VC_TRY(vc::launch_sort(a, lab, a.perm_tmp, st), "sort");

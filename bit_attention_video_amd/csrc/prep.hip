@@ -624,6 +624,162 @@ __global__ __launch_bounds__(256) void k_ksmooth(const uint16_t* __restrict__ K,
     }
 }
 
+// ---- cluster order (a blocking variant) --------------------------------------------
+// The clusters can be renumbered along the principal axis of their int8 codes
+// before the final assignment pass, so that a block straddling two clusters
+// joins similar ones (the chooseai.io brief, "V-Smooth", asks only that
+// similar tokens share a hardware block).  All of it is exact integer
+// arithmetic, so the order is reproducible bit for bit.  One workgroup per head:
+//   M = q^T q and the column sums s of the codes q [k, D] in int32 (packed
+//   int8 dot products; |M| <= 4096 * 127^2 < 2^31);
+//   S = k M - s s^T in int64; A = S >> max(0, bitlen(max|S|) - 24), in LDS;
+//   v = the column of A with the largest diagonal entry (lowest index on
+//   ties), then 16 steps u = A v, v = u >> max(0, bitlen(max|u|) - 24);
+//   p_c = q_c . v, rank[c] = #{c' : (p_c', c') < (p_c, c)}.
+constexpr int kOrderThreads = 1024;
+constexpr int kOrderChunk = 128;      // centroid rows per LDS chunk
+constexpr int kOrderSteps = 16;
+constexpr int kOrderBits = 24;
+
+__device__ __forceinline__ int bitlen64(unsigned long long x) { return x ? 64 - __clzll(x) : 0; }
+
+// maximum of x over the workgroup (every thread gets it)
+__device__ __forceinline__ unsigned long long block_max_u64(unsigned long long x, unsigned long long* red) {
+  for (int o = 32; o > 0; o >>= 1) {
+    const unsigned long long y = __shfl_xor(x, o, 64);
+    x = y > x ? y : x;
+  }
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+  __syncthreads();
+  x = 0;
+  for (int w = 0; w < kOrderThreads / 64; ++w) x = red[w] > x ? red[w] : x;
+  return x;
+}
+
+template <int D>
+__global__ __launch_bounds__(kOrderThreads) void k_cluster_order(const int8_t* __restrict__ Cq, int k, int kpad,
+                                                                 int32_t* __restrict__ rank) {
+  constexpr int EPT = D * D / kOrderThreads;        // entries of M per thread
+  constexpr int JG = D / EPT;                       // threads per row of M
+  constexpr int CW = kOrderChunk / 4;               // 4-code words per column of a chunk
+  __shared__ __attribute__((aligned(16))) int8_t sT[D][kOrderChunk];   // chunk, transposed
+  __shared__ int32_t sA[D][D];
+  __shared__ long long sP[kMaxClusters];
+  __shared__ long long sV[D];
+  __shared__ int32_t sS[D];
+  __shared__ unsigned long long sRed[kOrderThreads / 64];
+  __shared__ int sArg;
+  const int bh = blockIdx.x, t = threadIdx.x;
+  const int8_t* q = Cq + static_cast<size_t>(bh) * kpad * D;
+  const int i = t / JG, jb = (t % JG) * EPT;
+
+  int32_t acc[EPT];
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) acc[e] = 0;
+  int32_t colsum = 0;
+  for (int c0 = 0; c0 < k; c0 += kOrderChunk) {
+    // 16 codes of one row per thread, scattered into the transposed chunk
+    for (int x = t; x < kOrderChunk * D / 16; x += kOrderThreads) {
+      const int r = x / (D / 16), j0 = (x % (D / 16)) * 16;
+      uint4 w = make_uint4(0u, 0u, 0u, 0u);
+      if (c0 + r < k) w = *reinterpret_cast<const uint4*>(q + static_cast<size_t>(c0 + r) * D + j0);
+      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int b = 0; b < 16; ++b) sT[j0 + b][r] = static_cast<int8_t>(ws[b >> 2] >> (8 * (b & 3)));
+    }
+    __syncthreads();
+    const int32_t* Ti = reinterpret_cast<const int32_t*>(sT[i]);
+#pragma unroll 4
+    for (int w = 0; w < CW; ++w) {
+      const int32_t a = Ti[w];
+#pragma unroll
+      for (int e = 0; e < EPT; ++e)
+        acc[e] = __builtin_amdgcn_sdot4(a, reinterpret_cast<const int32_t*>(sT[jb + e])[w], acc[e], false);
+    }
+    if (t < D) {
+      const int32_t* Tt = reinterpret_cast<const int32_t*>(sT[t]);
+      for (int w = 0; w < CW; ++w) colsum = __builtin_amdgcn_sdot4(Tt[w], 0x01010101, colsum, false);
+    }
+    __syncthreads();
+  }
+  if (t < D) sS[t] = colsum;
+  __syncthreads();
+
+  // S = k M - s s^T, its shift, and A in LDS
+  long long Sv[EPT];
+  unsigned long long smax = 0;
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    Sv[e] = static_cast<long long>(k) * acc[e] - static_cast<long long>(sS[i]) * sS[jb + e];
+    const unsigned long long m = static_cast<unsigned long long>(Sv[e] < 0 ? -Sv[e] : Sv[e]);
+    smax = m > smax ? m : smax;
+  }
+  smax = block_max_u64(smax, sRed);
+  const int sh = max(0, bitlen64(smax) - kOrderBits);
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) sA[i][jb + e] = static_cast<int32_t>(Sv[e] >> sh);
+  __syncthreads();
+
+  // start: the column with the largest diagonal entry, lowest index on ties
+  if (t < 64) {
+    int best = t, bval = sA[t][t];
+    for (int j = t + 64; j < D; j += 64)
+      if (sA[j][j] > bval) { bval = sA[j][j]; best = j; }
+    for (int o = 32; o > 0; o >>= 1) {
+      const int ov = __shfl_xor(bval, o, 64), oi = __shfl_xor(best, o, 64);
+      if (ov > bval || (ov == bval && oi < best)) { bval = ov; best = oi; }
+    }
+    if (t == 0) sArg = best;
+  }
+  __syncthreads();
+  if (t < D) sV[t] = sA[t][sArg];
+  __syncthreads();
+
+  // power steps: row i of A . v by 8 threads (D = 128) or 16 (D = 64)
+  constexpr int TPR = kOrderThreads / D, SEG = D / TPR;
+  for (int it = 0; it < kOrderSteps; ++it) {
+    const int row = t / TPR, part = t % TPR;
+    long long u = 0;
+#pragma unroll
+    for (int j = part * SEG; j < part * SEG + SEG; ++j) u += static_cast<long long>(sA[row][j]) * sV[j];
+    for (int o = TPR / 2; o > 0; o >>= 1) u += __shfl_xor(u, o, 64);
+    const unsigned long long um = block_max_u64(static_cast<unsigned long long>(u < 0 ? -u : u), sRed);
+    if (um == 0) break;                                   // uniform
+    const int s2 = max(0, bitlen64(um) - kOrderBits);
+    __syncthreads();
+    if (part == 0) sV[row] = u >> s2;
+    __syncthreads();
+  }
+
+  // projections and ranks
+  for (int c = t; c < k; c += kOrderThreads) {
+    const int8_t* qc = q + static_cast<size_t>(c) * D;
+    long long pc = 0;
+    for (int j = 0; j < D; ++j) pc += static_cast<long long>(qc[j]) * sV[j];
+    sP[c] = pc;
+  }
+  __syncthreads();
+  for (int c = t; c < k; c += kOrderThreads) {
+    const long long pc = sP[c];
+    int r = 0;
+    for (int c2 = 0; c2 < k; ++c2) {
+      const long long p2 = sP[c2];
+      r += (p2 < pc) | ((p2 == pc) & (c2 < c));
+    }
+    rank[static_cast<size_t>(bh) * k + c] = r;
+  }
+}
+
+// Cn[rank[c]] = C[c] (fp32 centroid rows of one head)
+template <int D>
+__global__ __launch_bounds__(D) void k_permute_centroids(const float* __restrict__ C, const int32_t* __restrict__ rank,
+                                                         int k, float* __restrict__ Cn) {
+  const int c = blockIdx.x, bh = blockIdx.y;
+  const int r = rank[static_cast<size_t>(bh) * k + c];
+  Cn[(static_cast<size_t>(bh) * k + r) * D + threadIdx.x] = C[(static_cast<size_t>(bh) * k + c) * D + threadIdx.x];
+}
+
 // ---- host launchers ---------------------------------------------------------------
 static inline unsigned blocks_for(size_t n, int per) { return static_cast<unsigned>((n + per - 1) / per); }
 
@@ -675,6 +831,19 @@ static hipError_t assign_t(const PrepArgs& a, int32_t* labels, hipStream_t st) {
 }
 hipError_t launch_assign(const PrepArgs& a, int32_t* labels, hipStream_t st) {
   return a.d == 64 ? assign_t<64>(a, labels, st) : assign_t<128>(a, labels, st);
+}
+
+template <int D>
+static hipError_t order_t(const PrepArgs& a, hipStream_t st) {
+  const int BH = a.B * a.H;
+  hipLaunchKernelGGL(k_quant_centroids<D>, dim3((a.kpad + 3) / 4, BH), dim3(256), 0, st, a.C, a.sV, a.k, a.kpad,
+                     a.Cq, a.cn32);
+  hipLaunchKernelGGL(k_cluster_order<D>, dim3(BH), dim3(kOrderThreads), 0, st, a.Cq, a.k, a.kpad, a.rank);
+  hipLaunchKernelGGL(k_permute_centroids<D>, dim3(a.k, BH), dim3(D), 0, st, a.C, a.rank, a.k, a.Ctmp);
+  return hipMemcpyAsync(a.C, a.Ctmp, static_cast<size_t>(BH) * a.k * D * sizeof(float), hipMemcpyDeviceToDevice, st);
+}
+hipError_t launch_cluster_order(const PrepArgs& a, hipStream_t st) {
+  return a.d == 64 ? order_t<64>(a, st) : order_t<128>(a, st);
 }
 
 hipError_t launch_sort(const PrepArgs& a, const int32_t* labels, int32_t* perm, hipStream_t st) {

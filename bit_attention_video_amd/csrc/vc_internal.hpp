@@ -30,6 +30,8 @@ struct PrepArgs {
   int32_t* counts;     // [BH,k]
   int32_t* starts;     // [BH,k]
   uint32_t* vramax;    // [BH,d]     residual channel max bits
+  int32_t* rank;       // [BH,k]     cluster order (renumbering before the final pass)
+  float* Ctmp;         // [BH,k,d]   renumbered centroids
 };
 
 struct PrepOut {
@@ -59,6 +61,7 @@ hipError_t launch_quant_v_i8(const PrepArgs& a, hipStream_t st);
 hipError_t launch_init_centroids(const PrepArgs& a, const int32_t* init, hipStream_t st);
 hipError_t launch_assign(const PrepArgs& a, int32_t* labels, hipStream_t st);
 hipError_t launch_sort(const PrepArgs& a, const int32_t* labels, int32_t* perm, hipStream_t st);
+hipError_t launch_cluster_order(const PrepArgs& a, hipStream_t st);
 hipError_t launch_update(const PrepArgs& a, const int32_t* perm, hipStream_t st);
 hipError_t launch_iota(int32_t* perm, int N, size_t total, hipStream_t st);
 hipError_t launch_vres_ksmooth(const PrepArgs& a, const int32_t* perm, const PrepOut& o, hipStream_t st);

@@ -81,6 +81,9 @@ typedef struct {
   float beta;               /* ExpCast offset, -0.5 <= beta <= 0.45                */
   int32_t p_mode;           /* 0: ExpCast-FP8 probability bytes; 1: ExpCast off,   */
                             /*    p = E4M3(exp2(x)) (see below)                    */
+  int32_t cluster_order;    /* 0: clusters in k-means label order; 1: renumbered   */
+                            /*    along the principal axis of their int8 codes     */
+                            /*    before the final pass (see vsmooth_prepare)      */
 } vc_config;
 
 /* Bytes of workspace vsmooth_prepare needs (k-means and sort scratch). */
@@ -101,6 +104,11 @@ size_t vc_attention_workspace_bytes(const vc_config* cfg);
  * one per-head scale, ties to the lowest cluster index, fp32 centroid means;
  * stable sort by label and fixed blocks; K smoothed by its per-channel mean
  * and quantised per block.
+ * cfg->cluster_order == 1 (a blocking variant): before the final assignment
+ * pass the centroids are renumbered by their position along the principal
+ * axis of their int8 codes (exact integer covariance and power iteration;
+ * ties to the lower index), so the blocks follow that order; labels and
+ * centroids_out use the new numbering.
  */
 vc_status vsmooth_prepare(const vc_config* cfg, const void* K, const void* V,
                           const int32_t* init_idx, uint8_t* Kq, float* k_scale,

@@ -46,9 +46,13 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def cfg(**kw):
+    raw = {f: kw.pop(f) for f in ("cluster_order",) if f in kw}    # set as given, not as a flag
     base = dict(B=1, H=2, N=1000, d=64, kv_block=64, n_clusters=16, iters=3)
     base.update(kw)
-    return vb.make_config(**base)
+    c = vb.make_config(**base)
+    for f, x in raw.items():
+        setattr(c, f, x)
+    return c
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -63,6 +67,7 @@ def cfg(**kw):
     (dict(beta=-0.6), VC_ERR_INVALID_ARG),
     (dict(v_format=2), VC_ERR_UNSUPPORTED),
     (dict(p_mode=2), VC_ERR_UNSUPPORTED),
+    (dict(cluster_order=2), VC_ERR_UNSUPPORTED),
 ])
 def test_invalid_config_rejected_before_launch(lib, kw, status):
     c = cfg(**kw)

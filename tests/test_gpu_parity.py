@@ -44,11 +44,12 @@ def fmt_id(fmt):
     return vb.E4M3 if fmt == "e4m3" else vb.MXFP4
 
 
-def cfg_for(w, H=None, N=None, vsmooth=True, fmt=None, out_fp32=True, beta=DEFAULT_BETA, mode="expcast"):
+def cfg_for(w, H=None, N=None, vsmooth=True, fmt=None, out_fp32=True, beta=DEFAULT_BETA, mode="expcast",
+            order=False):
     fmt = fmt or w.v_format
     N = N or w.N
     return vb.make_config(w.B, H or w.H, N, w.d, w.kv_block, min(w.k, N), w.iters, vsmooth, fmt_id(fmt),
-                          out_fp32, 0.0, beta, vb.EXPCAST if mode == "expcast" else vb.EXP2_CAST)
+                          out_fp32, 0.0, beta, vb.EXPCAST if mode == "expcast" else vb.EXP2_CAST, order)
 
 
 def gen(w, H=None, N=None):
@@ -359,6 +360,56 @@ def test_perm_reuse_clamps_entries_outside_the_head():
                             1, w.kv_block, w.v_format, perm=clamped)
     g["perm"] = np.where((g["perm"] >= 0) & (g["perm"] < 700), g["perm"], 0)
     compare_prep(g, o, 0, 0, w.v_format, vsmooth=False)
+
+
+# ------------------------------------------------------------------ cluster order (blocking variant)
+@pytest.mark.parametrize("name,H,N,fmt", [
+    ("tiny", 2, None, "e4m3"), ("tiny", 1, 700, "mxfp4"), ("mid", 1, 3000, "e4m3"), ("tiny", 1, 16, "e4m3"),
+])
+def test_cluster_order_prepare_bit_exact(name, H, N, fmt):
+    # renumbered clusters before the final pass: labels, perm, blocks, codes
+    # and means all equal the oracle's, bit for bit
+    w = inputs.WORKLOADS[name]
+    host, dev = gen(w, H=H, N=N)
+    cfg = cfg_for(w, H=H, N=N, fmt=fmt, order=True)
+    g = prep_to_numpy(vb.vsmooth_prepare(cfg, dev["K"], dev["V"], dev["init"]), fmt)
+    q, kb, vb_, init = host
+    for h in range(H):
+        o = oracle.prepare_head(oracle.bf16_to_f64(kb[0, h]), oracle.bf16_to_f64(vb_[0, h]), init[0, h],
+                                cfg.n_clusters, w.iters, w.kv_block, fmt, cluster_order=True)
+        compare_prep(g, o, 0, h, fmt)
+
+
+def test_cluster_order_warm_start_and_attention():
+    # warm start from centroids_out with the order on, then attention on the
+    # ordered blocks against the oracle
+    w = inputs.WORKLOADS["tiny"]
+    host, dev = gen(w, H=2)
+    cfg = cfg_for(w, H=2, order=True)
+    k = cfg.n_clusters
+    C0 = torch.empty((1, 2, k, w.d), dtype=torch.float32, device="cuda")
+    p0 = vb.vsmooth_prepare_warm(cfg, dev["K"], dev["V"], init_idx=dev["init"], centroids_out=C0)
+    cfg1 = cfg_for(w, H=2, order=True)
+    cfg1.iters = 1
+    C1 = torch.empty_like(C0)
+    p1 = vb.vsmooth_prepare_warm(cfg1, dev["K"], dev["V"], init_centroids=C0, centroids_out=C1)
+    g1 = _prep_np(p1, w.v_format)
+    O = vb.vc_attn_fwd(cfg1, dev["Q"], p1).cpu().numpy()
+    q, kb, vb_, init = host
+    C0n, C1n = C0.cpu().numpy(), C1.cpu().numpy()
+    ntile = oracle.n_q_tiles(w.N)
+    for h in range(2):
+        K, V = oracle.bf16_to_f64(kb[0, h]), oracle.bf16_to_f64(vb_[0, h])
+        o0 = oracle.prepare_head(K, V, init[0, h], k, w.iters, w.kv_block, w.v_format, cluster_order=True)
+        assert np.array_equal(C0n[0, h], o0["final_centroids"].astype(np.float32))
+        o1 = oracle.prepare_head(K, V, None, k, 1, w.kv_block, w.v_format, init_centroids=C0n[0, h],
+                                 cluster_order=True)
+        compare_prep(g1, o1, 0, h, w.v_format)
+        assert np.array_equal(C1n[0, h], o1["final_centroids"].astype(np.float32))
+        rows = oracle_rows(w, host, 0, h, o1, list(range(ntile)))
+        Oref = np.concatenate([rows[t] for t in range(ntile)])
+        vmax = float(np.max(np.abs(V)))
+        check_close(O[0, h], Oref, vmax, f"ordered h{h}")
 
 
 # ------------------------------------------------------------------ full-size workloads, sampled
