@@ -247,6 +247,16 @@ def main():
               "attn_tflops": round(w.flops / (t_ma * 1e-3) / 1e12, 2)}
         log(f"mxfp4 residuals: prep {t_mp:.2f} ms, attention {t_ma:.2f} ms")
 
+    # clusters renumbered along their principal axis before the final pass
+    # (a blocking variant): preparation time, PSNR below
+    cfg_o = vb.make_config(w.B, w.H, w.N, w.d, w.kv_block, w.k, w.iters, True, fmt, False, cluster_order=True)
+    prep_o = vb.alloc_prepared(cfg_o, "cuda", with_labels=False)
+    O_o = vb.alloc_out(cfg_o)
+    t_op = timed(lambda: vb.vsmooth_prepare(cfg_o, K, V, I, out=prep_o, ws=ws))
+    vb.vc_attn_fwd(cfg_o, Q, prep_o, out=O_o)
+    ordered = {"t_prep_ms": round(t_op, 3)}
+    log(f"cluster order: prep {t_op:.2f} ms")
+
     if args.calib_copy_mib:
         a = torch.empty(args.calib_copy_mib << 20, dtype=torch.uint8, device="cuda")
         b = torch.empty_like(a)
@@ -259,7 +269,14 @@ def main():
         cfg_off = vb.make_config(w.B, w.H, w.N, w.d, w.kv_block, w.k, w.iters, False, fmt, False)
         O_off = vb.vc_attention(cfg_off, Q, K, V, None).float().cpu().numpy()
         outs = {"vsmooth_on": O_on, "vsmooth_off": O_off, "vsmooth_on_expcast_off": O_x.float().cpu().numpy()}
+        outs["vsmooth_on_cluster_order"] = O_o.float().cpu().numpy()
+        cfg_xo = vb.make_config(w.B, w.H, w.N, w.d, w.kv_block, w.k, w.iters, True, fmt, False,
+                                p_mode=vb.EXP2_CAST, cluster_order=True)
+        outs["vsmooth_on_cluster_order_expcast_off"] = vb.vc_attn_fwd(cfg_xo, Q, prep_o).float().cpu().numpy()
         if mx is not None:
+            cfg_m_o = vb.make_config(w.B, w.H, w.N, w.d, w.kv_block, w.k, w.iters, True, vb.MXFP4, False,
+                                     cluster_order=True)
+            outs["mxfp4_vsmooth_on_cluster_order"] = vb.vc_attention(cfg_m_o, Q, K, V, I).float().cpu().numpy()
             cfg_moff = vb.make_config(w.B, w.H, w.N, w.d, w.kv_block, w.k, w.iters, False, vb.MXFP4, False)
             outs["mxfp4_vsmooth_on"] = O_m.float().cpu().numpy()
             outs["mxfp4_vsmooth_off"] = vb.vc_attention(cfg_moff, Q, K, V, None).float().cpu().numpy()
@@ -302,6 +319,7 @@ def main():
                         "expcast_speedup": round(t_x / t_fwd, 3)},
         "pct_mfma_loop_attn": round(100 * achieved / loop_tflops, 2),
         "mxfp4_residuals": mx,
+        "cluster_order": ordered,
         "roofline": {"bound": "mfma", "kernel": "k_attn_fwd", "achieved": round(achieved, 2),
                      "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4),
                      "traffic": traffic},
