@@ -114,13 +114,13 @@ def e8m0_decode(codes) -> np.ndarray:
     return np.where(c == 255, np.nan, np.ldexp(1.0, (c - 127).astype(np.int64)))
 
 
-def mx_shared_exponent(amax) -> np.ndarray:
-    """OCP MX v1.0 scale rule for E2M1 elements: X = 2^(floor(log2 amax) - 2),
-    2 being E2M1's largest exponent.  The exponent is clamped to E8M0's range;
-    an all-zero block uses X = 1."""
+def mx_shared_exponent(amax, emax: int = 2) -> np.ndarray:
+    """OCP MX v1.0 scale rule: X = 2^(floor(log2 amax) - emax), emax being the
+    element format's largest exponent (E2M1: 2, E4M3: 8).  The exponent is
+    clamped to E8M0's range; an all-zero block uses X = 1."""
     a = np.asarray(amax, dtype=np.float64)
     _, ex = np.frexp(np.where(a > 0, a, 1.0))
-    e = np.where(a > 0, (ex - 1) - 2, 0)
+    e = np.where(a > 0, (ex - 1) - emax, 0)
     return np.clip(e, -127, 127).astype(np.int64)
 
 

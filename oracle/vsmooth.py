@@ -19,6 +19,10 @@ Readings (the pages leave these open):
     code = E4M3(fp32(r / s_v)).  The per-channel scale factors out of P.V.
   * MXFP4 residuals: per 32 consecutive sorted tokens x channel, E8M0 scale
     2^(floor(log2 amax) - 2) and E2M1 elements (OCP MX rule).
+  * MXFP8 residuals (a variant with per-(token group, channel) scales in place
+    of one scale per channel): per 32 consecutive sorted tokens x channel,
+    E8M0 scale 2^(floor(log2 amax) - 8) and E4M3 elements, round to nearest
+    even, saturating at 448 (OCP MX rule for E4M3).
   * K smoothing (prior art the pages contrast V-Smooth with: "earlier
     low-bit methods ... smoothed queries and keys"): mu_K = fp32(fp64 mean over
     all tokens, per channel); K' = fp32(K - mu_K); per block
@@ -69,8 +73,8 @@ def vsmooth_values(V: np.ndarray, perm: np.ndarray, kv_block: int, fmt: str = "e
                    vsmooth: bool = True, quantize: bool = True) -> dict:
     """V: [N, d] fp64 (bf16 values).  Returns natural-layout results:
        codes [nblk*kv_block, d] (E4M3 bytes or E2M1 nibbles, one per element),
-       vres  decoded residual values (E4M3: in units of s_v; MXFP4: real units),
-       col_scale [d] (E4M3: s_v; MXFP4: ones), e8m0 [nblk*kv_block/32, d] (MXFP4),
+       vres  decoded residual values (E4M3: in units of s_v; MX formats: real units),
+       col_scale [d] (E4M3: s_v; MX formats: ones), e8m0 [nblk*kv_block/32, d] (MX),
        means [nblk, d]."""
     N, d = V.shape
     nblk = n_blocks(N, kv_block)
@@ -98,6 +102,14 @@ def vsmooth_values(V: np.ndarray, perm: np.ndarray, kv_block: int, fmt: str = "e
         codes = e2m1_encode(g / np.ldexp(1.0, e)[:, None, :]).reshape(Np, d)
         codes[N:] = 0
         vals = (e2m1_decode(codes).reshape(Np // 32, 32, d) * np.ldexp(1.0, e)[:, None, :]).reshape(Np, d)
+        out.update(codes=codes, vres=vals, col_scale=np.ones(d), e8m0=(e + 127).astype(np.uint8))
+    elif fmt == "mxfp8":
+        g = r.reshape(Np // 32, 32, d)
+        amax = np.max(np.abs(g), axis=1)
+        e = mx_shared_exponent(amax, emax=8)
+        codes = e4m3_encode(g / np.ldexp(1.0, e)[:, None, :]).reshape(Np, d)
+        codes[N:] = 0
+        vals = (e4m3_decode(codes).reshape(Np // 32, 32, d) * np.ldexp(1.0, e)[:, None, :]).reshape(Np, d)
         out.update(codes=codes, vres=vals, col_scale=np.ones(d), e8m0=(e + 127).astype(np.uint8))
     else:
         raise ValueError(fmt)
