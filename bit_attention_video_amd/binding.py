@@ -21,7 +21,7 @@ LIB_PATH = os.environ.get("VCATTN_LIBRARY") or os.path.join(_HERE, "libvcattn.so
 # 8z + 56 + beta on the exact E4M3 code of 2^z over fractional z.
 DEFAULT_BETA = 8.0 / math.log(2.0) - 12.0
 
-E4M3, MXFP4 = 0, 1
+E4M3, MXFP4, MXFP8 = 0, 1, 2    # residual formats
 EXPCAST, EXP2_CAST = 0, 1      # p_mode: ExpCast-FP8 bytes, or exp2 then E4M3 cast
 
 
@@ -143,7 +143,7 @@ def alloc_prepared(cfg: VcConfig, device="cuda", with_labels: bool = True) -> Pr
     nblk = _nblk(cfg)
     Np = nblk * kvb
     u8 = dict(dtype=torch.uint8, device=device)
-    Vres = torch.empty((B, H, Np // 64, d, 64 if cfg.v_format == E4M3 else 32), **u8)
+    Vres = torch.empty((B, H, Np // 64, d, 32 if cfg.v_format == MXFP4 else 64), **u8)
     v_scale = (torch.empty((B, H, d), dtype=torch.float32, device=device) if cfg.v_format == E4M3
                else torch.empty((B, H, Np // 32, d), **u8))
     return Prepared(

@@ -38,7 +38,8 @@ vc_status validate(const vc_config* c, bool need_kmeans, Dims* out) {
   if (c->d != 64 && c->d != 128) return fail(VC_ERR_UNSUPPORTED, "d must be 64 or 128");
   if (c->kv_block != 64 && c->kv_block != 128) return fail(VC_ERR_UNSUPPORTED, "kv_block must be 64 or 128");
   if (c->vsmooth != 0 && c->vsmooth != 1) return fail(VC_ERR_INVALID_ARG, "vsmooth must be 0 or 1");
-  if (c->v_format != 0 && c->v_format != 1) return fail(VC_ERR_UNSUPPORTED, "v_format must be 0 (E4M3) or 1 (MXFP4)");
+  if (c->v_format < 0 || c->v_format > 2)
+    return fail(VC_ERR_UNSUPPORTED, "v_format must be 0 (E4M3), 1 (MXFP4) or 2 (MXFP8)");
   if (c->out_fp32 != 0 && c->out_fp32 != 1) return fail(VC_ERR_INVALID_ARG, "out_fp32 must be 0 or 1");
   if (!(std::isfinite(c->softmax_scale) && c->softmax_scale >= 0.0f))
     return fail(VC_ERR_INVALID_ARG, "softmax_scale must be finite and >= 0");
@@ -107,7 +108,7 @@ OutSizes out_sizes(const Dims& D, int v_format) {
   OutSizes s;
   s.kq = D.BH * Np * D.d;
   s.ks = D.BH * D.nblk;
-  s.vres = D.BH * Np * D.d / (v_format == 0 ? 1 : 2);
+  s.vres = D.BH * Np * D.d / (v_format == 1 ? 2 : 1);
   s.vsc_bytes = v_format == 0 ? D.BH * D.d * sizeof(float) : D.BH * (Np / 32) * D.d;
   s.vmean = D.BH * D.nblk * D.d;
   s.perm = D.BH * D.N;

@@ -109,10 +109,10 @@ struct AttnTile {
   static constexpr int NKT = KVB / 32;    // 32-key tiles of S^T per block
   static constexpr int NKS = KVB / 64;    // 64-key steps of the PV contraction
   static constexpr int NDT = D / 32;      // 32-channel tiles of O^T
-  static constexpr int VROW = VF == 0 ? 64 : 32;
+  static constexpr int VROW = VF == 1 ? 32 : 64;   // residual bytes per channel row of a 64-key step
   static constexpr int KBYTES = KVB * D;
   static constexpr int VBYTES = NKS * D * VROW;
-  static constexpr int SBYTES = VF == 1 ? (KVB / 32) * D : 0;
+  static constexpr int SBYTES = VF != 0 ? (KVB / 32) * D : 0;    // E8M0 scales (MX formats)
   static constexpr int STAGE = KBYTES + VBYTES + (SBYTES + 1023) / 1024 * 1024;
   static constexpr int MSLOT = 8;         // blocks per mean-restoration flush
   static constexpr int NTH = kAttnThreads;
@@ -141,7 +141,7 @@ struct LaneOffsets {
 #pragma unroll
       for (int h = 0; h < 2; ++h) k_rd[c][h] = col * D + swz<D>(col, 4 * c + 2 * g + h) * 16;
     v_rd[0] = col * T::VROW + swz<T::VROW>(col, g) * 16;
-    v_rd[1] = col * T::VROW + swz<T::VROW>(col, VF == 0 ? 2 + g : g) * 16;
+    v_rd[1] = col * T::VROW + swz<T::VROW>(col, VF != 1 ? 2 + g : g) * 16;
     // round r fetches chunk NTH*r + tid: its row is NTH*r/(D/16) rows further
     // down, a multiple of 32, so the swizzled chunk is the same as in round 0
     const int t = threadIdx.x;
@@ -190,7 +190,7 @@ __device__ __forceinline__ void stage_block_v(uint8_t* sv, const uint8_t* vr, ui
     if ((r * T::NTH + wave * 64) * 16 < T::VBYTES)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(sv + (r * T::NTH + wave * 64) * 16), 16,
                                                static_cast<uint32_t>(lo.v_src), blk_off + static_cast<uint32_t>(r * L::RB), 0, 0);
-  if constexpr (VF == 1 && R0 == 0) {
+  if constexpr (VF != 0 && R0 == 0) {
     const auto rsc = VC_BUFFER_RSRC(sc, sc_bytes);
     if (wave == 0 && lane < T::SBYTES / 16)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsc, (lds_ptr_t)(sv + T::VBYTES), 16, static_cast<uint32_t>(lane * 16),
@@ -408,9 +408,12 @@ __device__ __forceinline__ void block_step(
       } else if constexpr (PL::kind(j) == 2) {
         constexpr int sj = PL::step_of(j), T = PL::pv_T(j);
         const uint8_t* vb = sV + (sj * D + 32 * T) * VROW;
-        if constexpr (VF == 0) {
+        if constexpr (VF != 1) {
           opnd[j % 3] = join8(*reinterpret_cast<const uint4*>(vb + lo.v_rd[0]),
                               *reinterpret_cast<const uint4*>(vb + lo.v_rd[1]));
+          // MXFP8: lane group g's scale covers contraction block g, i.e.
+          // sorted positions [32g, 32g+32) of the step (measured)
+          if constexpr (VF == 2) osc[j % 3] = sS[(2 * sj + g) * D + 32 * T + col];
         } else {
           const uint4 q = *reinterpret_cast<const uint4*>(vb + lo.v_rd[0]);
           opnd[j % 3] = v8i{static_cast<int>(q.x), static_cast<int>(q.y), static_cast<int>(q.z),
@@ -454,6 +457,9 @@ __device__ __forceinline__ void block_step(
       if constexpr (VF == 0)
         st.acc[T] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(opnd[i % 3], P[sj], st.acc[T], 0, 0, 0, 0, 0,
                                                                    0);
+      else if constexpr (VF == 2)
+        st.acc[T] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(opnd[i % 3], P[sj], st.acc[T], 0, 0, 0,
+                                                                   osc[i % 3], 0, 127);
       else
         st.acc[T] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(opnd[i % 3], P[sj], st.acc[T], 4, 0, 0,
                                                                    osc[i % 3], 0, 127);
@@ -517,7 +523,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_fwd(AttnArgs p) {
 
   const uint8_t* kq = p.Kq + static_cast<size_t>(bh) * nblk * KVB * D;
   const uint8_t* vr = p.Vres + static_cast<size_t>(bh) * nblk * NKS * D * VROW;
-  const uint8_t* scb = VF == 1 ? reinterpret_cast<const uint8_t*>(p.v_scale) +
+  const uint8_t* scb = VF != 0 ? reinterpret_cast<const uint8_t*>(p.v_scale) +
                                      static_cast<size_t>(bh) * nblk * (KVB / 32) * D
                                : nullptr;
   const float* ks = p.k_scale + static_cast<size_t>(bh) * nblk;
@@ -537,7 +543,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_fwd(AttnArgs p) {
   // through buffer descriptors: block offset in a scalar, lane offset fixed
   const uint32_t kq_bytes = static_cast<uint32_t>(nblk) * TT::KBYTES;
   const uint32_t vr_bytes = static_cast<uint32_t>(nblk) * TT::VBYTES;
-  const uint32_t sc_bytes = VF == 1 ? static_cast<uint32_t>(nblk) * TT::SBYTES : 0u;
+  const uint32_t sc_bytes = VF != 0 ? static_cast<uint32_t>(nblk) * TT::SBYTES : 0u;
   // K_j into slot par = j & 1 (direct-load rounds [R0, R1))
   auto stage_k = [&](int j, auto par, auto r0, auto r1) {
     stage_block_k<D, KVB, VF, decltype(r0)::value, decltype(r1)::value>(
@@ -750,6 +756,7 @@ static void launch_attn_t(const AttnArgs& a, hipStream_t st) {
 template <int D, int KVB>
 static void launch_attn_f(const AttnArgs& a, hipStream_t st) {
   if (a.v_format == 0) launch_attn_t<D, KVB, 0>(a, st);
+  else if (a.v_format == 2) launch_attn_t<D, KVB, 2>(a, st);
   else launch_attn_t<D, KVB, 1>(a, st);
 }
 

@@ -565,6 +565,57 @@ __global__ __launch_bounds__(256) void k_vres_mxfp4(const uint16_t* __restrict__
   }
 }
 
+// MXFP8 residuals: per 32 sorted positions x channel, E8M0 exponent
+// floor(log2 amax) - 8 (E4M3's largest exponent; clamped to [-127, 127], 0 for
+// an all-zero group) and E4M3 codes of r / 2^e, round to nearest even and
+// saturating at 448; layout as the E4M3 residuals, [Np/64][d][64 bytes].
+template <int D>
+__global__ __launch_bounds__(256) void k_vres_mxfp8(const uint16_t* __restrict__ V,
+                                                    const int32_t* __restrict__ perm,
+                                                    const float* __restrict__ v_mean, int N,
+                                                    int kvb, int nblk, uint8_t* __restrict__ Vres,
+                                                    uint8_t* __restrict__ e8m0) {
+  const int bh = blockIdx.y, b = blockIdx.x;
+  const int p0 = b * kvb;
+  const int32_t* pp = perm + static_cast<size_t>(bh) * N;
+  const uint16_t* vv = V + static_cast<size_t>(bh) * N * D;
+  const float* mean = v_mean + (static_cast<size_t>(bh) * nblk + b) * D;
+  const int ngrp = kvb / 32;
+  for (int w = threadIdx.x; w < D * ngrp; w += 256) {
+    const int c = w % D, grp = w / D;
+    const float mc = mean[c];
+    float r[32];
+    float am = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+      const int pos = p0 + grp * 32 + e;
+      r[e] = pos < N ? bf16_to_f32(vv[static_cast<size_t>(clamp_tok(pp[pos], N)) * D + c]) - mc : 0.0f;
+      am = fmaxf(am, fabsf(r[e]));
+    }
+    int ex = 0;
+    if (am > 0.0f) {
+      int fe;
+      frexpf(am, &fe);                   // am = f * 2^fe, f in [0.5, 1)
+      ex = min(max(fe - 1 - 8, -127), 127);
+    }
+    const int gpos = p0 + grp * 32;
+    e8m0[(static_cast<size_t>(bh) * (nblk * kvb / 32) + gpos / 32) * D + c] = static_cast<uint8_t>(ex + 127);
+    // |r / 2^e| < 512: clamping to 448 first gives the saturating RNE code
+    // (the hardware convert itself does not saturate)
+    uint32_t words[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      float x[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = fminf(fmaxf(ldexpf(r[4 * q + e], -ex), -448.0f), 448.0f);
+      words[q] = e4m3x4(x[0], x[1], x[2], x[3]);
+    }
+    uint8_t* dst = Vres + ((static_cast<size_t>(bh) * (nblk * kvb / 64) + gpos / 64) * D + c) * 64 + (gpos & 63);
+    reinterpret_cast<uint4*>(dst)[0] = make_uint4(words[0], words[1], words[2], words[3]);
+    reinterpret_cast<uint4*>(dst)[1] = make_uint4(words[4], words[5], words[6], words[7]);
+  }
+}
+
 // K smoothing and per-block E4M3: K' = K - mean_K (per channel over the
 // head's tokens), gathered in sorted order; s_k = max|K'_block| / 448;
 // Kq = E4M3(K' / s_k) in k-step row order.  Rows are read as whole 16-byte
@@ -878,8 +929,11 @@ static hipError_t vres_t(const PrepArgs& a, const int32_t* perm, const PrepOut& 
   if (e4)
     hipLaunchKernelGGL((k_vres_e4m3<D, KVB>), dim3(a.nblk, BH), dim3(256), 0, st, a.V, perm, o.v_mean, a.vramax,
                        a.N, a.nblk, o.Vres, reinterpret_cast<float*>(o.v_scale));
-  else
+  else if (a.v_format == 1)
     hipLaunchKernelGGL(k_vres_mxfp4<D>, dim3(a.nblk, BH), dim3(256), 0, st, a.V, perm, o.v_mean, a.N, a.kvb,
+                       a.nblk, o.Vres, reinterpret_cast<uint8_t*>(o.v_scale));
+  else
+    hipLaunchKernelGGL(k_vres_mxfp8<D>, dim3(a.nblk, BH), dim3(256), 0, st, a.V, perm, o.v_mean, a.N, a.kvb,
                        a.nblk, o.Vres, reinterpret_cast<uint8_t*>(o.v_scale));
   hipLaunchKernelGGL((k_ksmooth<D, KVB>), dim3(a.nblk, BH), dim3(256), 0, st, a.K, perm, a.mu, a.N, a.nblk, o.Kq,
                      o.k_scale);

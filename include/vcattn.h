@@ -45,8 +45,9 @@
  *                   one 64-byte row per channel (position order).
  *            MXFP4: uint8 [B,H,Np/64,d,32]  same, two E2M1 codes per byte, the
  *                   even position in the low nibble.
+ *            MXFP8: as E4M3 (codes relative to the E8M0 scales below).
  *   v_scale  E4M3:  fp32 [B,H,d]  per-channel residual scale.
- *            MXFP4: uint8 E8M0 [B,H,Np/32,d]  one scale per 32 sorted
+ *            MXFP4, MXFP8: uint8 E8M0 [B,H,Np/32,d]  one scale per 32 sorted
  *                   positions and channel.
  *   v_mean   fp32 [B,H,nblk,d]  block means (zero when V-Smooth is off).
  */
@@ -75,7 +76,9 @@ typedef struct {
   int32_t n_clusters;       /* k-means clusters k, 1 <= k <= min(N, 4096)          */
   int32_t iters;            /* k-means assignment passes I, 1..16                  */
   int32_t vsmooth;          /* 1: V-Smooth on; 0: identity order, zero means       */
-  int32_t v_format;         /* 0: E4M3 residuals, per-channel scale; 1: MXFP4      */
+  int32_t v_format;         /* 0: E4M3 residuals, per-channel scale; 1: MXFP4;     */
+                            /*    2: MXFP8 (E4M3 codes, E8M0 scale per 32 sorted   */
+                            /*    positions and channel)                           */
   int32_t out_fp32;         /* 0: O is bf16; 1: O is fp32                          */
   float softmax_scale;      /* 0 selects fp32(1/sqrt(d))                           */
   float beta;               /* ExpCast offset, -0.5 <= beta <= 0.45                */

@@ -41,7 +41,7 @@ def _gpu():
 
 
 def fmt_id(fmt):
-    return vb.E4M3 if fmt == "e4m3" else vb.MXFP4
+    return {"e4m3": vb.E4M3, "mxfp4": vb.MXFP4, "mxfp8": vb.MXFP8}[fmt]
 
 
 def cfg_for(w, H=None, N=None, vsmooth=True, fmt=None, out_fp32=True, beta=DEFAULT_BETA, mode="expcast",
@@ -197,7 +197,8 @@ def test_kmeans_assign_given_oracle_centroids(name, H, N):
 @pytest.mark.parametrize("name,H,N,vsmooth,fmt", [
     ("tiny", 2, None, True, "e4m3"), ("tiny", 2, None, False, "e4m3"), ("tiny", 2, None, True, "mxfp4"),
     ("tiny", 1, 1000, True, "e4m3"), ("tiny", 1, 1, True, "e4m3"), ("mid", 2, None, True, "e4m3"),
-    ("mid", 1, 3000, True, "mxfp4"),
+    ("mid", 1, 3000, True, "mxfp4"), ("tiny", 2, None, True, "mxfp8"), ("mid", 1, 3000, True, "mxfp8"),
+    ("tiny", 1, 1000, False, "mxfp8"),
 ])
 def test_prepare_bit_exact(name, H, N, vsmooth, fmt):
     w = inputs.WORKLOADS[name]
@@ -227,6 +228,9 @@ def oracle_rows(w, host, b, h, prep_o, tiles, beta=DEFAULT_BETA, mode="expcast")
     ("tiny", 2, None, True, "e4m3", None, None, "exp2"),       # ExpCast off
     ("tiny", 1, 1000, False, "mxfp4", 128, 128, "exp2"),
     ("mid", 2, None, True, "e4m3", None, None, "exp2"),
+    ("tiny", 2, None, True, "mxfp8", None, None, "expcast"),     # per-(32 tokens, channel) E8M0 scales
+    ("tiny", 1, 1000, True, "mxfp8", 128, 128, "expcast"),
+    ("mid", 1, 5000, True, "mxfp8", None, None, "exp2"),
 ])
 def test_attention_parity(name, H, N, vsmooth, fmt, kvb, d, mode):
     import dataclasses
