@@ -124,6 +124,19 @@ def mx_shared_exponent(amax, emax: int = 2) -> np.ndarray:
     return np.clip(e, -127, 127).astype(np.int64)
 
 
+def e4m3_group_exponent(amax) -> np.ndarray:
+    """Power-of-two scale for a group of E4M3 elements: the smallest e with
+    amax <= 448 * 2^e, so no element saturates (OCP MX's floor(log2 amax) - 8
+    lets the group maximum clamp by up to 12.5%).  Clamped to E8M0's range; an
+    all-zero group uses 2^0."""
+    a = np.asarray(amax, dtype=np.float64)
+    _, ex = np.frexp(np.where(a > 0, a, 1.0))
+    e0 = (ex - 1) - 8                                # floor(log2 amax) - 8
+    e = np.where(a > 448.0 * np.ldexp(1.0, e0), e0 + 1, e0)
+    e = np.where(a > 0, e, 0)
+    return np.clip(e, -127, 127).astype(np.int64)
+
+
 # ------------------------------------------------------- fp32 fused multiply-add
 def fma_f32(a, b, c) -> np.ndarray:
     """Correctly rounded binary32 fma(a, b, c) for binary32 inputs.

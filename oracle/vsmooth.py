@@ -20,9 +20,9 @@ Readings (the pages leave these open):
   * MXFP4 residuals: per 32 consecutive sorted tokens x channel, E8M0 scale
     2^(floor(log2 amax) - 2) and E2M1 elements (OCP MX rule).
   * MXFP8 residuals (a variant with per-(token group, channel) scales in place
-    of one scale per channel): per 32 consecutive sorted tokens x channel,
-    E8M0 scale 2^(floor(log2 amax) - 8) and E4M3 elements, round to nearest
-    even, saturating at 448 (OCP MX rule for E4M3).
+    of one scale per channel): per 32 consecutive sorted tokens x channel an
+    E8M0 scale 2^e, e the smallest integer with amax <= 448 * 2^e (so no
+    element saturates), and E4M3 elements of r / 2^e, round to nearest even.
   * K smoothing (prior art the pages contrast V-Smooth with: "earlier
     low-bit methods ... smoothed queries and keys"): mu_K = fp32(fp64 mean over
     all tokens, per channel); K' = fp32(K - mu_K); per block
@@ -36,7 +36,8 @@ from __future__ import annotations
 
 import numpy as np
 
-from .formats import f32, e4m3_encode, e4m3_decode, e2m1_encode, e2m1_decode, mx_shared_exponent
+from .formats import (f32, e4m3_encode, e4m3_decode, e2m1_encode, e2m1_decode, mx_shared_exponent,
+                      e4m3_group_exponent)
 
 
 def stable_sort_perm(labels: np.ndarray, k: int) -> np.ndarray:
@@ -106,7 +107,7 @@ def vsmooth_values(V: np.ndarray, perm: np.ndarray, kv_block: int, fmt: str = "e
     elif fmt == "mxfp8":
         g = r.reshape(Np // 32, 32, d)
         amax = np.max(np.abs(g), axis=1)
-        e = mx_shared_exponent(amax, emax=8)
+        e = e4m3_group_exponent(amax)
         codes = e4m3_encode(g / np.ldexp(1.0, e)[:, None, :]).reshape(Np, d)
         codes[N:] = 0
         vals = (e4m3_decode(codes).reshape(Np // 32, 32, d) * np.ldexp(1.0, e)[:, None, :]).reshape(Np, d)

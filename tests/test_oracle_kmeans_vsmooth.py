@@ -165,10 +165,10 @@ def test_mxfp4_residuals_within_block_bound():
 
 
 def test_mxfp8_residuals_scale_rule_and_bound():
-    # OCP MX for E4M3 elements: the group maximum lands in [256 X, 512 X);
-    # values up to 448 X round to nearest even on the E4M3 grid (relative
-    # step 2^-3 for normals, absolute 2^-9 X below 2^-6 X), larger ones
-    # saturate at 448 X
+    # the group scale is the smallest power of two with amax <= 448 X, so the
+    # group maximum lands in (224 X, 448 X] and nothing saturates; every
+    # element rounds to nearest even on the E4M3 grid (relative step 2^-3 for
+    # normals, absolute 2^-9 X below 2^-6 X)
     rng = np.random.default_rng(18)
     N, d, kvb = 300, 6, 64
     V = F.f32(rng.standard_normal((N, d)) * np.array([0.01, 0.3, 1, 3, 30, 200]))
@@ -181,22 +181,23 @@ def test_mxfp8_residuals_scale_rule_and_bound():
     X = F.e8m0_decode(out["e8m0"].astype(np.int64))              # [Np/32, d]
     amax = np.max(np.abs(r.reshape(Np // 32, 32, d)), axis=1)
     live = amax > 0
-    assert np.all((amax[live] / X[live] >= 256) & (amax[live] / X[live] < 512))
+    assert np.all((amax[live] / X[live] > 224) & (amax[live] / X[live] <= 448))
     Xe = np.repeat(X, 32, axis=0)
     a = np.abs(r) / Xe
     ulp = np.where(a < 2.0 ** -6, 2.0 ** -9, 2.0 ** (np.floor(np.log2(np.maximum(a, 2.0 ** -6))) - 3))
     err = np.abs(out["vres"] - r) / Xe
-    assert np.all(err <= ulp / 2 + np.maximum(a - 448, 0) + 1e-12)
+    assert np.all(err <= ulp / 2 + 1e-12)
     # decoded = code value times the group scale, exactly
     assert np.array_equal(out["vres"], F.e4m3_decode(out["codes"]) * Xe)
     assert np.all(out["codes"][N:] == 0) and np.all(out["col_scale"] == 1)
 
 
 def test_mx_exponent_rule_examples():
-    # X = 2^(floor(log2 amax) - emax): E2M1 emax 2, E4M3 emax 8
-    amax = np.array([1.0, 448.0, 500.0, 0.75, 2.0 ** -130, 0.0])
-    assert list(F.mx_shared_exponent(amax, 8)) == [-8, 0, 0, -9, -127, 0]
-    assert list(F.mx_shared_exponent(amax, 2)) == [-2, 6, 6, -3, -127, 0]
+    # OCP MX X = 2^(floor(log2 amax) - emax) (E2M1: emax 2); E4M3 groups: the
+    # smallest power of two with amax <= 448 X
+    amax = np.array([1.0, 448.0, 449.0, 500.0, 0.75, 2.0 ** -130, 0.0, 224.0])
+    assert list(F.mx_shared_exponent(amax, 2)) == [-2, 6, 6, 6, -3, -127, 0, 5]
+    assert list(F.e4m3_group_exponent(amax)) == [-8, 0, 1, 1, -9, -127, 0, -1]
 
 
 def test_vsmooth_off_is_plain_per_channel_quantisation():
