@@ -232,20 +232,23 @@ def main():
     t_x = float(np.mean(x_ms)) * 1e-3
     log(f"expcast off: attention {t_x * 1e3:.2f} ms")
 
-    # 4-bit residuals (MXFP4, E8M0 scales per 32 sorted tokens and channel) on
-    # the same inputs: preparation and attention time, and below the PSNR
-    # with V-Smooth on and off
-    mx = None
+    # MX residual formats on the same inputs (E8M0 scales per 32 sorted tokens
+    # and channel; elements E2M1 for MXFP4, E4M3 for MXFP8): preparation and
+    # attention time, and below the PSNR with V-Smooth on and off
+    mx, mx_out = {}, {}
     if fmt == vb.E4M3:
-        cfg_m = vb.make_config(w.B, w.H, w.N, w.d, w.kv_block, w.k, w.iters, True, vb.MXFP4, False)
-        prep_m = vb.alloc_prepared(cfg_m, "cuda", with_labels=False)
-        ws_m = torch.empty(vb.workspace_bytes(cfg_m), dtype=torch.uint8, device="cuda")
-        O_m = vb.alloc_out(cfg_m)
-        t_mp = timed(lambda: vb.vsmooth_prepare(cfg_m, K, V, I, out=prep_m, ws=ws_m))
-        t_ma = timed(lambda: vb.vc_attn_fwd(cfg_m, Q, prep_m, out=O_m))
-        mx = {"t_prep_ms": round(t_mp, 3), "t_attn_ms": round(t_ma, 3),
-              "attn_tflops": round(w.flops / (t_ma * 1e-3) / 1e12, 2)}
-        log(f"mxfp4 residuals: prep {t_mp:.2f} ms, attention {t_ma:.2f} ms")
+        for name, f in (("mxfp4", vb.MXFP4), ("mxfp8", vb.MXFP8)):
+            cfg_m = vb.make_config(w.B, w.H, w.N, w.d, w.kv_block, w.k, w.iters, True, f, False)
+            prep_m = vb.alloc_prepared(cfg_m, "cuda", with_labels=False)
+            ws_m = torch.empty(vb.workspace_bytes(cfg_m), dtype=torch.uint8, device="cuda")
+            O_m = vb.alloc_out(cfg_m)
+            t_mp = timed(lambda: vb.vsmooth_prepare(cfg_m, K, V, I, out=prep_m, ws=ws_m))
+            t_ma = timed(lambda: vb.vc_attn_fwd(cfg_m, Q, prep_m, out=O_m))
+            mx[name] = {"t_prep_ms": round(t_mp, 3), "t_attn_ms": round(t_ma, 3),
+                        "attn_tflops": round(w.flops / (t_ma * 1e-3) / 1e12, 2)}
+            mx_out[name] = (f, O_m)
+            del prep_m, ws_m
+            log(f"{name} residuals: prep {t_mp:.2f} ms, attention {t_ma:.2f} ms")
 
     # clusters renumbered along their principal axis before the final pass
     # (a blocking variant): preparation time, PSNR below
@@ -273,13 +276,13 @@ def main():
         cfg_xo = vb.make_config(w.B, w.H, w.N, w.d, w.kv_block, w.k, w.iters, True, fmt, False,
                                 p_mode=vb.EXP2_CAST, cluster_order=True)
         outs["vsmooth_on_cluster_order_expcast_off"] = vb.vc_attn_fwd(cfg_xo, Q, prep_o).float().cpu().numpy()
-        if mx is not None:
-            cfg_m_o = vb.make_config(w.B, w.H, w.N, w.d, w.kv_block, w.k, w.iters, True, vb.MXFP4, False,
-                                     cluster_order=True)
-            outs["mxfp4_vsmooth_on_cluster_order"] = vb.vc_attention(cfg_m_o, Q, K, V, I).float().cpu().numpy()
-            cfg_moff = vb.make_config(w.B, w.H, w.N, w.d, w.kv_block, w.k, w.iters, False, vb.MXFP4, False)
-            outs["mxfp4_vsmooth_on"] = O_m.float().cpu().numpy()
-            outs["mxfp4_vsmooth_off"] = vb.vc_attention(cfg_moff, Q, K, V, None).float().cpu().numpy()
+        for name, (f, O_m) in mx_out.items():
+            cfg_moff = vb.make_config(w.B, w.H, w.N, w.d, w.kv_block, w.k, w.iters, False, f, False)
+            outs[f"{name}_vsmooth_on"] = O_m.float().cpu().numpy()
+            outs[f"{name}_vsmooth_off"] = vb.vc_attention(cfg_moff, Q, K, V, None).float().cpu().numpy()
+            cfg_mx = vb.make_config(w.B, w.H, w.N, w.d, w.kv_block, w.k, w.iters, True, f, False,
+                                    p_mode=vb.EXP2_CAST)
+            outs[f"{name}_vsmooth_on_expcast_off"] = vb.vc_attention(cfg_mx, Q, K, V, I).float().cpu().numpy()
         extra["psnr_db_vs_fp64_exact"] = psnr_report(w, host, outs, [0, w.H - 1])
         log(f"psnr {extra['psnr_db_vs_fp64_exact']}")
 
@@ -318,7 +321,7 @@ def main():
         "expcast_off": {"t_attn_ms": round(t_x * 1e3, 3), "attn_tflops": round(flops / t_x / 1e12, 2),
                         "expcast_speedup": round(t_x / t_fwd, 3)},
         "pct_mfma_loop_attn": round(100 * achieved / loop_tflops, 2),
-        "mxfp4_residuals": mx,
+        "mx_residuals": mx or None,
         "cluster_order": ordered,
         "roofline": {"bound": "mfma", "kernel": "k_attn_fwd", "achieved": round(achieved, 2),
                      "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4),

@@ -394,31 +394,40 @@ __device__ __forceinline__ void block_step(
 
   v8i P[NKS];
   v4f rsum;
-  v8i opnd[3];
-  int osc[3];
+  // operand ring: loads run RD-1 matrix instructions ahead (two for most
+  // formats; one for MXFP8, whose per-lane scales would otherwise push the
+  // step past the register file)
+  constexpr int RD = VF == 2 ? 2 : 3;
+  v8i opnd[RD];
+  // MX formats: the E8M0 scales of this lane for the NDT channel tiles of a
+  // 64-key step, one byte each (stored adjacent), op_sel picks the tile's
+  int osc[NKS];
   (void)osc;
-  // operand of MFMA j into ring slot j % 3
+  // operand of MFMA j into ring slot j % RD
   auto load_opnd = [&](auto jc) {
     constexpr int j = decltype(jc)::value;
     if constexpr (j < PL::M) {
       if constexpr (PL::kind(j) == 0) {
         constexpr int kt = PL::qk_kt(j), c = PL::qk_c(j);
-        opnd[j % 3] = join8(*reinterpret_cast<const uint4*>(sKn + kt * 32 * D + lo.k_rd[c][0]),
+        opnd[j % RD] = join8(*reinterpret_cast<const uint4*>(sKn + kt * 32 * D + lo.k_rd[c][0]),
                             *reinterpret_cast<const uint4*>(sKn + kt * 32 * D + lo.k_rd[c][1]));
       } else if constexpr (PL::kind(j) == 2) {
         constexpr int sj = PL::step_of(j), T = PL::pv_T(j);
         const uint8_t* vb = sV + (sj * D + 32 * T) * VROW;
         if constexpr (VF != 1) {
-          opnd[j % 3] = join8(*reinterpret_cast<const uint4*>(vb + lo.v_rd[0]),
+          opnd[j % RD] = join8(*reinterpret_cast<const uint4*>(vb + lo.v_rd[0]),
                               *reinterpret_cast<const uint4*>(vb + lo.v_rd[1]));
-          // MXFP8: lane group g's scale covers contraction block g, i.e.
-          // sorted positions [32g, 32g+32) of the step (measured)
-          if constexpr (VF == 2) osc[j % 3] = sS[(2 * sj + g) * D + 32 * T + col];
         } else {
           const uint4 q = *reinterpret_cast<const uint4*>(vb + lo.v_rd[0]);
-          opnd[j % 3] = v8i{static_cast<int>(q.x), static_cast<int>(q.y), static_cast<int>(q.z),
+          opnd[j % RD] = v8i{static_cast<int>(q.x), static_cast<int>(q.y), static_cast<int>(q.z),
                             static_cast<int>(q.w), 0, 0, 0, 0};
-          osc[j % 3] = sS[(2 * sj + g) * D + 32 * T + col];
+        }
+        // lane group g's scale covers contraction block g, i.e. sorted
+        // positions [32g, 32g+32) of the step (measured for both MX formats)
+        if constexpr (VF != 0 && T == 0) {
+          const uint8_t* sc = sS + (2 * sj + g) * D + col * NDT;
+          if constexpr (NDT == 4) osc[sj] = *reinterpret_cast<const int*>(sc);
+          else osc[sj] = *reinterpret_cast<const uint16_t*>(sc);
         }
       }
     }
@@ -432,8 +441,7 @@ __device__ __forceinline__ void block_step(
         static_cast<int>(pword4<PM>(sv[4 * q], sv[4 * q + 1], sv[4 * q + 2], sv[4 * q + 3], A8, Bq));
   };
 
-  load_opnd(std::integral_constant<int, 0>{});
-  load_opnd(std::integral_constant<int, 1>{});
+  static_for<RD - 1>([&](auto jc) { load_opnd(jc); });
 #pragma unroll
   for (int q = 0; q < 4; ++q)
     P[0][q] = static_cast<int>(pword4<PM>(S[0][4 * q], S[0][4 * q + 1], S[0][4 * q + 2], S[0][4 * q + 3], A8, Bq));
@@ -441,10 +449,10 @@ __device__ __forceinline__ void block_step(
 
   static_for<PL::M>([&](auto ic) {
     constexpr int i = decltype(ic)::value;
-    load_opnd(std::integral_constant<int, i + 2>{});
+    load_opnd(std::integral_constant<int, i + RD - 1>{});
     if constexpr (PL::kind(i) == 0) {
       constexpr int kt = PL::qk_kt(i), c = PL::qk_c(i);
-      S[kt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(opnd[i % 3], qb[c], c == 0 ? v16f{} : S[kt], 0, 0,
+      S[kt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(opnd[i % RD], qb[c], c == 0 ? v16f{} : S[kt], 0, 0,
                                                              0, 0, 0, 0);
     } else if constexpr (PL::kind(i) == 1) {
       constexpr int sj = PL::step_of(i);
@@ -455,14 +463,14 @@ __device__ __forceinline__ void block_step(
     } else {
       constexpr int sj = PL::step_of(i), T = PL::pv_T(i);
       if constexpr (VF == 0)
-        st.acc[T] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(opnd[i % 3], P[sj], st.acc[T], 0, 0, 0, 0, 0,
+        st.acc[T] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(opnd[i % RD], P[sj], st.acc[T], 0, 0, 0, 0, 0,
                                                                    0);
       else if constexpr (VF == 2)
-        st.acc[T] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(opnd[i % 3], P[sj], st.acc[T], 0, 0, 0,
-                                                                   osc[i % 3], 0, 127);
+        st.acc[T] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(opnd[i % RD], P[sj], st.acc[T], 0, 0, T,
+                                                                   osc[sj], 0, 127);
       else
-        st.acc[T] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(opnd[i % 3], P[sj], st.acc[T], 4, 0, 0,
-                                                                   osc[i % 3], 0, 127);
+        st.acc[T] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(opnd[i % RD], P[sj], st.acc[T], 4, 0, T,
+                                                                   osc[sj], 0, 127);
     }
     static_for<PL::wbeg(i + 1) - PL::wbeg(i)>([&](auto kc2) {
       ecast(std::integral_constant<int, PL::wbeg(i) + decltype(kc2)::value>{});

@@ -556,7 +556,8 @@ __global__ __launch_bounds__(256) void k_vres_mxfp4(const uint16_t* __restrict__
       ex = min(max(fe - 1 - 2, -127), 127);
     }
     const int gpos = p0 + grp * 32;
-    e8m0[(static_cast<size_t>(bh) * (nblk * kvb / 32) + gpos / 32) * D + c] = static_cast<uint8_t>(ex + 127);
+    e8m0[(static_cast<size_t>(bh) * (nblk * kvb / 32) + gpos / 32) * D + mx_scale_slot<D>(c)] =
+        static_cast<uint8_t>(ex + 127);
     uint32_t words[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int e = 0; e < 32; ++e) words[e >> 3] |= e2m1_encode(ldexpf(r[e], -ex)) << (4 * (e & 7));
@@ -565,10 +566,10 @@ __global__ __launch_bounds__(256) void k_vres_mxfp4(const uint16_t* __restrict__
   }
 }
 
-// MXFP8 residuals: per 32 sorted positions x channel, E8M0 exponent
-// floor(log2 amax) - 8 (E4M3's largest exponent; clamped to [-127, 127], 0 for
-// an all-zero group) and E4M3 codes of r / 2^e, round to nearest even and
-// saturating at 448; layout as the E4M3 residuals, [Np/64][d][64 bytes].
+// MXFP8 residuals: per 32 sorted positions x channel, the E8M0 exponent e is
+// the smallest integer with amax <= 448 * 2^e (clamped to [-127, 127], 0 for
+// an all-zero group), so no element saturates; E4M3 codes of r / 2^e, round to
+// nearest even; layout as the E4M3 residuals, [Np/64][d][64 bytes].
 template <int D>
 __global__ __launch_bounds__(256) void k_vres_mxfp8(const uint16_t* __restrict__ V,
                                                     const int32_t* __restrict__ perm,
@@ -596,12 +597,15 @@ __global__ __launch_bounds__(256) void k_vres_mxfp8(const uint16_t* __restrict__
     if (am > 0.0f) {
       int fe;
       frexpf(am, &fe);                   // am = f * 2^fe, f in [0.5, 1)
-      ex = min(max(fe - 1 - 8, -127), 127);
+      ex = fe - 1 - 8;
+      if (am > ldexpf(448.0f, ex)) ++ex;
+      ex = min(max(ex, -127), 127);
     }
     const int gpos = p0 + grp * 32;
-    e8m0[(static_cast<size_t>(bh) * (nblk * kvb / 32) + gpos / 32) * D + c] = static_cast<uint8_t>(ex + 127);
-    // |r / 2^e| < 512: clamping to 448 first gives the saturating RNE code
-    // (the hardware convert itself does not saturate)
+    e8m0[(static_cast<size_t>(bh) * (nblk * kvb / 32) + gpos / 32) * D + mx_scale_slot<D>(c)] =
+        static_cast<uint8_t>(ex + 127);
+    // |r / 2^e| <= 448 unless the exponent clamp binds; the clamp keeps the
+    // hardware convert (which does not saturate) finite then
     uint32_t words[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q) {

@@ -86,6 +86,14 @@ __device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
   return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true));
 }
 
+// MX scale storage order inside one 32-position group: channel c = 32T + col
+// sits at col * (D/32) + T, so the scales of one attention lane (one col, all
+// 32-channel tiles T) are adjacent bytes.
+template <int D>
+__host__ __device__ __forceinline__ int mx_scale_slot(int c) {
+  return (c & 31) * (D / 32) + (c >> 5);
+}
+
 // int8 code of x / s for the k-means distances: clamp(rne(fp32(x / s)), -127, 127)
 __device__ __forceinline__ int32_t i8_code(float x, float s) {
   float r = rintf(x / s);

@@ -48,7 +48,8 @@
  *            MXFP8: as E4M3 (codes relative to the E8M0 scales below).
  *   v_scale  E4M3:  fp32 [B,H,d]  per-channel residual scale.
  *            MXFP4, MXFP8: uint8 E8M0 [B,H,Np/32,d]  one scale per 32 sorted
- *                   positions and channel.
+ *                   positions and channel; inside a group, channel c = 32T + u
+ *                   (u < 32) is stored at byte u * (d/32) + T.
  *   v_mean   fp32 [B,H,nblk,d]  block means (zero when V-Smooth is off).
  */
 #ifndef VCATTN_H

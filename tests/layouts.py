@@ -39,3 +39,11 @@ def vres_natural(Vres: np.ndarray, fmt: str) -> np.ndarray:
 def to_device_bf16(bits: np.ndarray, device="cuda"):
     import torch
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(device)
+
+
+def mx_scales_natural(vs: np.ndarray) -> np.ndarray:
+    """E8M0 scales [..., groups, d] stored in lane order (channel c = 32T + col
+    at col * (d/32) + T) -> natural channel order."""
+    d = vs.shape[-1]
+    c = np.arange(d)
+    return vs[..., (c & 31) * (d // 32) + (c >> 5)]

@@ -20,7 +20,7 @@ from oracle import formats as F
 from oracle.attention import DEFAULT_BETA, exact_attention, exp2cast_bytes, expcast_bytes, softmax_scale
 from bit_attention_video_amd import binding as vb
 from bit_attention_video_amd import inputs
-from layouts import kq_natural, vres_natural, to_device_bf16
+from layouts import kq_natural, mx_scales_natural, vres_natural, to_device_bf16
 
 pytestmark = pytest.mark.gpu
 
@@ -64,6 +64,8 @@ def prep_to_numpy(prep: vb.Prepared, fmt):
     out["labels"] = prep.labels.cpu().numpy() if prep.labels is not None else None
     out["Kq_nat"] = kq_natural(out["Kq"])
     out["Vres_nat"] = vres_natural(out["Vres"], fmt)
+    if fmt != "e4m3":
+        out["v_scale"] = mx_scales_natural(out["v_scale"])
     return out
 
 
