@@ -523,100 +523,120 @@ __global__ __launch_bounds__(256) void k_vres_e4m3(const uint16_t* __restrict__ 
   }
 }
 
-// MXFP4 residuals: per 32 sorted positions x channel, E8M0 exponent
-// floor(log2 amax) - 2 (clamped to [-127, 127]; 0 for an all-zero group) and
-// E2M1 codes of r / 2^e; layout [Np/64][d][32 bytes], even position low nibble.
-template <int D>
-__global__ __launch_bounds__(256) void k_vres_mxfp4(const uint16_t* __restrict__ V,
-                                                    const int32_t* __restrict__ perm,
-                                                    const float* __restrict__ v_mean, int N,
-                                                    int kvb, int nblk, uint8_t* __restrict__ Vres,
-                                                    uint8_t* __restrict__ e8m0) {
+// MX residuals of one block, per 32 sorted positions x channel:
+//   FMT 1, MXFP4: E8M0 exponent floor(log2 amax) - 2 (OCP MX rule), E2M1 codes
+//     of r / 2^e; layout [Np/64][d][32 bytes], even position in the low nibble;
+//   FMT 2, MXFP8: E8M0 exponent e, the smallest integer with amax <= 448 * 2^e
+//     (no element saturates), E4M3 codes of r / 2^e (round to nearest even);
+//     layout as the E4M3 residuals, [Np/64][d][64 bytes].
+// Exponents are clamped to [-127, 127] (0 for an all-zero group); scales are
+// stored in lane order (mx_scale_slot).  Rows are gathered whole by
+// BlockRows; the group maxima meet in LDS (max of the fp32 bit patterns of
+// |r|), then every thread encodes its values into a code tile in LDS, which
+// is written out in 16-byte pieces.
+template <int D, int KVB, int FMT>
+__global__ __launch_bounds__(256) void k_vres_mx(const uint16_t* __restrict__ V, const int32_t* __restrict__ perm,
+                                                 const float* __restrict__ v_mean, int N, int nblk,
+                                                 uint8_t* __restrict__ Vres, uint8_t* __restrict__ e8m0) {
+  using BR = BlockRows<D, KVB>;
+  constexpr int NG = KVB / 32;                       // scale groups per block
+  __shared__ float sMean[D];
+  __shared__ uint32_t sAm[NG][D];
+  __shared__ int sE[NG][D];
+  __shared__ __attribute__((aligned(16))) uint32_t sT[D][KVB / 4 + 1];   // codes [channel][position/4]
   const int bh = blockIdx.y, b = blockIdx.x;
-  const int p0 = b * kvb;
-  const int32_t* pp = perm + static_cast<size_t>(bh) * N;
-  const uint16_t* vv = V + static_cast<size_t>(bh) * N * D;
-  const float* mean = v_mean + (static_cast<size_t>(bh) * nblk + b) * D;
-  const int ngrp = kvb / 32;
-  for (int w = threadIdx.x; w < D * ngrp; w += 256) {
-    const int c = w % D, grp = w / D;
-    const float mc = mean[c];
-    float r[32];
-    float am = 0.0f;
+  const int p0 = b * KVB;
+  const int cg = threadIdx.x % BR::CG, q = threadIdx.x / BR::CG;
+  for (int i = threadIdx.x; i < NG * D; i += 256) (&sAm[0][0])[i] = 0u;
+  if (threadIdx.x < D) sMean[threadIdx.x] = v_mean[(static_cast<size_t>(bh) * nblk + b) * D + threadIdx.x];
+  BR rows;
+  rows.load(V + static_cast<size_t>(bh) * N * D, perm + static_cast<size_t>(bh) * N, p0, N);
+  __syncthreads();
 #pragma unroll
-    for (int e = 0; e < 32; ++e) {
-      const int pos = p0 + grp * 32 + e;
-      r[e] = pos < N ? bf16_to_f32(vv[static_cast<size_t>(clamp_tok(pp[pos], N)) * D + c]) - mc : 0.0f;
-      am = fmaxf(am, fabsf(r[e]));
-    }
-    int ex = 0;
-    if (am > 0.0f) {
-      int fe;
-      frexpf(am, &fe);                   // am = f * 2^fe, f in [0.5, 1)
-      ex = min(max(fe - 1 - 2, -127), 127);
-    }
-    const int gpos = p0 + grp * 32;
-    e8m0[(static_cast<size_t>(bh) * (nblk * kvb / 32) + gpos / 32) * D + mx_scale_slot<D>(c)] =
-        static_cast<uint8_t>(ex + 127);
-    uint32_t words[4] = {0u, 0u, 0u, 0u};
+  for (int pass = 0; pass < BR::PASS; ++pass) {
+    const int r4 = pass * BR::RQ + q;
+    if (r4 * 4 < KVB) {
 #pragma unroll
-    for (int e = 0; e < 32; ++e) words[e >> 3] |= e2m1_encode(ldexpf(r[e], -ex)) << (4 * (e & 7));
-    *reinterpret_cast<uint4*>(Vres + ((static_cast<size_t>(bh) * (nblk * kvb / 64) + gpos / 64) * D + c) * 32 +
-                              (gpos & 63) / 2) = make_uint4(words[0], words[1], words[2], words[3]);
+      for (int e = 0; e < 8; ++e) {
+        const int c = cg * 8 + e;
+        float am = 0.0f;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const float x = p0 + r4 * 4 + rr < N ? rows.v[pass][rr][e] - sMean[c] : 0.0f;
+          rows.v[pass][rr][e] = x;
+          am = fmaxf(am, fabsf(x));
+        }
+        atomicMax(&sAm[r4 / 8][c], __float_as_uint(am));
+      }
+    }
   }
-}
-
-// MXFP8 residuals: per 32 sorted positions x channel, the E8M0 exponent e is
-// the smallest integer with amax <= 448 * 2^e (clamped to [-127, 127], 0 for
-// an all-zero group), so no element saturates; E4M3 codes of r / 2^e, round to
-// nearest even; layout as the E4M3 residuals, [Np/64][d][64 bytes].
-template <int D>
-__global__ __launch_bounds__(256) void k_vres_mxfp8(const uint16_t* __restrict__ V,
-                                                    const int32_t* __restrict__ perm,
-                                                    const float* __restrict__ v_mean, int N,
-                                                    int kvb, int nblk, uint8_t* __restrict__ Vres,
-                                                    uint8_t* __restrict__ e8m0) {
-  const int bh = blockIdx.y, b = blockIdx.x;
-  const int p0 = b * kvb;
-  const int32_t* pp = perm + static_cast<size_t>(bh) * N;
-  const uint16_t* vv = V + static_cast<size_t>(bh) * N * D;
-  const float* mean = v_mean + (static_cast<size_t>(bh) * nblk + b) * D;
-  const int ngrp = kvb / 32;
-  for (int w = threadIdx.x; w < D * ngrp; w += 256) {
-    const int c = w % D, grp = w / D;
-    const float mc = mean[c];
-    float r[32];
-    float am = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 32; ++e) {
-      const int pos = p0 + grp * 32 + e;
-      r[e] = pos < N ? bf16_to_f32(vv[static_cast<size_t>(clamp_tok(pp[pos], N)) * D + c]) - mc : 0.0f;
-      am = fmaxf(am, fabsf(r[e]));
-    }
+  __syncthreads();
+  for (int i = threadIdx.x; i < NG * D; i += 256) {
+    const int grp = i / D, c = i % D;
+    const float am = __uint_as_float(sAm[grp][c]);
     int ex = 0;
     if (am > 0.0f) {
       int fe;
       frexpf(am, &fe);                   // am = f * 2^fe, f in [0.5, 1)
-      ex = fe - 1 - 8;
-      if (am > ldexpf(448.0f, ex)) ++ex;
+      if constexpr (FMT == 1) {
+        ex = fe - 1 - 2;
+      } else {
+        ex = fe - 1 - 8;
+        if (am > ldexpf(448.0f, ex)) ++ex;
+      }
       ex = min(max(ex, -127), 127);
     }
-    const int gpos = p0 + grp * 32;
-    e8m0[(static_cast<size_t>(bh) * (nblk * kvb / 32) + gpos / 32) * D + mx_scale_slot<D>(c)] =
+    sE[grp][c] = ex;
+    e8m0[(static_cast<size_t>(bh) * (nblk * KVB / 32) + p0 / 32 + grp) * D + mx_scale_slot<D>(c)] =
         static_cast<uint8_t>(ex + 127);
-    // |r / 2^e| <= 448 unless the exponent clamp binds; the clamp keeps the
-    // hardware convert (which does not saturate) finite then
-    uint32_t words[8];
+  }
+  __syncthreads();
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      float x[4];
+  for (int pass = 0; pass < BR::PASS; ++pass) {
+    const int r4 = pass * BR::RQ + q;
+    if (r4 * 4 < KVB) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) x[e] = fminf(fmaxf(ldexpf(r[4 * q + e], -ex), -448.0f), 448.0f);
-      words[q] = e4m3x4(x[0], x[1], x[2], x[3]);
+      for (int e = 0; e < 8; ++e) {
+        const int c = cg * 8 + e;
+        const int ex = sE[r4 / 8][c];
+        float x[4];
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) x[rr] = ldexpf(rows.v[pass][rr][e], -ex);
+        if constexpr (FMT == 1) {
+          sT[c][r4] = e2m1_encode(x[0]) | (e2m1_encode(x[1]) << 4) | (e2m1_encode(x[2]) << 8) |
+                      (e2m1_encode(x[3]) << 12);
+        } else {
+          // |x| <= 448 unless the exponent clamp binds; the clamp keeps the
+          // hardware convert (which does not saturate) finite then
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) x[rr] = fminf(fmaxf(x[rr], -448.0f), 448.0f);
+          sT[c][r4] = e4m3x4(x[0], x[1], x[2], x[3]);
+        }
+      }
     }
-    uint8_t* dst = Vres + ((static_cast<size_t>(bh) * (nblk * kvb / 64) + gpos / 64) * D + c) * 64 + (gpos & 63);
-    reinterpret_cast<uint4*>(dst)[0] = make_uint4(words[0], words[1], words[2], words[3]);
-    reinterpret_cast<uint4*>(dst)[1] = make_uint4(words[4], words[5], words[6], words[7]);
+  }
+  __syncthreads();
+  if constexpr (FMT == 1) {
+    // [Np/64][D][32 bytes]: 16 quads of 2 bytes per channel row
+    uint8_t* out = Vres + (static_cast<size_t>(bh) * nblk * KVB + p0) * D / 2;
+    for (int i = threadIdx.x; i < (KVB / 64) * D * 2; i += 256) {   // 16-byte pieces
+      const int step = i / (D * 2), rem = i % (D * 2), c = rem / 2, part = rem % 2;
+      const uint32_t* src = &sT[c][step * 16 + part * 8];
+      uint32_t w[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) w[k] = (src[2 * k] & 0xffffu) | (src[2 * k + 1] << 16);
+      *reinterpret_cast<uint4*>(out + (static_cast<size_t>(step) * D + c) * 32 + part * 16) =
+          make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  } else {
+    // as the E4M3 residuals: per 64-position step, D rows of 64 bytes
+    uint32_t* out = reinterpret_cast<uint32_t*>(Vres + (static_cast<size_t>(bh) * nblk * KVB + p0) * D);
+    for (int i = threadIdx.x; i < (KVB / 64) * D * 4; i += 256) {
+      const int step = i / (D * 4), rem = i % (D * 4), c = rem / 4, part = rem % 4;
+      const uint32_t* src = &sT[c][step * 16 + part * 4];
+      *reinterpret_cast<uint4*>(out + (static_cast<size_t>(step) * D + c) * 16 + part * 4) =
+          make_uint4(src[0], src[1], src[2], src[3]);
+    }
   }
 }
 
@@ -934,10 +954,10 @@ static hipError_t vres_t(const PrepArgs& a, const int32_t* perm, const PrepOut& 
     hipLaunchKernelGGL((k_vres_e4m3<D, KVB>), dim3(a.nblk, BH), dim3(256), 0, st, a.V, perm, o.v_mean, a.vramax,
                        a.N, a.nblk, o.Vres, reinterpret_cast<float*>(o.v_scale));
   else if (a.v_format == 1)
-    hipLaunchKernelGGL(k_vres_mxfp4<D>, dim3(a.nblk, BH), dim3(256), 0, st, a.V, perm, o.v_mean, a.N, a.kvb,
+    hipLaunchKernelGGL((k_vres_mx<D, KVB, 1>), dim3(a.nblk, BH), dim3(256), 0, st, a.V, perm, o.v_mean, a.N,
                        a.nblk, o.Vres, reinterpret_cast<uint8_t*>(o.v_scale));
   else
-    hipLaunchKernelGGL(k_vres_mxfp8<D>, dim3(a.nblk, BH), dim3(256), 0, st, a.V, perm, o.v_mean, a.N, a.kvb,
+    hipLaunchKernelGGL((k_vres_mx<D, KVB, 2>), dim3(a.nblk, BH), dim3(256), 0, st, a.V, perm, o.v_mean, a.N,
                        a.nblk, o.Vres, reinterpret_cast<uint8_t*>(o.v_scale));
   hipLaunchKernelGGL((k_ksmooth<D, KVB>), dim3(a.nblk, BH), dim3(256), 0, st, a.K, perm, a.mu, a.N, a.nblk, o.Kq,
                      o.k_scale);
