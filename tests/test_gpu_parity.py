@@ -232,6 +232,8 @@ def oracle_rows(w, host, b, h, prep_o, tiles, beta=DEFAULT_BETA, mode="expcast")
     ("mid", 2, None, True, "e4m3", None, None, "exp2"),
     ("tiny", 2, None, True, "mxfp8", None, None, "expcast"),     # per-(32 tokens, channel) E8M0 scales
     ("tiny", 1, 1000, True, "mxfp8", 128, 128, "expcast"),
+    ("tiny", 1, 77, True, "mxfp8", 64, None, "expcast"),        # partial scale groups
+    ("tiny", 1, 1, True, "mxfp8", 64, None, "expcast"),         # a single token
     ("mid", 1, 5000, True, "mxfp8", None, None, "exp2"),
 ])
 def test_attention_parity(name, H, N, vsmooth, fmt, kvb, d, mode):
@@ -371,6 +373,7 @@ def test_perm_reuse_clamps_entries_outside_the_head():
 # ------------------------------------------------------------------ cluster order (blocking variant)
 @pytest.mark.parametrize("name,H,N,fmt", [
     ("tiny", 2, None, "e4m3"), ("tiny", 1, 700, "mxfp4"), ("mid", 1, 3000, "e4m3"), ("tiny", 1, 16, "e4m3"),
+    ("tiny", 1, 1, "e4m3"), ("tiny", 1, 900, "mxfp8"),
 ])
 def test_cluster_order_prepare_bit_exact(name, H, N, fmt):
     # renumbered clusters before the final pass: labels, perm, blocks, codes
