@@ -37,6 +37,10 @@ vc_status validate(const vc_config* c, bool need_kmeans, Dims* out) {
   if (c->N > (1 << 26)) return fail(VC_ERR_UNSUPPORTED, "N must be <= 2^26");
   if (c->d != 64 && c->d != 128) return fail(VC_ERR_UNSUPPORTED, "d must be 64 or 128");
   if (c->kv_block != 64 && c->kv_block != 128) return fail(VC_ERR_UNSUPPORTED, "kv_block must be 64 or 128");
+  // the attention kernel addresses one head's blocked keys and residuals
+  // through buffer descriptors: 32-bit sizes and offsets
+  if ((static_cast<int64_t>(c->N) + c->kv_block - 1) / c->kv_block * c->kv_block * c->d > INT32_MAX)
+    return fail(VC_ERR_UNSUPPORTED, "N * d must stay below 2^31 (one head's blocked keys)");
   if (c->vsmooth != 0 && c->vsmooth != 1) return fail(VC_ERR_INVALID_ARG, "vsmooth must be 0 or 1");
   if (c->v_format < 0 || c->v_format > 2)
     return fail(VC_ERR_UNSUPPORTED, "v_format must be 0 (E4M3), 1 (MXFP4) or 2 (MXFP8)");

@@ -72,7 +72,7 @@ typedef enum {
 } vc_status;
 
 typedef struct {
-  int32_t B, H, N, d;       /* N >= 1; d in {64, 128}                              */
+  int32_t B, H, N, d;       /* N >= 1 with N * d < 2^31; d in {64, 128}            */
   int32_t kv_block;         /* 64 or 128 tokens per hardware block                 */
   int32_t n_clusters;       /* k-means clusters k, 1 <= k <= min(N, 4096)          */
   int32_t iters;            /* k-means assignment passes I, 1..16                  */

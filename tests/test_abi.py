@@ -68,6 +68,7 @@ def cfg(**kw):
     (dict(v_format=3), VC_ERR_UNSUPPORTED),
     (dict(p_mode=2), VC_ERR_UNSUPPORTED),
     (dict(cluster_order=2), VC_ERR_UNSUPPORTED),
+    (dict(N=(1 << 24), d=128, n_clusters=16), VC_ERR_UNSUPPORTED),     # 2^31 bytes of blocked keys per head
 ])
 def test_invalid_config_rejected_before_launch(lib, kw, status):
     c = cfg(**kw)
