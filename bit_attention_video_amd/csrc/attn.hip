@@ -13,8 +13,9 @@
 //               fused multiply-add writes the E4M3 probability byte; the
 //               byte convert rounds to nearest even and clamps at 0)
 //       rowsum = sum of the decoded bytes (exact in fp32)
-//       acc = alpha*acc + Vres^T . P^T (FP8 MFMA; MXFP4 residuals use the
-//             scaled f8f6f4 MFMA with E8M0 block scales) + rowsum * mean_b/s_v
+//       acc = alpha*acc + Vres^T . P^T (FP8 MFMA; MXFP4 and MXFP8 residuals
+//             use the scaled f8f6f4 MFMA with E8M0 scales per 32 keys and
+//             channel) + rowsum * mean_b/s_v
 //       l   = alpha*l + rowsum
 //   * O = s_v * acc / l.
 // Operand layouts (measured on gfx950 with a one-wave probe):
@@ -22,7 +23,9 @@
 //     column l%32;
 //   * fp8 A and B operands: byte s of lane group g (g = l/32) holds contraction
 //     index 16g + s for s < 16 and 32 + 16g + (s-16) for s >= 16 (A and B agree);
-//   * FP4 A operand: nibble s of lane group g holds contraction index 32g + s.
+//   * FP4 A operand: nibble s of lane group g holds contraction index 32g + s;
+//   * E8M0 scales of the scaled MFMA: lane group b's scale covers contraction
+//     block [32b, 32b+32), for FP8 and FP4 A operands alike.
 // A 64-key step therefore uses sorted position kappa as the contraction index:
 // Kq rows are stored so that S^T tile t, register r, lane group g holds
 // kappa = 32t + 16g + r, which is exactly where the P^T B operand wants the byte
@@ -132,7 +135,7 @@ struct LaneOffsets {
   static constexpr int KR = (T::KBYTES + RB - 1) / RB;    // direct-load rounds for K
   static constexpr int VR = (T::VBYTES + RB - 1) / RB;    // ... and for the residuals
   int k_rd[T::NDC][2];   // K operand: 16-byte halves of the 32-byte chunk (c, h)
-  int v_rd[2];           // residual operand chunks (E4M3: g and 2+g; MXFP4: g)
+  int v_rd[2];           // residual operand chunks (E4M3, MXFP8: g and 2+g; MXFP4: g)
   int k_src, v_src;      // source offsets of this lane's direct loads (round 0)
   __device__ __forceinline__ LaneOffsets(int lane) {
     const int g = lane >> 5, col = lane & 31;
@@ -501,7 +504,7 @@ __device__ __forceinline__ void block_step(
 // 128-row tiles with a query scale each), so every staged K/V block serves
 // 256 queries.  Block b+1's S^T MFMAs run inside block b's step, so each block
 // starts with its scores ready: K is staged two blocks ahead and V one block
-// ahead, each in a two-slot LDS ring filled by direct global->LDS loads.
+// ahead, each in a two-slot LDS ring filled by direct buffer->LDS loads.
 template <int D, int KVB, int VF, int O32, int PM>
 __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_fwd(AttnArgs p) {
   using TT = AttnTile<D, KVB, VF>;

@@ -1,6 +1,8 @@
 // V-Smooth preparation kernels for gfx950: statistics, int8 k-means on the
-// matrix cores, stable counting sort into fixed blocks, block means with
-// per-channel E4M3 (or MXFP4) residuals, and K smoothing with per-block E4M3.
+// matrix cores (optionally with the clusters renumbered along their principal
+// axis), stable counting sort into fixed blocks, block means with per-channel
+// E4M3 residuals (or MXFP4 / MXFP8 with E8M0 scales per 32 sorted tokens and
+// channel), and K smoothing with per-block E4M3.
 //
 // Method: chooseai.io brief on VC-Attention, section "V-Smooth" (cluster
 // similar value tokens into one hardware block, subtract the block mean kept
