@@ -608,13 +608,17 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_fwd(AttnArgs p) {
     const float* tr = sRed + (wave & ~3);      // the four waves of this wave's 128-row scale tile
     const float amax = fmaxf(fmaxf(tr[0], tr[1]), fmaxf(tr[2], tr[3]));
     const float sq = amax > 0.0f ? amax / 448.0f : 1.0f;
+    const float yq = 1.0f / sq;
+    // codes of fp32(q / s_q) (correctly rounded quotient, see div_rn), round to
+    // nearest even by the packed convert; |q / s_q| <= 448 (up to one rounding
+    // of s_q, well below 464 where the non-saturating convert would overflow)
 #pragma unroll
     for (int c = 0; c < NDC; ++c)
 #pragma unroll
       for (int w = 0; w < 8; ++w) {
-        uint32_t word = 0u;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) word |= e4m3_encode(qv[c][4 * w + e] / sq) << (8 * e);
+        const float* x = &qv[c][4 * w];
+        const uint32_t word = e4m3x4(div_rn(x[0], sq, yq), div_rn(x[1], sq, yq), div_rn(x[2], sq, yq),
+                                     div_rn(x[3], sq, yq));
         qb[c][w] = static_cast<int>(word);
       }
     const float t = sq * p.scale;
@@ -741,8 +745,10 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_fwd(AttnArgs p) {
         if constexpr (O32) {
           *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.O) + off) = make_float4(o0, o1, o2, o3);
         } else {
-          const uint32_t w0 = f32_to_bf16_rne(o0) | (static_cast<uint32_t>(f32_to_bf16_rne(o1)) << 16);
-          const uint32_t w1 = f32_to_bf16_rne(o2) | (static_cast<uint32_t>(f32_to_bf16_rne(o3)) << 16);
+          // bf16 round to nearest even (v_cvt_pk_bf16_f32)
+          typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+          const uint32_t w0 = __builtin_bit_cast(uint32_t, v2bf{static_cast<__bf16>(o0), static_cast<__bf16>(o1)});
+          const uint32_t w1 = __builtin_bit_cast(uint32_t, v2bf{static_cast<__bf16>(o2), static_cast<__bf16>(o3)});
           *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.O) + off) = make_uint2(w0, w1);
         }
       }
