@@ -677,22 +677,19 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_fwd(AttnArgs p) {
       k_next = ks[b + 1];
       if (threadIdx.x < D) mnext = vm[static_cast<size_t>(b + 1) * D + threadIdx.x];
     }
-    // K round r behind matrix instruction 4r, V round r behind 4r+2 (with
-    // ExpCast off, whose exponentials need more registers, all K rounds go
-    // behind instruction 0 and all V rounds behind 4: spreading them further
-    // makes that variant spill inside the loop)
+    // K round r behind matrix instruction 4r, V round r behind 4r+2
     auto hook = [&](auto ic) {
       constexpr int i = decltype(ic)::value;
       static_for<LO::KR>([&](auto rc) {
         constexpr int r = decltype(rc)::value;
-        constexpr int at = PM == 0 ? 4 * r : 0;
+        constexpr int at = 4 * r;
         if constexpr (i == (at < PL::M ? at : PL::M - 1)) {
           if (b + 2 < nblk) stage_k(b + 2, par, rc, std::integral_constant<int, r + 1>{});
         }
       });
       static_for<LO::VR>([&](auto rc) {
         constexpr int r = decltype(rc)::value;
-        constexpr int at = PM == 0 ? 4 * r + 2 : 4;
+        constexpr int at = 4 * r + 2;
         if constexpr (i == (at < PL::M ? at : PL::M - 1)) {
           if (b + 1 < nblk) stage_v(b + 1, Q{}, rc, std::integral_constant<int, r + 1>{});
         }
