@@ -201,12 +201,17 @@ __device__ __forceinline__ void stage_block_v(uint8_t* sv, const uint8_t* vr, ui
   }
 }
 
-// bf16 round-to-nearest-even of a finite value (row sums and block means)
-__device__ __forceinline__ uint32_t bf16_bits(float f) {
-  const uint32_t u = __float_as_uint(f);
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+
+// bf16 hi + lo split of two finite values (row sums, block means): hi rounds
+// each to nearest even on the packed convert, lo rounds what hi leaves over;
+// two packed words, element a in the low half
+__device__ __forceinline__ void bf16_split2(float a, float b, uint32_t& hi, uint32_t& lo) {
+  const v2bf h = v2bf{static_cast<__bf16>(a), static_cast<__bf16>(b)};
+  const v2bf l = v2bf{static_cast<__bf16>(a - static_cast<float>(h[0])), static_cast<__bf16>(b - static_cast<float>(h[1]))};
+  hi = __builtin_bit_cast(uint32_t, h);
+  lo = __builtin_bit_cast(uint32_t, l);
 }
-__device__ __forceinline__ float bf16_val(uint32_t b) { return __uint_as_float(b << 16); }
 
 __device__ __forceinline__ v8i join8(uint4 lo, uint4 hi) {
   return v8i{static_cast<int>(lo.x), static_cast<int>(lo.y), static_cast<int>(lo.z), static_cast<int>(lo.w),
@@ -317,10 +322,10 @@ __device__ __forceinline__ void mean_flush(SoftmaxState<D / 32, AttnTile<D, KVB,
   v4i bhi, blo;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const uint32_t h0 = bf16_bits(st.RS[2 * i]), h1 = bf16_bits(st.RS[2 * i + 1]);
-    const uint32_t l0 = bf16_bits(st.RS[2 * i] - bf16_val(h0)), l1 = bf16_bits(st.RS[2 * i + 1] - bf16_val(h1));
-    bhi[i] = static_cast<int>(h0 | (h1 << 16));
-    blo[i] = static_cast<int>(l0 | (l1 << 16));
+    uint32_t h, l;
+    bf16_split2(st.RS[2 * i], st.RS[2 * i + 1], h, l);
+    bhi[i] = static_cast<int>(h);
+    blo[i] = static_cast<int>(l);
   }
   typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 #pragma unroll
@@ -627,10 +632,10 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_fwd(AttnArgs p) {
 
   // mean of block 0 into the restoration ring (slot 0 of half 0)
   if (threadIdx.x < D) {
-    const float ms = vm[threadIdx.x] * rcol;
-    const uint32_t hi = bf16_bits(ms);
+    uint32_t hi, lo;
+    bf16_split2(vm[threadIdx.x] * rcol, 0.0f, hi, lo);
     sM[(0 * D + threadIdx.x) * MS + 0] = static_cast<uint16_t>(hi);
-    sM[(1 * D + threadIdx.x) * MS + 0] = static_cast<uint16_t>(bf16_bits(ms - bf16_val(hi)));
+    sM[(1 * D + threadIdx.x) * MS + 0] = static_cast<uint16_t>(lo);
   }
 
   SoftmaxState<NDT, MS> st;
@@ -703,11 +708,11 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_fwd(AttnArgs p) {
       mean_flush<D, KVB, VF>(st, sM + ((b >> 3) & 1) * 2 * D * MS, g, col);
     if (b + 1 < nblk && threadIdx.x < D) {
       const int nb = b + 1;
-      const float ms = mnext * sRcol[threadIdx.x];
-      const uint32_t hi = bf16_bits(ms);
+      uint32_t hi, lo;
+      bf16_split2(mnext * sRcol[threadIdx.x], 0.0f, hi, lo);
       uint16_t* mh = sM + ((nb >> 3) & 1) * 2 * D * MS;
       mh[(0 * D + threadIdx.x) * MS + (nb & (MS - 1))] = static_cast<uint16_t>(hi);
-      mh[(1 * D + threadIdx.x) * MS + (nb & (MS - 1))] = static_cast<uint16_t>(bf16_bits(ms - bf16_val(hi)));
+      mh[(1 * D + threadIdx.x) * MS + (nb & (MS - 1))] = static_cast<uint16_t>(lo);
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -743,7 +748,6 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_fwd(AttnArgs p) {
           *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.O) + off) = make_float4(o0, o1, o2, o3);
         } else {
           // bf16 round to nearest even (v_cvt_pk_bf16_f32)
-          typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
           const uint32_t w0 = __builtin_bit_cast(uint32_t, v2bf{static_cast<__bf16>(o0), static_cast<__bf16>(o1)});
           const uint32_t w1 = __builtin_bit_cast(uint32_t, v2bf{static_cast<__bf16>(o2), static_cast<__bf16>(o3)});
           *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.O) + off) = make_uint2(w0, w1);
