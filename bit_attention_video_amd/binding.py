@@ -104,6 +104,8 @@ def _ptr(t):
 
 
 def _need(t: torch.Tensor, dtype, shape, name: str):
+    if t is None:
+        raise ValueError(f"{name} is required")
     if t.device.type != "cuda":
         raise ValueError(f"{name} must be a device tensor")
     if t.dtype != dtype:
@@ -138,21 +140,42 @@ class Prepared:
     labels: torch.Tensor | None
 
 
-def alloc_prepared(cfg: VcConfig, device="cuda", with_labels: bool = True) -> Prepared:
+def _prepared_layout(cfg: VcConfig) -> dict:
+    """(dtype, shape) of every Prepared field for this configuration."""
     B, H, N, d, kvb = cfg.B, cfg.H, cfg.N, cfg.d, cfg.kv_block
     nblk = _nblk(cfg)
     Np = nblk * kvb
-    u8 = dict(dtype=torch.uint8, device=device)
-    Vres = torch.empty((B, H, Np // 64, d, 32 if cfg.v_format == MXFP4 else 64), **u8)
-    v_scale = (torch.empty((B, H, d), dtype=torch.float32, device=device) if cfg.v_format == E4M3
-               else torch.empty((B, H, Np // 32, d), **u8))
-    return Prepared(
-        Kq=torch.empty((B, H, Np, d), **u8),
-        k_scale=torch.empty((B, H, nblk), dtype=torch.float32, device=device),
-        Vres=Vres, v_scale=v_scale,
-        v_mean=torch.empty((B, H, nblk, d), dtype=torch.float32, device=device),
-        perm=torch.empty((B, H, N), dtype=torch.int32, device=device),
-        labels=torch.empty((B, H, N), dtype=torch.int32, device=device) if with_labels else None)
+    return dict(
+        Kq=(torch.uint8, (B, H, Np, d)),
+        k_scale=(torch.float32, (B, H, nblk)),
+        Vres=(torch.uint8, (B, H, Np // 64, d, 32 if cfg.v_format == MXFP4 else 64)),
+        v_scale=(torch.float32, (B, H, d)) if cfg.v_format == E4M3 else (torch.uint8, (B, H, Np // 32, d)),
+        v_mean=(torch.float32, (B, H, nblk, d)),
+        perm=(torch.int32, (B, H, N)),
+        labels=(torch.int32, (B, H, N)))
+
+
+def alloc_prepared(cfg: VcConfig, device="cuda", with_labels: bool = True) -> Prepared:
+    lay = _prepared_layout(cfg)
+    t = {k: torch.empty(shape, dtype=dt, device=device) for k, (dt, shape) in lay.items()
+         if k != "labels" or with_labels}
+    return Prepared(labels=t.pop("labels", None), **t)
+
+
+def _check_prepared(cfg: VcConfig, prep: Prepared):
+    """The library cannot see buffer sizes: every field must match cfg."""
+    for k, (dt, shape) in _prepared_layout(cfg).items():
+        t = getattr(prep, k)
+        if t is not None or k != "labels":
+            _need(t, dt, shape, f"prep.{k}")
+
+
+def _workspace(ws: torch.Tensor | None, nbytes: int, device) -> torch.Tensor:
+    if ws is not None:
+        _need(ws, torch.uint8, (ws.numel(),), "ws")
+        if ws.numel() >= nbytes:
+            return ws
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
 
 
 def vsmooth_prepare(cfg: VcConfig, K: torch.Tensor, V: torch.Tensor, init_idx: torch.Tensor | None,
@@ -163,10 +186,11 @@ def vsmooth_prepare(cfg: VcConfig, K: torch.Tensor, V: torch.Tensor, init_idx: t
     _need(V, torch.bfloat16, shp, "V")
     if cfg.vsmooth:
         _need(init_idx, torch.int32, (cfg.B, cfg.H, cfg.n_clusters), "init_idx")
-    out = out or alloc_prepared(cfg, K.device, with_labels)
-    nbytes = workspace_bytes(cfg)
-    if ws is None or ws.numel() < nbytes:
-        ws = torch.empty(nbytes, dtype=torch.uint8, device=K.device)
+    if out is None:
+        out = alloc_prepared(cfg, K.device, with_labels)
+    else:
+        _check_prepared(cfg, out)
+    ws = _workspace(ws, workspace_bytes(cfg), K.device)
     _check(lib().vsmooth_prepare(ctypes.byref(cfg), _ptr(K), _ptr(V), _ptr(init_idx) if cfg.vsmooth else None,
                                  _ptr(out.Kq), _ptr(out.k_scale), _ptr(out.Vres), _ptr(out.v_scale),
                                  _ptr(out.v_mean), _ptr(out.perm), _ptr(out.labels), _ptr(ws), ws.numel(),
@@ -193,10 +217,11 @@ def vsmooth_prepare_warm(cfg: VcConfig, K: torch.Tensor, V: torch.Tensor, *,
         _need(perm_in, torch.int32, (cfg.B, cfg.H, cfg.N), "perm_in")
     if centroids_out is not None:
         _need(centroids_out, torch.float32, cshape, "centroids_out")
-    out = out or alloc_prepared(cfg, K.device, with_labels)
-    nbytes = workspace_bytes(cfg)
-    if ws is None or ws.numel() < nbytes:
-        ws = torch.empty(nbytes, dtype=torch.uint8, device=K.device)
+    if out is None:
+        out = alloc_prepared(cfg, K.device, with_labels)
+    else:
+        _check_prepared(cfg, out)
+    ws = _workspace(ws, workspace_bytes(cfg), K.device)
     _check(lib().vsmooth_prepare_warm(ctypes.byref(cfg), _ptr(K), _ptr(V), _ptr(init_idx), _ptr(init_centroids),
                                       _ptr(perm_in), _ptr(centroids_out), _ptr(out.Kq), _ptr(out.k_scale),
                                       _ptr(out.Vres), _ptr(out.v_scale), _ptr(out.v_mean), _ptr(out.perm),
@@ -204,14 +229,25 @@ def vsmooth_prepare_warm(cfg: VcConfig, K: torch.Tensor, V: torch.Tensor, *,
     return out
 
 
+def _out_dtype(cfg: VcConfig):
+    return torch.float32 if cfg.out_fp32 else torch.bfloat16
+
+
 def alloc_out(cfg: VcConfig, device="cuda") -> torch.Tensor:
-    return torch.empty((cfg.B, cfg.H, cfg.N, cfg.d), device=device,
-                       dtype=torch.float32 if cfg.out_fp32 else torch.bfloat16)
+    return torch.empty((cfg.B, cfg.H, cfg.N, cfg.d), device=device, dtype=_out_dtype(cfg))
+
+
+def _output(cfg: VcConfig, out: torch.Tensor | None, device) -> torch.Tensor:
+    if out is None:
+        return alloc_out(cfg, device)
+    _need(out, _out_dtype(cfg), (cfg.B, cfg.H, cfg.N, cfg.d), "out")
+    return out
 
 
 def vc_attn_fwd(cfg: VcConfig, Q: torch.Tensor, prep: Prepared, out: torch.Tensor | None = None) -> torch.Tensor:
     _need(Q, torch.bfloat16, (cfg.B, cfg.H, cfg.N, cfg.d), "Q")
-    out = alloc_out(cfg, Q.device) if out is None else out
+    _check_prepared(cfg, prep)
+    out = _output(cfg, out, Q.device)
     _check(lib().vc_attn_fwd(ctypes.byref(cfg), _ptr(Q), _ptr(prep.Kq), _ptr(prep.k_scale), _ptr(prep.Vres),
                              _ptr(prep.v_scale), _ptr(prep.v_mean), _ptr(out), _stream()), "vc_attn_fwd")
     return out
@@ -223,10 +259,8 @@ def vc_attention(cfg: VcConfig, Q, K, V, init_idx, out=None, ws=None) -> torch.T
         _need(t, torch.bfloat16, shp, n)
     if cfg.vsmooth:
         _need(init_idx, torch.int32, (cfg.B, cfg.H, cfg.n_clusters), "init_idx")
-    out = alloc_out(cfg, Q.device) if out is None else out
-    nbytes = workspace_bytes(cfg, attention=True)
-    if ws is None or ws.numel() < nbytes:
-        ws = torch.empty(nbytes, dtype=torch.uint8, device=Q.device)
+    out = _output(cfg, out, Q.device)
+    ws = _workspace(ws, workspace_bytes(cfg, attention=True), Q.device)
     _check(lib().vc_attention(ctypes.byref(cfg), _ptr(Q), _ptr(K), _ptr(V),
                               _ptr(init_idx) if cfg.vsmooth else None, _ptr(out), _ptr(ws), ws.numel(),
                               _stream()), "vc_attention")

@@ -258,6 +258,50 @@ def test_attention_parity(name, H, N, vsmooth, fmt, kvb, d, mode):
         check_close(Og, Oref, vmax, f"{name} N={N} h{h} vs={vsmooth} {fmt} {mode}")
 
 
+@pytest.mark.parametrize("fmt", ["e4m3", "mxfp4"])
+def test_batch_of_two_and_explicit_parameters(fmt):
+    """B = 2 (every (b, h) pair prepared and attended in one call), with an
+    explicit softmax scale and ExpCast bias instead of the defaults."""
+    import dataclasses
+    w = dataclasses.replace(inputs.WORKLOADS["tiny"], B=2)
+    H, N, scale, beta = 2, 700, 0.07, 0.3
+    host, dev = gen(w, H=H, N=N)
+    cfg = vb.make_config(w.B, H, N, w.d, w.kv_block, min(w.k, N), w.iters, True, fmt_id(fmt), True, scale, beta,
+                         vb.EXPCAST, False)
+    prep = vb.vsmooth_prepare(cfg, dev["K"], dev["V"], dev["init"])
+    g = prep_to_numpy(prep, fmt)
+    O = vb.vc_attn_fwd(cfg, dev["Q"], prep).cpu().numpy()
+    tiles = list(range(oracle.n_q_tiles(N)))
+    for b in range(w.B):
+        for h in range(H):
+            o = oracle_head(w, host, b, h, True, fmt)
+            compare_prep(g, o, b, h, fmt)
+            rows = oracle.attend_rows(oracle.bf16_to_f64(host[0][b, h]), o, tiles, scale, beta)
+            vmax = float(np.max(np.abs(oracle.bf16_to_f64(host[2][b, h]))))
+            check_close(O[b, h], np.concatenate([rows[t] for t in tiles]), vmax, f"b{b} h{h} {fmt}")
+
+
+def test_binding_rejects_mismatched_buffers():
+    """The C ABI cannot see buffer sizes, so the binding checks every caller
+    buffer against the configuration before the call."""
+    w = inputs.WORKLOADS["tiny"]
+    host, dev = gen(w, H=1, N=300)
+    cfg = cfg_for(w, H=1, N=300)
+    prep = vb.vsmooth_prepare(cfg, dev["K"], dev["V"], dev["init"])
+    other = cfg_for(w, H=1, N=200)
+    with pytest.raises(ValueError, match="prep.Kq"):
+        vb.vc_attn_fwd(other, dev["Q"][:, :, :200].contiguous(), prep)
+    with pytest.raises(ValueError, match="out"):
+        vb.vc_attn_fwd(cfg, dev["Q"], prep, out=torch.empty((1, 1, 299, w.d), device="cuda"))
+    with pytest.raises(ValueError, match="out"):
+        vb.vc_attn_fwd(cfg, dev["Q"], prep, out=torch.empty((1, 1, 300, w.d), device="cuda", dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="prep.Vres"):
+        vb.vsmooth_prepare(cfg_for(w, H=1, N=300, fmt="mxfp4"), dev["K"], dev["V"], dev["init"], out=prep)
+    with pytest.raises(ValueError, match="ws"):
+        vb.vsmooth_prepare(cfg, dev["K"], dev["V"], dev["init"], ws=torch.empty(10, device="cuda"))
+    torch.cuda.synchronize()
+
+
 def test_bf16_output_and_determinism():
     w = inputs.WORKLOADS["mid"]
     host, dev = gen(w, H=2)
