@@ -191,3 +191,63 @@ def test_exp2cast_is_closer_to_exact_than_expcast():
     on = np.concatenate([o for _, o in sorted(oracle.attend_rows(Q, prep, range(8), mode="expcast").items())])
     off = np.concatenate([o for _, o in sorted(oracle.attend_rows(Q, prep, range(8), mode="exp2").items())])
     assert oracle.psnr(off, ref) > oracle.psnr(on, ref)
+
+
+def _unit_log2_scale():
+    """An fp32 softmax scale x with fp32(x * fp32(log2 e)) == 1 exactly, so
+    that with s_q = s_k = 1 the log2-domain scores are the raw dot products."""
+    l2e = np.float32(1.4426950408889634)
+    up = down = np.float32(np.log(2.0))
+    for _ in range(64):
+        for x in (up, down):
+            if np.float32(x * l2e) == np.float32(1.0):
+                return float(x)
+        up = np.nextafter(up, np.float32(np.inf))
+        down = np.nextafter(down, np.float32(-np.inf))
+    raise AssertionError("no fp32 scale maps log2 e to 1")
+
+
+@pytest.mark.parametrize("mode,window", [("expcast", 6), ("exp2", 9)])
+def test_integer_log2_scores_give_exact_base2_softmax(mode, window):
+    """Closed form for the whole quantised composition (bytes from the FMA,
+    decode, online rescaling across blocks, row sums, mean restoration, column
+    scale, padded tail).  When every log2-domain score is an integer within
+    `window` of the running maximum, the probability bytes are exactly
+    2^(t - m): ExpCast's 8z + 56 + beta rounds to 8z + 56 for |beta| < 0.5 and
+    z in [-6, 0], which is the E4M3 code of 2^z; the exp2 path is exact down to
+    the smallest subnormal 2^-9.  The output must then equal the base-2 softmax
+    of the scores applied to col_scale * vres + mean, computed here in exact
+    rationals from that definition alone."""
+    rng = np.random.default_rng(7)
+    d, kvb, N = 4, 4, 10                       # three blocks, the last with 2 real keys
+    nblk = (N + kvb - 1) // kvb
+    n = 5
+    # channel 0 carries 448 in one query row (so s_q = 1) and is zero in every key
+    Q = rng.integers(-2, 3, size=(n, d)).astype(np.float64)
+    Q[:, 0] = 0.0
+    Q[0, 0] = 448.0
+    kdec = np.zeros((nblk * kvb, d))
+    kdec[:N, 1:] = rng.integers(-1, 2, size=(N, d - 1))
+    kdec[N:, 1:] = 1.0                           # padded rows score like real keys unless masked
+    S = Q @ kdec[:N].T
+    # every score within `window` of the row maximum (so also of the running
+    # maximum at its block); the running maximum moves after the first block in
+    # some row (rescaling is exercised); unmasked, a padded key would carry
+    # weight in some row
+    assert np.all(S.max(axis=1, keepdims=True) - S <= window)
+    assert np.any(S[:, :kvb].max(axis=1) < S.max(axis=1))
+    assert np.any((Q @ kdec[N:].T).max(axis=1) >= S.max(axis=1) - 6)
+    vres = np.zeros((nblk * kvb, d))
+    vres[:N] = rng.integers(-16, 17, size=(N, d)) / 8.0
+    vres[N:] = 123.0                             # padded rows must not contribute
+    col_scale = np.array([0.5, 1.0, 2.0, 0.25])
+    means = rng.integers(-8, 9, size=(nblk, d)) / 4.0
+    scale = _unit_log2_scale()
+    O = attend_tile(Q, kdec, np.ones(nblk), vres, col_scale, means, N, kvb, scale, beta=-0.25, mode=mode)
+    for i in range(n):
+        w = [Fraction(2) ** int(S[i, j]) for j in range(N)]
+        tot = sum(w)
+        for c in range(d):
+            want = sum(w[j] * (Fraction(col_scale[c]) * Fraction(vres[j, c]) + Fraction(means[j // kvb, c]))
+                       for j in range(N)) / tot
+            assert abs(O[i, c] - float(want)) <= 1e-13 * (1 + abs(float(want))), (mode, i, c, O[i, c], want)
