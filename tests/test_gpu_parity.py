@@ -302,6 +302,41 @@ def test_binding_rejects_mismatched_buffers():
     torch.cuda.synchronize()
 
 
+@pytest.mark.parametrize("mode,d,kvb", [("expcast", 64, 64), ("exp2", 64, 64), ("expcast", 128, 128),
+                                         ("exp2", 128, 128), ("expcast", 128, 64)])
+def test_integer_scores_give_exact_base2_softmax(mode, d, kvb):
+    """Closed form, independent of the oracle: with the inputs of
+    closed_forms.integer_score_qkv the library's own quantisation is exact and
+    every log2-domain score is an integer in [-3, 3], so every probability
+    byte is exactly 2^(t - m) and the fp32 output must be the base-2 softmax
+    of the scores applied to V.  The FP8 matrix instructions sum each group
+    of 8 products aligned to the group's largest, dropping bits about 13
+    places below it; here every nonzero product is within 2^10 of the others,
+    so the sums are exact.  Every block holds keys and their negations, so the
+    running maximum starts at 0 or above and ends at 3 or below: rescaled
+    partial sums are multiples of 2^-4 below 2^18, exact in fp32, and only the
+    final normalisation rounds (twice: 1/l, then the product)."""
+    from closed_forms import integer_score_qkv, base2_softmax, unit_log2_scale
+    N = 300
+    Q, K, V = integer_score_qkv(N, d, kvb)
+    dv = {n: torch.from_numpy(x).to(torch.bfloat16).reshape(1, 1, N, d).cuda() for n, x in
+          (("Q", Q), ("K", K), ("V", V))}
+    cfg = vb.make_config(1, 1, N, d, kvb, 1, 1, False, vb.E4M3, True, unit_log2_scale(), -0.25,
+                         vb.EXPCAST if mode == "expcast" else vb.EXP2_CAST, False)
+    prep = vb.vsmooth_prepare(cfg, dv["K"], dv["V"], None)
+    O = vb.vc_attn_fwd(cfg, dv["Q"], prep)[0, 0].cpu().numpy().astype(np.float64)
+    assert torch.all(prep.k_scale == 1.0) and torch.all(prep.v_scale == 1.0)
+    S = Q @ K.T
+    want = base2_softmax(S, V)
+    err = np.abs(O - want)
+    W = np.exp2(S - S.max(axis=1, keepdims=True))
+    mag = (W @ np.abs(V)) / W.sum(axis=1, keepdims=True)      # sum of |terms| / l
+    rel = err / np.maximum(np.abs(want), 1e-30)
+    log(f"  {mode} d {d} kv_block {kvb}: max rel err {np.max(rel):.2e}, "
+        f"max err / (2^-24 sum|terms|/l) {np.max(err / (2.0 ** -24 * mag)):.3g}")
+    assert np.all(err <= 4.0 * 2.0 ** -24 * np.abs(want) + 1e-30)
+
+
 def test_bf16_output_and_determinism():
     w = inputs.WORKLOADS["mid"]
     host, dev = gen(w, H=2)

@@ -10,6 +10,7 @@ import oracle
 from oracle import formats as F
 from oracle.attention import attend_tile, exact_attention, softmax_scale
 from bit_attention_video_amd import inputs
+from closed_forms import unit_log2_scale
 
 
 def _head(N, d=64, kvb=64, k=16, seed=7):
@@ -193,20 +194,6 @@ def test_exp2cast_is_closer_to_exact_than_expcast():
     assert oracle.psnr(off, ref) > oracle.psnr(on, ref)
 
 
-def _unit_log2_scale():
-    """An fp32 softmax scale x with fp32(x * fp32(log2 e)) == 1 exactly, so
-    that with s_q = s_k = 1 the log2-domain scores are the raw dot products."""
-    l2e = np.float32(1.4426950408889634)
-    up = down = np.float32(np.log(2.0))
-    for _ in range(64):
-        for x in (up, down):
-            if np.float32(x * l2e) == np.float32(1.0):
-                return float(x)
-        up = np.nextafter(up, np.float32(np.inf))
-        down = np.nextafter(down, np.float32(-np.inf))
-    raise AssertionError("no fp32 scale maps log2 e to 1")
-
-
 @pytest.mark.parametrize("mode,window", [("expcast", 6), ("exp2", 9)])
 def test_integer_log2_scores_give_exact_base2_softmax(mode, window):
     """Closed form for the whole quantised composition (bytes from the FMA,
@@ -242,7 +229,7 @@ def test_integer_log2_scores_give_exact_base2_softmax(mode, window):
     vres[N:] = 123.0                             # padded rows must not contribute
     col_scale = np.array([0.5, 1.0, 2.0, 0.25])
     means = rng.integers(-8, 9, size=(nblk, d)) / 4.0
-    scale = _unit_log2_scale()
+    scale = unit_log2_scale()
     O = attend_tile(Q, kdec, np.ones(nblk), vres, col_scale, means, N, kvb, scale, beta=-0.25, mode=mode)
     for i in range(n):
         w = [Fraction(2) ** int(S[i, j]) for j in range(N)]
@@ -251,3 +238,23 @@ def test_integer_log2_scores_give_exact_base2_softmax(mode, window):
             want = sum(w[j] * (Fraction(col_scale[c]) * Fraction(vres[j, c]) + Fraction(means[j // kvb, c]))
                        for j in range(N)) / tot
             assert abs(O[i, c] - float(want)) <= 1e-13 * (1 + abs(float(want))), (mode, i, c, O[i, c], want)
+
+
+@pytest.mark.parametrize("mode", ["expcast", "exp2"])
+def test_integer_score_inputs_through_the_whole_oracle(mode):
+    """The inputs of closed_forms.integer_score_qkv through the oracle's own
+    preparation (V-Smooth off: identity order, K smoothing, per-block s_k,
+    per-channel s_v) and attention reproduce the base-2 softmax of the integer
+    scores; the same inputs pin the GPU path."""
+    from closed_forms import integer_score_qkv, base2_softmax
+    N, d, kvb = 300, 64, 64
+    Q, K, V = integer_score_qkv(N, d, kvb)
+    prep = oracle.prepare_head(K, V, None, 1, 1, kvb, "e4m3", False)
+    assert np.all(prep["k"]["k_scale"] == 1.0) and np.all(prep["v"]["col_scale"] == 1.0)
+    S = Q @ K.T
+    assert np.all(np.abs(S) <= 3) and np.all(S == np.rint(S))
+    tiles = list(range(oracle.n_q_tiles(N)))
+    rows = oracle.attend_rows(Q, prep, tiles, unit_log2_scale(), -0.25, mode=mode)
+    O = np.concatenate([rows[t] for t in tiles])
+    want = base2_softmax(S, V)
+    assert np.max(np.abs(O - want)) <= 1e-12 * np.max(np.abs(want))
