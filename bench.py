@@ -122,8 +122,8 @@ def main():
                     help="also run one plain device copy of this size (HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}); "
-              "heads shard across GPUs with no communication, see the design notes", file=sys.stderr)
+        print(f"bench.py measures one GPU (asked for --gpus {args.gpus}): the library has no multi-GPU path; "
+              "its heads shard across GPUs with no communication", file=sys.stderr)
         sys.exit(2)
 
     import torch
