@@ -237,12 +237,14 @@ def main():
     t_x = float(np.mean(x_ms)) * 1e-3
     log(f"expcast off: attention {t_x * 1e3:.2f} ms")
 
-    # MX residual formats on the same inputs (E8M0 scales per 32 sorted tokens
-    # and channel; elements E2M1 for MXFP4, E4M3 for MXFP8): preparation and
-    # attention time, and below the PSNR with V-Smooth on and off
+    # block-scaled residual formats on the same inputs (MX: E8M0 scales per 32
+    # sorted tokens and channel, elements E2M1 for MXFP4, E4M3 for MXFP8;
+    # NVFP4 style: E4M3 scales per 16 sorted tokens and channel, E2M1
+    # elements, multiplied as two E4M3 parts): preparation and attention time,
+    # and below the PSNR with V-Smooth on and off
     mx, mx_out = {}, {}
     if fmt == vb.E4M3:
-        for name, f in (("mxfp4", vb.MXFP4), ("mxfp8", vb.MXFP8)):
+        for name, f in (("mxfp4", vb.MXFP4), ("mxfp8", vb.MXFP8), ("nvfp4", vb.NVFP4)):
             cfg_m = vb.make_config(w.B, w.H, w.N, w.d, w.kv_block, w.k, w.iters, True, f, False)
             prep_m = vb.alloc_prepared(cfg_m, "cuda", with_labels=False)
             ws_m = torch.empty(vb.workspace_bytes(cfg_m), dtype=torch.uint8, device="cuda")
@@ -331,7 +333,7 @@ def main():
         "expcast_off": {"t_attn_ms": round(t_x * 1e3, 3), "attn_tflops": round(flops / t_x / 1e12, 2),
                         "expcast_speedup": round(t_x / t_fwd, 3)},
         "pct_mfma_loop_attn": round(100 * achieved / loop_tflops, 2),
-        "mx_residuals": mx or None,
+        "residual_formats": mx or None,
         "cluster_order": ordered,
         "roofline": {"bound": "mfma", "kernel": "k_attn_fwd", "achieved": round(achieved, 2),
                      "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4),

@@ -21,7 +21,7 @@ LIB_PATH = os.environ.get("VCATTN_LIBRARY") or os.path.join(_HERE, "libvcattn.so
 # 8z + 56 + beta on the exact E4M3 code of 2^z over fractional z.
 DEFAULT_BETA = 8.0 / math.log(2.0) - 12.0
 
-E4M3, MXFP4, MXFP8 = 0, 1, 2    # residual formats
+E4M3, MXFP4, MXFP8, NVFP4 = 0, 1, 2, 3    # residual formats (NVFP4: 16-token E4M3 scales, emulated)
 EXPCAST, EXP2_CAST = 0, 1      # p_mode: ExpCast-FP8 bytes, or exp2 then E4M3 cast
 
 
@@ -148,7 +148,8 @@ def _prepared_layout(cfg: VcConfig) -> dict:
     return dict(
         Kq=(torch.uint8, (B, H, Np, d)),
         k_scale=(torch.float32, (B, H, nblk)),
-        Vres=(torch.uint8, (B, H, Np // 64, d, 32 if cfg.v_format == MXFP4 else 64)),
+        Vres=(torch.uint8, (B, H, nblk, 2, kvb // 64, d, 64) if cfg.v_format == NVFP4 else
+              (B, H, Np // 64, d, 32 if cfg.v_format == MXFP4 else 64)),
         v_scale=(torch.float32, (B, H, d)) if cfg.v_format == E4M3 else (torch.uint8, (B, H, Np // 32, d)),
         v_mean=(torch.float32, (B, H, nblk, d)),
         perm=(torch.int32, (B, H, N)),

@@ -42,8 +42,8 @@ vc_status validate(const vc_config* c, bool need_kmeans, Dims* out) {
   if ((static_cast<int64_t>(c->N) + c->kv_block - 1) / c->kv_block * c->kv_block * c->d > INT32_MAX)
     return fail(VC_ERR_UNSUPPORTED, "N * d must stay below 2^31 (one head's blocked keys)");
   if (c->vsmooth != 0 && c->vsmooth != 1) return fail(VC_ERR_INVALID_ARG, "vsmooth must be 0 or 1");
-  if (c->v_format < 0 || c->v_format > 2)
-    return fail(VC_ERR_UNSUPPORTED, "v_format must be 0 (E4M3), 1 (MXFP4) or 2 (MXFP8)");
+  if (c->v_format < 0 || c->v_format > 3)
+    return fail(VC_ERR_UNSUPPORTED, "v_format must be 0 (E4M3), 1 (MXFP4), 2 (MXFP8) or 3 (NVFP4 style)");
   if (c->out_fp32 != 0 && c->out_fp32 != 1) return fail(VC_ERR_INVALID_ARG, "out_fp32 must be 0 or 1");
   if (!(std::isfinite(c->softmax_scale) && c->softmax_scale >= 0.0f))
     return fail(VC_ERR_INVALID_ARG, "softmax_scale must be finite and >= 0");
@@ -112,7 +112,7 @@ OutSizes out_sizes(const Dims& D, int v_format) {
   OutSizes s;
   s.kq = D.BH * Np * D.d;
   s.ks = D.BH * D.nblk;
-  s.vres = D.BH * Np * D.d / (v_format == 1 ? 2 : 1);
+  s.vres = D.BH * Np * D.d * (v_format == 3 ? 2 : 1) / (v_format == 1 ? 2 : 1);
   s.vsc_bytes = v_format == 0 ? D.BH * D.d * sizeof(float) : D.BH * (Np / 32) * D.d;
   s.vmean = D.BH * D.nblk * D.d;
   s.perm = D.BH * D.N;

@@ -15,7 +15,9 @@
 //       rowsum = sum of the decoded bytes (exact in fp32)
 //       acc = alpha*acc + Vres^T . P^T (FP8 MFMA; MXFP4 and MXFP8 residuals
 //             use the scaled f8f6f4 MFMA with E8M0 scales per 32 keys and
-//             channel) + rowsum * mean_b/s_v
+//             channel; NVFP4-style residuals, whose E4M3 scales per 16 keys
+//             vary along the contraction, arrive as two E4M3 parts under one
+//             E8M0 scale and take two MFMAs) + rowsum * mean_b/s_v
 //       l   = alpha*l + rowsum
 //   * O = s_v * acc / l.
 // Operand layouts (measured on gfx950 with a one-wave probe):
@@ -114,7 +116,8 @@ struct AttnTile {
   static constexpr int NDT = D / 32;      // 32-channel tiles of O^T
   static constexpr int VROW = VF == 1 ? 32 : 64;   // residual bytes per channel row of a 64-key step
   static constexpr int KBYTES = KVB * D;
-  static constexpr int VBYTES = NKS * D * VROW;
+  static constexpr int VHALF = NKS * D * VROW;                 // one code set of a block
+  static constexpr int VBYTES = VF == 3 ? 2 * VHALF : VHALF;   // NVFP4 emulation: high, then low parts
   static constexpr int SBYTES = VF != 0 ? (KVB / 32) * D : 0;    // E8M0 scales (MX formats)
   static constexpr int STAGE = KBYTES + VBYTES + (SBYTES + 1023) / 1024 * 1024;
   static constexpr int MSLOT = 8;         // blocks per mean-restoration flush
@@ -287,7 +290,8 @@ template <int D, int KVB, int VF>
 struct StepPlan {
   using TT = AttnTile<D, KVB, VF>;
   static constexpr int NDC = TT::NDC, NKT = TT::NKT, NKS = TT::NKS, NDT = TT::NDT;
-  static constexpr int PER_S = 2 * NDC + 1 + NDT;
+  static constexpr int NPV = VF == 3 ? 2 * NDT : NDT;   // P.V MFMAs per 64 keys (NVFP4 emulation: high, low)
+  static constexpr int PER_S = 2 * NDC + 1 + NPV;
   static constexpr int M = NKS * PER_S;          // MFMAs per step
   static constexpr int NW = (NKT - 1) * 4;       // ExpCast words behind the MFMAs
   static constexpr int RATE = NDC == 1 ? 2 : 1;
@@ -297,7 +301,9 @@ struct StepPlan {
   static constexpr int step_of(int i) { return i / PER_S; }
   static constexpr int qk_kt(int i) { return 2 * step_of(i) + (i % PER_S) / NDC; }
   static constexpr int qk_c(int i) { return (i % PER_S) % NDC; }
-  static constexpr int pv_T(int i) { return i % PER_S - 2 * NDC - 1; }
+  static constexpr int pv_u(int i) { return i % PER_S - 2 * NDC - 1; }
+  static constexpr int pv_T(int i) { return VF == 3 ? pv_u(i) / 2 : pv_u(i); }   // channel tile
+  static constexpr int pv_half(int i) { return VF == 3 ? pv_u(i) % 2 : 0; }    // 1: low parts
   static constexpr int qk_slot(int kt) { return (kt / 2) * PER_S + (kt % 2) * NDC; }
   static constexpr int wbeg(int i) {
     const int w = i < NDC ? i * (4 / NDC) : 4 + (i - NDC) * RATE;
@@ -403,9 +409,9 @@ __device__ __forceinline__ void block_step(
   v8i P[NKS];
   v4f rsum;
   // operand ring: loads run RD-1 matrix instructions ahead (two for most
-  // formats; one for MXFP8, whose per-lane scales would otherwise push the
-  // step past the register file)
-  constexpr int RD = VF == 2 ? 2 : 3;
+  // formats; one for MXFP8 and the NVFP4 emulation, whose per-lane scales
+  // would otherwise push the step past the register file)
+  constexpr int RD = VF >= 2 ? 2 : 3;
   v8i opnd[RD];
   // MX formats: the E8M0 scales of this lane for the NDT channel tiles of a
   // 64-key step, one byte each (stored adjacent), op_sel picks the tile's
@@ -420,8 +426,8 @@ __device__ __forceinline__ void block_step(
         opnd[j % RD] = join8(*reinterpret_cast<const uint4*>(sKn + kt * 32 * D + lo.k_rd[c][0]),
                             *reinterpret_cast<const uint4*>(sKn + kt * 32 * D + lo.k_rd[c][1]));
       } else if constexpr (PL::kind(j) == 2) {
-        constexpr int sj = PL::step_of(j), T = PL::pv_T(j);
-        const uint8_t* vb = sV + (sj * D + 32 * T) * VROW;
+        constexpr int sj = PL::step_of(j), T = PL::pv_T(j), hl = PL::pv_half(j);
+        const uint8_t* vb = sV + hl * TT::VHALF + (sj * D + 32 * T) * VROW;
         if constexpr (VF != 1) {
           opnd[j % RD] = join8(*reinterpret_cast<const uint4*>(vb + lo.v_rd[0]),
                               *reinterpret_cast<const uint4*>(vb + lo.v_rd[1]));
@@ -432,7 +438,7 @@ __device__ __forceinline__ void block_step(
         }
         // lane group g's scale covers contraction block g, i.e. sorted
         // positions [32g, 32g+32) of the step (measured for both MX formats)
-        if constexpr (VF != 0 && T == 0) {
+        if constexpr (VF != 0 && PL::pv_u(j) == 0) {
           const uint8_t* sc = sS + (2 * sj + g) * D + col * NDT;
           if constexpr (NDT == 4) osc[sj] = *reinterpret_cast<const int*>(sc);
           else osc[sj] = *reinterpret_cast<const uint16_t*>(sc);
@@ -474,6 +480,9 @@ __device__ __forceinline__ void block_step(
         st.acc[T] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(opnd[i % RD], P[sj], st.acc[T], 0, 0, 0, 0, 0,
                                                                    0);
       else if constexpr (VF == 2)
+        st.acc[T] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(opnd[i % RD], P[sj], st.acc[T], 0, 0, T,
+                                                                   osc[sj], 0, 127);
+      else if constexpr (VF == 3)   // residual = (high + low) * 2^scale: one slot each
         st.acc[T] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(opnd[i % RD], P[sj], st.acc[T], 0, 0, T,
                                                                    osc[sj], 0, 127);
       else
@@ -538,7 +547,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_fwd(AttnArgs p) {
   const int qrow = qt * TT::ROWS + wave * 32 + col;
 
   const uint8_t* kq = p.Kq + static_cast<size_t>(bh) * nblk * KVB * D;
-  const uint8_t* vr = p.Vres + static_cast<size_t>(bh) * nblk * NKS * D * VROW;
+  const uint8_t* vr = p.Vres + static_cast<size_t>(bh) * nblk * TT::VBYTES;
   const uint8_t* scb = VF != 0 ? reinterpret_cast<const uint8_t*>(p.v_scale) +
                                      static_cast<size_t>(bh) * nblk * (KVB / 32) * D
                                : nullptr;
@@ -775,6 +784,7 @@ template <int D, int KVB>
 static void launch_attn_f(const AttnArgs& a, hipStream_t st) {
   if (a.v_format == 0) launch_attn_t<D, KVB, 0>(a, st);
   else if (a.v_format == 2) launch_attn_t<D, KVB, 2>(a, st);
+  else if (a.v_format == 3) launch_attn_t<D, KVB, 3>(a, st);
   else launch_attn_t<D, KVB, 1>(a, st);
 }
 

@@ -530,27 +530,60 @@ __global__ __launch_bounds__(256) void k_vres_e4m3(const uint16_t* __restrict__ 
 //     of r / 2^e; layout [Np/64][d][32 bytes], even position in the low nibble;
 //   FMT 2, MXFP8: E8M0 exponent e, the smallest integer with amax <= 448 * 2^e
 //     (no element saturates), E4M3 codes of r / 2^e (round to nearest even);
-//     layout as the E4M3 residuals, [Np/64][d][64 bytes].
-// Exponents are clamped to [-127, 127] (0 for an all-zero group); scales are
+//     layout as the E4M3 residuals, [Np/64][d][64 bytes];
+//   FMT 3, NVFP4-style residuals in the exact form the FP8 matrix core takes:
+//     the head's second-level scale 2^t (smallest t with max|r| <= 6*448*2^t),
+//     per 16 positions x channel the E4M3 block scale
+//     s16 = E4M3(fp32(amax16 / (6 * 2^t))) and E2M1 elements
+//     q = E2M1(fp32(r / (s16 * 2^t))) (zeros where s16 rounds to 0).  The
+//     value v = q * s16 has at most six significant bits; per 32 positions
+//     e is the smallest integer with max|v| <= 448 * 2^e, and v / 2^e is
+//     stored as two E4M3 codes, high = E4M3(v / 2^e) and
+//     low = E4M3(v / 2^e - high), with the E8M0 byte e + t + 127.  Per block
+//     all high codes ([KVB/64][d][64 bytes]), then all low codes.
+// Exponents are clamped to E8M0's range (0 for an all-zero group); scales are
 // stored in lane order (mx_scale_slot).  Rows are gathered whole by
 // BlockRows; the group maxima meet in LDS (max of the fp32 bit patterns of
 // |r|), then every thread encodes its values into a code tile in LDS, which
 // is written out in 16-byte pieces.
 template <int D, int KVB, int FMT>
 __global__ __launch_bounds__(256) void k_vres_mx(const uint16_t* __restrict__ V, const int32_t* __restrict__ perm,
-                                                 const float* __restrict__ v_mean, int N, int nblk,
+                                                 const float* __restrict__ v_mean,
+                                                 const uint32_t* __restrict__ vramax, int N, int nblk,
                                                  uint8_t* __restrict__ Vres, uint8_t* __restrict__ e8m0) {
   using BR = BlockRows<D, KVB>;
+  constexpr bool NV = FMT == 3;
   constexpr int NG = KVB / 32;                       // scale groups per block
+  constexpr int NA = NV ? KVB / 16 : NG;             // amax groups (16 positions for FMT 3)
   __shared__ float sMean[D];
-  __shared__ uint32_t sAm[NG][D];
+  __shared__ uint32_t sAm[NA][D];
   __shared__ int sE[NG][D];
+  __shared__ float sDen[NV ? NA : 1][D];             // FMT 3: s16 * 2^t per 16-position block
+  __shared__ int sTx;                                 // FMT 3: t
   __shared__ __attribute__((aligned(16))) uint32_t sT[D][KVB / 4 + 1];   // codes [channel][position/4]
+  __shared__ __attribute__((aligned(16))) uint32_t sT2[NV ? D : 1][KVB / 4 + 1];   // FMT 3: low codes
   const int bh = blockIdx.y, b = blockIdx.x;
   const int p0 = b * KVB;
   const int cg = threadIdx.x % BR::CG, q = threadIdx.x / BR::CG;
-  for (int i = threadIdx.x; i < NG * D; i += 256) (&sAm[0][0])[i] = 0u;
+  for (int i = threadIdx.x; i < NA * D; i += 256) (&sAm[0][0])[i] = 0u;
   if (threadIdx.x < D) sMean[threadIdx.x] = v_mean[(static_cast<size_t>(bh) * nblk + b) * D + threadIdx.x];
+  if constexpr (NV) {
+    if (threadIdx.x < 64) {
+      float m = 0.0f;
+      for (int c = threadIdx.x; c < D; c += 64) m = fmaxf(m, __uint_as_float(vramax[static_cast<size_t>(bh) * D + c]));
+      m = wave_max(m);
+      if (threadIdx.x == 0) {
+        int t = 0;
+        if (m > 0.0f) {
+          int fe;
+          frexpf(m, &fe);                  // m = f * 2^fe, f in [0.5, 1); 2688 * 2^(fe-12) = 1.3125 * 2^(fe-1)
+          t = fe - 12;
+          if (m > ldexpf(2688.0f, t)) ++t;
+        }
+        sTx = t;
+      }
+    }
+  }
   BR rows;
   rows.load(V + static_cast<size_t>(bh) * N * D, perm + static_cast<size_t>(bh) * N, p0, N);
   __syncthreads();
@@ -568,14 +601,30 @@ __global__ __launch_bounds__(256) void k_vres_mx(const uint16_t* __restrict__ V,
           rows.v[pass][rr][e] = x;
           am = fmaxf(am, fabsf(x));
         }
-        atomicMax(&sAm[r4 / 8][c], __float_as_uint(am));
+        atomicMax(&sAm[NV ? r4 / 4 : r4 / 8][c], __float_as_uint(am));
       }
     }
   }
   __syncthreads();
+  if constexpr (NV) {
+    // block scales, and each 16-position block's largest |q * s16| (the
+    // quotient and E2M1 rounding are monotone, so it is the maximum's)
+    const float st = ldexpf(1.0f, sTx);
+    for (int i = threadIdx.x; i < NA * D; i += 256) {
+      const int sub = i / D, c = i % D;
+      const float am = __uint_as_float(sAm[sub][c]);
+      const float s16 = e4m3_value(e4m3_encode(am / (6.0f * st)));
+      const float den = s16 * st;
+      sDen[sub][c] = den;
+      const float vm = den > 0.0f ? fabsf(e2m1_value(e2m1_encode(am / den))) * s16 : 0.0f;
+      sAm[sub][c] = __float_as_uint(vm);
+    }
+    __syncthreads();
+  }
   for (int i = threadIdx.x; i < NG * D; i += 256) {
     const int grp = i / D, c = i % D;
-    const float am = __uint_as_float(sAm[grp][c]);
+    const float am = NV ? fmaxf(__uint_as_float(sAm[2 * grp][c]), __uint_as_float(sAm[2 * grp + 1][c]))
+                        : __uint_as_float(sAm[grp][c]);
     int ex = 0;
     if (am > 0.0f) {
       int fe;
@@ -589,8 +638,9 @@ __global__ __launch_bounds__(256) void k_vres_mx(const uint16_t* __restrict__ V,
       ex = min(max(ex, -127), 127);
     }
     sE[grp][c] = ex;
+    const int byte = NV ? min(max(ex + sTx + 127, 0), 254) : ex + 127;
     e8m0[(static_cast<size_t>(bh) * (nblk * KVB / 32) + p0 / 32 + grp) * D + mx_scale_slot<D>(c)] =
-        static_cast<uint8_t>(ex + 127);
+        static_cast<uint8_t>(byte);
   }
   __syncthreads();
 #pragma unroll
@@ -601,18 +651,35 @@ __global__ __launch_bounds__(256) void k_vres_mx(const uint16_t* __restrict__ V,
       for (int e = 0; e < 8; ++e) {
         const int c = cg * 8 + e;
         const int ex = sE[r4 / 8][c];
-        float x[4];
+        if constexpr (NV) {
+          const float den = sDen[r4 / 4][c];
+          const float s16 = ldexpf(den, -sTx);
+          float y[4];
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) x[rr] = ldexpf(rows.v[pass][rr][e], -ex);
-        if constexpr (FMT == 1) {
-          sT[c][r4] = e2m1_encode(x[0]) | (e2m1_encode(x[1]) << 4) | (e2m1_encode(x[2]) << 8) |
-                      (e2m1_encode(x[3]) << 12);
+          for (int rr = 0; rr < 4; ++rr) {
+            const float xq = den > 0.0f ? rows.v[pass][rr][e] / den : 0.0f;
+            y[rr] = ldexpf(e2m1_value(e2m1_encode(xq)) * s16, -ex);    // exact; |y| <= 448
+          }
+          const uint32_t hi = e4m3x4(y[0], y[1], y[2], y[3]);
+          float l[4];
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) l[rr] = y[rr] - e4m3_value((hi >> (8 * rr)) & 0xffu);
+          sT[c][r4] = hi;
+          sT2[c][r4] = e4m3x4(l[0], l[1], l[2], l[3]);
         } else {
-          // |x| <= 448 unless the exponent clamp binds; the clamp keeps the
-          // hardware convert (which does not saturate) finite then
+          float x[4];
 #pragma unroll
-          for (int rr = 0; rr < 4; ++rr) x[rr] = fminf(fmaxf(x[rr], -448.0f), 448.0f);
-          sT[c][r4] = e4m3x4(x[0], x[1], x[2], x[3]);
+          for (int rr = 0; rr < 4; ++rr) x[rr] = ldexpf(rows.v[pass][rr][e], -ex);
+          if constexpr (FMT == 1) {
+            sT[c][r4] = e2m1_encode(x[0]) | (e2m1_encode(x[1]) << 4) | (e2m1_encode(x[2]) << 8) |
+                        (e2m1_encode(x[3]) << 12);
+          } else {
+            // |x| <= 448 unless the exponent clamp binds; the clamp keeps the
+            // hardware convert (which does not saturate) finite then
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) x[rr] = fminf(fmaxf(x[rr], -448.0f), 448.0f);
+            sT[c][r4] = e4m3x4(x[0], x[1], x[2], x[3]);
+          }
         }
       }
     }
@@ -631,12 +698,16 @@ __global__ __launch_bounds__(256) void k_vres_mx(const uint16_t* __restrict__ V,
           make_uint4(w[0], w[1], w[2], w[3]);
     }
   } else {
-    // as the E4M3 residuals: per 64-position step, D rows of 64 bytes
-    uint32_t* out = reinterpret_cast<uint32_t*>(Vres + (static_cast<size_t>(bh) * nblk * KVB + p0) * D);
-    for (int i = threadIdx.x; i < (KVB / 64) * D * 4; i += 256) {
-      const int step = i / (D * 4), rem = i % (D * 4), c = rem / 4, part = rem % 4;
-      const uint32_t* src = &sT[c][step * 16 + part * 4];
-      *reinterpret_cast<uint4*>(out + (static_cast<size_t>(step) * D + c) * 16 + part * 4) =
+    // as the E4M3 residuals: per 64-position step, D rows of 64 bytes (FMT 3:
+    // the high codes, then the low codes)
+    constexpr int NSET = NV ? 2 : 1;
+    uint32_t* out = reinterpret_cast<uint32_t*>(Vres + (static_cast<size_t>(bh) * nblk * KVB + p0) * D * NSET);
+    for (int i = threadIdx.x; i < NSET * (KVB / 64) * D * 4; i += 256) {
+      const int set = i / ((KVB / 64) * D * 4), j = i % ((KVB / 64) * D * 4);
+      const int step = j / (D * 4), rem = j % (D * 4), c = rem / 4, part = rem % 4;
+      const uint32_t* src = set == 0 ? &sT[c][step * 16 + part * 4] : &sT2[NV ? c : 0][step * 16 + part * 4];
+      *reinterpret_cast<uint4*>(out + static_cast<size_t>(set) * KVB * D / 4 +
+                                (static_cast<size_t>(step) * D + c) * 16 + part * 4) =
           make_uint4(src[0], src[1], src[2], src[3]);
     }
   }
@@ -950,17 +1021,23 @@ template <int D, int KVB>
 static hipError_t vres_t(const PrepArgs& a, const int32_t* perm, const PrepOut& o, hipStream_t st) {
   const int BH = a.B * a.H;
   const int e4 = a.v_format == 0;
+  // the per-channel max |r| of the head: the E4M3 scales, the NVFP4-style second-level scale
+  const int want_amax = a.v_format == 0 || a.v_format == 3;
   hipLaunchKernelGGL((k_vblock_stats<D, KVB>), dim3(a.nblk, BH), dim3(256), 0, st, a.V, perm, a.N, a.nblk,
-                     a.vsmooth, e4, o.v_mean, a.vramax);
+                     a.vsmooth, want_amax, o.v_mean, a.vramax);
+  uint8_t* e8 = reinterpret_cast<uint8_t*>(o.v_scale);
   if (e4)
     hipLaunchKernelGGL((k_vres_e4m3<D, KVB>), dim3(a.nblk, BH), dim3(256), 0, st, a.V, perm, o.v_mean, a.vramax,
                        a.N, a.nblk, o.Vres, reinterpret_cast<float*>(o.v_scale));
   else if (a.v_format == 1)
-    hipLaunchKernelGGL((k_vres_mx<D, KVB, 1>), dim3(a.nblk, BH), dim3(256), 0, st, a.V, perm, o.v_mean, a.N,
-                       a.nblk, o.Vres, reinterpret_cast<uint8_t*>(o.v_scale));
+    hipLaunchKernelGGL((k_vres_mx<D, KVB, 1>), dim3(a.nblk, BH), dim3(256), 0, st, a.V, perm, o.v_mean, a.vramax,
+                       a.N, a.nblk, o.Vres, e8);
+  else if (a.v_format == 2)
+    hipLaunchKernelGGL((k_vres_mx<D, KVB, 2>), dim3(a.nblk, BH), dim3(256), 0, st, a.V, perm, o.v_mean, a.vramax,
+                       a.N, a.nblk, o.Vres, e8);
   else
-    hipLaunchKernelGGL((k_vres_mx<D, KVB, 2>), dim3(a.nblk, BH), dim3(256), 0, st, a.V, perm, o.v_mean, a.N,
-                       a.nblk, o.Vres, reinterpret_cast<uint8_t*>(o.v_scale));
+    hipLaunchKernelGGL((k_vres_mx<D, KVB, 3>), dim3(a.nblk, BH), dim3(256), 0, st, a.V, perm, o.v_mean, a.vramax,
+                       a.N, a.nblk, o.Vres, e8);
   hipLaunchKernelGGL((k_ksmooth<D, KVB>), dim3(a.nblk, BH), dim3(256), 0, st, a.K, perm, a.mu, a.N, a.nblk, o.Kq,
                      o.k_scale);
   return hipGetLastError();

@@ -68,6 +68,21 @@ __device__ __forceinline__ uint32_t e2m1_encode(float x) {
   return code | sign;
 }
 
+// value of an OCP E2M1 nibble (sign in bit 3)
+__device__ __forceinline__ float e2m1_value(uint32_t c) {
+  const uint32_t m = c & 7u;
+  const float v = m < 5u ? 0.5f * static_cast<float>(m) : (m == 5u ? 3.0f : (m == 6u ? 4.0f : 6.0f));
+  return (c & 8u) ? -v : v;
+}
+
+// value of a finite OCP E4M3 code (sign in bit 7)
+__device__ __forceinline__ float e4m3_value(uint32_t c) {
+  const int e = static_cast<int>((c >> 3) & 15u);
+  const float m = static_cast<float>(c & 7u);
+  const float v = e == 0 ? ldexpf(m, -9) : ldexpf(1.0f + 0.125f * m, e - 7);
+  return (c & 0x80u) ? -v : v;
+}
+
 // x / s rounded once to binary32, given y = fp32(1 / s) rounded once:
 // q = x*y, then one correction from the exact residual x - q*s (Markstein's
 // division with a correctly rounded reciprocal; s > 0 normal, x finite).

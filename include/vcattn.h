@@ -46,10 +46,22 @@
  *            MXFP4: uint8 [B,H,Np/64,d,32]  same, two E2M1 codes per byte, the
  *                   even position in the low nibble.
  *            MXFP8: as E4M3 (codes relative to the E8M0 scales below).
+ *            NVFP4 style: uint8 [B,H,nblk,2,kv_block/64,d,64]  per block the
+ *                   E4M3 "high" codes of all its 64-position groups (E4M3
+ *                   layout), then the "low" codes.  The quantised residual
+ *                   (per 16 sorted positions x channel an E4M3 block scale s16
+ *                   = E4M3(amax16 / (6 * 2^t)), E2M1 elements, a power-of-two
+ *                   second-level scale 2^t per head) is v = e2m1 * s16 * 2^t;
+ *                   with e per 32 positions x channel the smallest integer with
+ *                   max|e2m1 * s16| <= 448 * 2^e, high = E4M3(e2m1 * s16 / 2^e)
+ *                   and low = E4M3(e2m1 * s16 / 2^e - high), so
+ *                   v = (high + low) * 2^(e + t) (exactly, unless the low part
+ *                   falls below E4M3's smallest subnormal).
  *   v_scale  E4M3:  fp32 [B,H,d]  per-channel residual scale.
- *            MXFP4, MXFP8: uint8 E8M0 [B,H,Np/32,d]  one scale per 32 sorted
- *                   positions and channel; inside a group, channel c = 32T + u
- *                   (u < 32) is stored at byte u * (d/32) + T.
+ *            MXFP4, MXFP8, NVFP4 style: uint8 E8M0 [B,H,Np/32,d]  one scale
+ *                   per 32 sorted positions and channel (NVFP4 style: e + t);
+ *                   inside a group, channel c = 32T + u (u < 32) is stored at
+ *                   byte u * (d/32) + T.
  *   v_mean   fp32 [B,H,nblk,d]  block means (zero when V-Smooth is off).
  */
 #ifndef VCATTN_H
@@ -79,7 +91,9 @@ typedef struct {
   int32_t vsmooth;          /* 1: V-Smooth on; 0: identity order, zero means       */
   int32_t v_format;         /* 0: E4M3 residuals, per-channel scale; 1: MXFP4;     */
                             /*    2: MXFP8 (E4M3 codes, E8M0 scale per 32 sorted   */
-                            /*    positions and channel)                           */
+                            /*    positions and channel); 3: NVFP4 style (E2M1,    */
+                            /*    E4M3 scale per 16 sorted positions and channel), */
+                            /*    stored and multiplied as two E4M3 parts          */
   int32_t out_fp32;         /* 0: O is bf16; 1: O is fp32                          */
   float softmax_scale;      /* 0 selects fp32(1/sqrt(d))                           */
   float beta;               /* ExpCast offset, -0.5 <= beta <= 0.45                */

@@ -23,6 +23,14 @@ Readings (the pages leave these open):
     of one scale per channel): per 32 consecutive sorted tokens x channel an
     E8M0 scale 2^e, e the smallest integer with amax <= 448 * 2^e (so no
     element saturates), and E4M3 elements of r / 2^e, round to nearest even.
+  * NVFP4-style residuals ([zh] names NVFP4 for the 4-bit residuals): per 16
+    consecutive sorted tokens x channel an E4M3 block scale
+    s16 = E4M3(fp32(amax16 / (6 * s_t))) and E2M1 elements
+    E2M1(fp32(r / (s16 * s_t))) (nearest even, saturating at 6; a block whose
+    scale rounds to 0 holds zeros).  The second-level scale s_t, one per head,
+    is a power of two here (the smallest 2^t with amax <= 6 * 448 * 2^t), so
+    that it folds into the matrix core's power-of-two scales; dequantised
+    value = e2m1 * s16 * s_t.
   * K smoothing (prior art the pages contrast V-Smooth with: "earlier
     low-bit methods ... smoothed queries and keys"): mu_K = fp32(fp64 mean over
     all tokens, per channel); K' = fp32(K - mu_K); per block
@@ -37,7 +45,7 @@ from __future__ import annotations
 import numpy as np
 
 from .formats import (f32, e4m3_encode, e4m3_decode, e2m1_encode, e2m1_decode, mx_shared_exponent,
-                      e4m3_group_exponent)
+                      e4m3_group_exponent, nv_tensor_exponent)
 
 
 def stable_sort_perm(labels: np.ndarray, k: int) -> np.ndarray:
@@ -112,6 +120,20 @@ def vsmooth_values(V: np.ndarray, perm: np.ndarray, kv_block: int, fmt: str = "e
         codes[N:] = 0
         vals = (e4m3_decode(codes).reshape(Np // 32, 32, d) * np.ldexp(1.0, e)[:, None, :]).reshape(Np, d)
         out.update(codes=codes, vres=vals, col_scale=np.ones(d), e8m0=(e + 127).astype(np.uint8))
+    elif fmt == "nvfp4":
+        amax = float(np.max(np.abs(r[:N]))) if N else 0.0
+        t = int(nv_tensor_exponent(amax))
+        s_t = np.ldexp(1.0, t)
+        g = r.reshape(Np // 16, 16, d)
+        a16 = np.max(np.abs(g), axis=1)                          # [Np/16, d]
+        s16c = e4m3_encode(f32(a16 / (6.0 * s_t)))
+        den = e4m3_decode(s16c) * s_t                            # exact: power-of-two factor
+        with np.errstate(divide="ignore", invalid="ignore"):
+            x = np.where(den[:, None, :] > 0, f32(g / den[:, None, :]), 0.0)
+        codes = e2m1_encode(x).reshape(Np, d)
+        codes[N:] = 0
+        vals = (e2m1_decode(codes).reshape(Np // 16, 16, d) * den[:, None, :]).reshape(Np, d)
+        out.update(codes=codes, vres=vals, col_scale=np.ones(d), e8m0=None, nv_scale=s16c, nv_t=t)
     else:
         raise ValueError(fmt)
     return out

@@ -47,3 +47,28 @@ def mx_scales_natural(vs: np.ndarray) -> np.ndarray:
     d = vs.shape[-1]
     c = np.arange(d)
     return vs[..., (c & 31) * (d // 32) + (c >> 5)]
+
+
+def nv_pair_natural(Vres: np.ndarray):
+    """NVFP4-style residuals [..., nblk, 2, kv_block/64, d, 64] -> (high, low)
+    E4M3 codes, each [..., Np, d] in sorted-position order."""
+    def nat(x):
+        x = x.reshape(*x.shape[:-4], x.shape[-4] * x.shape[-3], x.shape[-2], x.shape[-1])
+        return vres_natural(x, "e4m3")
+    return nat(Vres[..., 0, :, :, :]), nat(Vres[..., 1, :, :, :])
+
+
+def nv_pair_expected(codes: np.ndarray, s16c: np.ndarray, t: int):
+    """The library's documented storage of an NVFP4-style residual, computed
+    from the oracle's E2M1 codes [Np, d], E4M3 block scales [Np/16, d] and
+    second-level exponent t: v = e2m1 * s16; per 32 positions x channel e is
+    the smallest integer with max|v| <= 448 * 2^e (0 for an all-zero group);
+    high = E4M3(v / 2^e), low = E4M3(v / 2^e - high); E8M0 byte e + t + 127."""
+    from oracle import formats as F
+    Np, d = codes.shape
+    v = F.e2m1_decode(codes) * np.repeat(F.e4m3_decode(s16c), 16, axis=0)
+    e = F.e4m3_group_exponent(np.max(np.abs(v.reshape(Np // 32, 32, d)), axis=1))
+    y = v / np.repeat(np.ldexp(1.0, e), 32, axis=0)
+    hi = F.e4m3_encode(y)
+    lo = F.e4m3_encode(y - F.e4m3_decode(hi))
+    return hi, lo, np.clip(e + t + 127, 0, 254).astype(np.uint8)

@@ -65,7 +65,7 @@ def cfg(**kw):
     (dict(iters=0), VC_ERR_INVALID_ARG),
     (dict(beta=0.5), VC_ERR_INVALID_ARG),
     (dict(beta=-0.6), VC_ERR_INVALID_ARG),
-    (dict(v_format=3), VC_ERR_UNSUPPORTED),
+    (dict(v_format=4), VC_ERR_UNSUPPORTED),
     (dict(p_mode=2), VC_ERR_UNSUPPORTED),
     (dict(cluster_order=2), VC_ERR_UNSUPPORTED),
     (dict(N=(1 << 24), d=128, n_clusters=16), VC_ERR_UNSUPPORTED),     # 2^31 bytes of blocked keys per head

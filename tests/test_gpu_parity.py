@@ -20,7 +20,7 @@ from oracle import formats as F
 from oracle.attention import DEFAULT_BETA, exact_attention, exp2cast_bytes, expcast_bytes, softmax_scale
 from bit_attention_video_amd import binding as vb
 from bit_attention_video_amd import inputs
-from layouts import kq_natural, mx_scales_natural, vres_natural, to_device_bf16
+from layouts import kq_natural, mx_scales_natural, vres_natural, to_device_bf16, nv_pair_natural, nv_pair_expected
 
 pytestmark = pytest.mark.gpu
 
@@ -41,7 +41,7 @@ def _gpu():
 
 
 def fmt_id(fmt):
-    return {"e4m3": vb.E4M3, "mxfp4": vb.MXFP4, "mxfp8": vb.MXFP8}[fmt]
+    return {"e4m3": vb.E4M3, "mxfp4": vb.MXFP4, "mxfp8": vb.MXFP8, "nvfp4": vb.NVFP4}[fmt]
 
 
 def cfg_for(w, H=None, N=None, vsmooth=True, fmt=None, out_fp32=True, beta=DEFAULT_BETA, mode="expcast",
@@ -63,7 +63,10 @@ def prep_to_numpy(prep: vb.Prepared, fmt):
     out = {k: getattr(prep, k).cpu().numpy() for k in ("Kq", "k_scale", "Vres", "v_scale", "v_mean", "perm")}
     out["labels"] = prep.labels.cpu().numpy() if prep.labels is not None else None
     out["Kq_nat"] = kq_natural(out["Kq"])
-    out["Vres_nat"] = vres_natural(out["Vres"], fmt)
+    if fmt == "nvfp4":
+        out["hi"], out["lo"] = nv_pair_natural(out["Vres"])
+    else:
+        out["Vres_nat"] = vres_natural(out["Vres"], fmt)
     if fmt != "e4m3":
         out["v_scale"] = mx_scales_natural(out["v_scale"])
     return out
@@ -86,6 +89,18 @@ def compare_prep(g, o, b, h, fmt, vsmooth=True):
     kq_diff = np.count_nonzero(g["Kq_nat"][b, h] != o["k"]["codes"])
     assert kq_diff == 0, f"{kq_diff} Kq codes differ"
     assert np.array_equal(g["v_mean"][b, h], o["v"]["means"].astype(np.float32)), "means differ"
+    if fmt == "nvfp4":
+        hi, lo, e8 = nv_pair_expected(o["v"]["codes"], o["v"]["nv_scale"], o["v"]["nv_t"])
+        assert np.count_nonzero(g["hi"][b, h] != hi) == 0, "high codes differ"
+        assert np.count_nonzero(g["lo"][b, h] != lo) == 0, "low codes differ"
+        assert np.array_equal(g["v_scale"][b, h], e8), "E8M0 scales differ"
+        # high + low carry the oracle's dequantised residual (exactly, unless
+        # the low part falls below E4M3's smallest subnormal)
+        X = np.repeat(F.e8m0_decode(e8.astype(np.int64)), 32, axis=0)
+        rec = (F.e4m3_decode(hi) + F.e4m3_decode(lo)) * X
+        err = np.abs(rec - o["v"]["vres"])
+        assert np.all(err <= 2.0 ** -10 * X), float(np.max(err / X))
+        return
     v_diff = np.count_nonzero(g["Vres_nat"][b, h] != o["v"]["codes"])
     assert v_diff == 0, f"{v_diff} residual codes differ"
     if fmt == "e4m3":
@@ -200,7 +215,8 @@ def test_kmeans_assign_given_oracle_centroids(name, H, N):
     ("tiny", 2, None, True, "e4m3"), ("tiny", 2, None, False, "e4m3"), ("tiny", 2, None, True, "mxfp4"),
     ("tiny", 1, 1000, True, "e4m3"), ("tiny", 1, 1, True, "e4m3"), ("mid", 2, None, True, "e4m3"),
     ("mid", 1, 3000, True, "mxfp4"), ("tiny", 2, None, True, "mxfp8"), ("mid", 1, 3000, True, "mxfp8"),
-    ("tiny", 1, 1000, False, "mxfp8"),
+    ("tiny", 1, 1000, False, "mxfp8"), ("tiny", 2, None, True, "nvfp4"), ("mid", 1, 3000, True, "nvfp4"),
+    ("tiny", 1, 1000, False, "nvfp4"), ("tiny", 1, 77, True, "nvfp4"),
 ])
 def test_prepare_bit_exact(name, H, N, vsmooth, fmt):
     w = inputs.WORKLOADS[name]
@@ -235,6 +251,11 @@ def oracle_rows(w, host, b, h, prep_o, tiles, beta=DEFAULT_BETA, mode="expcast")
     ("tiny", 1, 77, True, "mxfp8", 64, None, "expcast"),        # partial scale groups
     ("tiny", 1, 1, True, "mxfp8", 64, None, "expcast"),         # a single token
     ("mid", 1, 5000, True, "mxfp8", None, None, "exp2"),
+    ("tiny", 2, None, True, "nvfp4", None, None, "expcast"),     # 16-token E4M3 block scales, emulated
+    ("tiny", 1, 1000, True, "nvfp4", 128, 128, "expcast"),
+    ("tiny", 1, 77, True, "nvfp4", 64, None, "expcast"),
+    ("tiny", 1, 1000, False, "nvfp4", 128, 128, "exp2"),
+    ("mid", 1, 5000, True, "nvfp4", None, None, "expcast"),
 ])
 def test_attention_parity(name, H, N, vsmooth, fmt, kvb, d, mode):
     import dataclasses

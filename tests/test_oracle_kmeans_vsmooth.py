@@ -200,6 +200,75 @@ def test_mx_exponent_rule_examples():
     assert list(F.e4m3_group_exponent(amax)) == [-8, 0, 1, 1, -9, -127, 0, -1]
 
 
+def test_nv_tensor_exponent_is_smallest_fitting_power():
+    # brute force: the smallest t with amax <= 6 * 448 * 2^t
+    rng = np.random.default_rng(21)
+    amax = np.concatenate([[2688.0, 2688.0 * (1 + 2.0 ** -40), 1344.0, 1.0, 0.0, 3.5e-6],
+                           np.exp(rng.uniform(-30, 30, 200))])
+    t = F.nv_tensor_exponent(amax)
+    for a, ti in zip(amax, t):
+        if a == 0:
+            assert ti == 0
+            continue
+        want = next(k for k in range(-80, 80) if a <= 2688.0 * 2.0 ** k)
+        assert ti == want, (a, ti, want)
+    assert list(t[:5]) == [0, 1, -1, -11, 0]
+
+
+def _nvfp4_case(seed=22):
+    rng = np.random.default_rng(seed)
+    N, d, kvb = 300, 6, 64
+    V = F.f32(rng.standard_normal((N, d)) * np.array([0.01, 0.3, 1, 3, 30, 200]))
+    V[rng.integers(0, N, 5), 1] *= 50.0                  # a few outliers in one channel
+    perm = rng.permutation(N).astype(np.int32)
+    out = VS.vsmooth_values(V, perm, kvb, "nvfp4")
+    Np = 320
+    r = np.zeros((Np, d))
+    r[:N] = F.f32(V[perm] - np.repeat(out["means"], kvb, 0)[:N])
+    return N, d, Np, r, out
+
+
+def test_nvfp4_residuals_nearest_on_the_block_grid():
+    """Every dequantised residual is the nearest point of its block's grid
+    {+-0, 0.5, 1, 1.5, 2, 3, 4, 6} * s16 * s_t (brute force over the grid;
+    values beyond 6 clip), and the block scale is the E4M3 value nearest to
+    amax16 / (6 s_t)."""
+    N, d, Np, r, out = _nvfp4_case()
+    t = out["nv_t"]
+    amax = np.max(np.abs(r[:N]))
+    assert amax <= 2688.0 * 2.0 ** t and amax > 1344.0 * 2.0 ** t
+    s16 = F.e4m3_decode(out["nv_scale"])                             # [Np/16, d]
+    a16 = np.max(np.abs(r.reshape(Np // 16, 16, d)), axis=1)
+    want = a16 / (6.0 * 2.0 ** t)
+    grid8 = F.e4m3_decode(np.arange(127, dtype=np.uint8))
+    nearest = grid8[np.argmin(np.abs(grid8[None, :] - want.reshape(-1, 1)), axis=1)].reshape(want.shape)
+    assert np.all(np.abs(s16 - want) <= np.abs(nearest - want) + 1e-300)
+    den = np.repeat(s16 * 2.0 ** t, 16, axis=0)
+    grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6])
+    cand = np.sign(r)[..., None] * grid * den[..., None]
+    best = np.min(np.abs(cand - r[..., None]), axis=-1)
+    err = np.abs(out["vres"] - r)
+    rel_ulp = 2.0 ** -20 * np.abs(r)                                 # the fp32 quotient's rounding
+    assert np.all(err <= best + rel_ulp + 1e-300)
+    assert np.array_equal(out["vres"], F.e2m1_decode(out["codes"]) * den)
+    assert np.all(out["codes"][N:] == 0) and np.all(out["col_scale"] == 1)
+
+
+def test_nvfp4_scales_with_powers_of_two():
+    # scaling V by 2^k scales the residuals, the second-level scale and the
+    # dequantised values by 2^k and leaves codes and block scales unchanged
+    N, d, Np, r, out = _nvfp4_case(23)
+    rng = np.random.default_rng(23)
+    V = F.f32(rng.standard_normal((N, d)) * np.array([0.01, 0.3, 1, 3, 30, 200]))
+    V[rng.integers(0, N, 5), 1] *= 50.0
+    perm = rng.permutation(N).astype(np.int32)
+    for k in (-7, 5):
+        o2 = VS.vsmooth_values(V * 2.0 ** k, perm, 64, "nvfp4")
+        assert o2["nv_t"] == out["nv_t"] + k
+        assert np.array_equal(o2["codes"], out["codes"]) and np.array_equal(o2["nv_scale"], out["nv_scale"])
+        assert np.array_equal(o2["vres"], out["vres"] * 2.0 ** k)
+
+
 def test_vsmooth_off_is_plain_per_channel_quantisation():
     rng = np.random.default_rng(18)
     V = F.f32(rng.standard_normal((100, 4)))
