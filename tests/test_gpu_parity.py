@@ -216,7 +216,7 @@ def test_kmeans_assign_given_oracle_centroids(name, H, N):
     ("tiny", 1, 1000, True, "e4m3"), ("tiny", 1, 1, True, "e4m3"), ("mid", 2, None, True, "e4m3"),
     ("mid", 1, 3000, True, "mxfp4"), ("tiny", 2, None, True, "mxfp8"), ("mid", 1, 3000, True, "mxfp8"),
     ("tiny", 1, 1000, False, "mxfp8"), ("tiny", 2, None, True, "nvfp4"), ("mid", 1, 3000, True, "nvfp4"),
-    ("tiny", 1, 1000, False, "nvfp4"), ("tiny", 1, 77, True, "nvfp4"),
+    ("tiny", 1, 1000, False, "nvfp4"), ("tiny", 1, 77, True, "nvfp4"), ("tiny", 1, 1, True, "nvfp4"),
 ])
 def test_prepare_bit_exact(name, H, N, vsmooth, fmt):
     w = inputs.WORKLOADS[name]
@@ -256,6 +256,8 @@ def oracle_rows(w, host, b, h, prep_o, tiles, beta=DEFAULT_BETA, mode="expcast")
     ("tiny", 1, 77, True, "nvfp4", 64, None, "expcast"),
     ("tiny", 1, 1000, False, "nvfp4", 128, 128, "exp2"),
     ("mid", 1, 5000, True, "nvfp4", None, None, "expcast"),
+    ("tiny", 1, 1, True, "nvfp4", 64, None, "expcast"),         # a single token
+    ("tiny", 1, 700, True, "nvfp4", 128, 64, "expcast"),        # d = 64 with 128-key blocks
 ])
 def test_attention_parity(name, H, N, vsmooth, fmt, kvb, d, mode):
     import dataclasses
@@ -279,7 +281,7 @@ def test_attention_parity(name, H, N, vsmooth, fmt, kvb, d, mode):
         check_close(Og, Oref, vmax, f"{name} N={N} h{h} vs={vsmooth} {fmt} {mode}")
 
 
-@pytest.mark.parametrize("fmt", ["e4m3", "mxfp4"])
+@pytest.mark.parametrize("fmt", ["e4m3", "mxfp4", "nvfp4"])
 def test_batch_of_two_and_explicit_parameters(fmt):
     """B = 2 (every (b, h) pair prepared and attended in one call), with an
     explicit softmax scale and ExpCast bias instead of the defaults."""
