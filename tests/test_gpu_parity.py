@@ -377,16 +377,16 @@ def _prep_np(prep, fmt):
     return prep_to_numpy(prep, fmt)
 
 
-@pytest.mark.parametrize("name,H,N", [("tiny", 2, None), ("mid", 1, 5000)])
-def test_warm_start_and_perm_reuse_bit_exact(name, H, N):
+@pytest.mark.parametrize("name,H,N,fmt", [("tiny", 2, None, "e4m3"), ("mid", 1, 5000, "e4m3"),
+                                          ("tiny", 1, None, "mxfp8"), ("tiny", 1, None, "nvfp4")])
+def test_warm_start_and_perm_reuse_bit_exact(name, H, N, fmt):
     # step 0: cold start with centroids_out; step 1 (perturbed K, V): one
     # warm-started pass from those centroids; step 2: reuse step 1's perm.
     # Every output is compared with the oracle bit for bit.
     w = inputs.WORKLOADS[name]
     host, dev = gen(w, H=H, N=N)
     N = N or w.N
-    fmt = w.v_format
-    cfg = cfg_for(w, H=H, N=N)
+    cfg = cfg_for(w, H=H, N=N, fmt=fmt)
     k = cfg.n_clusters
     C0 = torch.empty((1, H, k, w.d), dtype=torch.float32, device="cuda")
     p0 = vb.vsmooth_prepare_warm(cfg, dev["K"], dev["V"], init_idx=dev["init"], centroids_out=C0)
@@ -395,7 +395,7 @@ def test_warm_start_and_perm_reuse_bit_exact(name, H, N):
     q, kb, vb_, init = host
     k1 = inputs.next_step(w, kb, 1, 0.05, 1)
     v1 = inputs.next_step(w, vb_, 1, 0.05, 2)
-    cfg1 = cfg_for(w, H=H, N=N)
+    cfg1 = cfg_for(w, H=H, N=N, fmt=fmt)
     cfg1.iters = 1
     C1 = torch.empty_like(C0)
     p1 = vb.vsmooth_prepare_warm(cfg1, to_device_bf16(k1), to_device_bf16(v1), init_centroids=C0, centroids_out=C1)
