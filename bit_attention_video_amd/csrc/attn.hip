@@ -221,6 +221,15 @@ __device__ __forceinline__ v8i join8(uint4 lo, uint4 hi) {
              static_cast<int>(hi.x), static_cast<int>(hi.y), static_cast<int>(hi.z), static_cast<int>(hi.w)};
 }
 
+// Bijection from the hardware workgroup index (dispatched round-robin over
+// the 8 XCDs) to a logical index in which XCD x owns one contiguous range.
+__device__ __forceinline__ int xcd_major_index(int i, int n) {
+  constexpr int kXcds = 8;
+  const int x = i % kXcds, local = i / kXcds;
+  const int per = n / kXcds, rem = n % kXcds;
+  return x < rem ? x * (per + 1) + local : rem * (per + 1) + (x - rem) * per + local;
+}
+
 // Per-wave running state of the online softmax.
 template <int NDT, int MS>
 struct SoftmaxState {
@@ -543,7 +552,11 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_fwd(AttnArgs p) {
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);   // the wave index in a scalar register
   const int N = p.N, nblk = p.nblk;
   const int nqt = (N + TT::ROWS - 1) / TT::ROWS;
-  const int bh = blockIdx.x / nqt, qt = blockIdx.x % nqt;
+  // Workgroups reach the 8 XCDs round-robin by index; renumber them so that
+  // each XCD takes a contiguous range of (head, query tile) pairs, and the
+  // workgroups sharing an XCD's L2 stream the same heads' blocks.
+  const int wg = xcd_major_index(static_cast<int>(blockIdx.x), static_cast<int>(gridDim.x));
+  const int bh = wg / nqt, qt = wg % nqt;
   const int qrow = qt * TT::ROWS + wave * 32 + col;
 
   const uint8_t* kq = p.Kq + static_cast<size_t>(bh) * nblk * KVB * D;
