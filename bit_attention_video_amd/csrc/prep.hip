@@ -531,7 +531,8 @@ __global__ __launch_bounds__(256) void k_vres_e4m3(const uint16_t* __restrict__ 
 //   FMT 2, MXFP8: E8M0 exponent e, the smallest integer with amax <= 448 * 2^e
 //     (no element saturates), E4M3 codes of r / 2^e (round to nearest even);
 //     layout as the E4M3 residuals, [Np/64][d][64 bytes];
-//   FMT 3, NVFP4-style residuals in the exact form the FP8 matrix core takes:
+//   FMT 3, NVFP4-style residuals (the zerohour.day summary's key facts name
+//     NVFP4 for the 4-bit residuals), in the exact form the FP8 matrix core takes:
 //     the head's second-level scale 2^t (smallest t with max|r| <= 6*448*2^t),
 //     per 16 positions x channel the E4M3 block scale
 //     s16 = E4M3(fp32(amax16 / (6 * 2^t))) and E2M1 elements

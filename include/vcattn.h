@@ -46,7 +46,8 @@
  *            MXFP4: uint8 [B,H,Np/64,d,32]  same, two E2M1 codes per byte, the
  *                   even position in the low nibble.
  *            MXFP8: as E4M3 (codes relative to the E8M0 scales below).
- *            NVFP4 style: uint8 [B,H,nblk,2,kv_block/64,d,64]  per block the
+ *            NVFP4 style (zerohour.day summary, key facts: NVFP4 residuals):
+ *                   uint8 [B,H,nblk,2,kv_block/64,d,64]  per block the
  *                   E4M3 "high" codes of all its 64-position groups (E4M3
  *                   layout), then the "low" codes.  The quantised residual
  *                   (per 16 sorted positions x channel an E4M3 block scale s16
