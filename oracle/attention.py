@@ -28,6 +28,14 @@ online softmax keeps; [clarity]: one pass over the values):
   O = (col_scale * acc + accM) / l.
 Accumulators are fp64 here.
 
+Range-shifted ExpCast (mode="expcast_shifted"; a variant, not on the pages):
+the byte relation of [brief] "ExpCast-FP8" holds for any power-of-two
+multiple of p, and the normalisation divides every common factor out.  With
+the addend 120 + beta instead of 56 + beta the FMA writes the byte of
+2^8 * 2^z, clamped to [0, 120] (120 is the E4M3 code of 2^8), so bytes stay in
+E4M3's normal range for z >= -14 instead of z >= -6.  Everything else is the
+literal mode's.
+
 ExpCast off (mode="exp2"): the path ExpCast replaces ([rw] "ExpCast-FP8
 goes after the other end": an fp32 exponential, then a conversion to the
 8-bit format).  Reading: the same log2-domain argument in one binary32 FMA,
@@ -49,11 +57,25 @@ LOG2E = 1.4426950408889634
 DEFAULT_BETA = 8.0 / math.log(2.0) - 12.0
 
 
-def expcast_bytes(S32: np.ndarray, A: float, B: np.ndarray) -> np.ndarray:
-    """Bytes = clamp(rne(fma_f32(S32, A, B)), 0, 56).  B broadcasts per row."""
+# addend of the ExpCast FMA and top byte (the byte of p = 1 times the mode's
+# power-of-two factor): literal 56 = E4M3(1), range-shifted 120 = E4M3(2^8)
+EXPCAST_BASE = {"expcast": 56.0, "expcast_shifted": 120.0}
+
+# smallest scale any quantiser uses: a scale below the smallest normal fp32
+# would have an infinite reciprocal, so amax / 448 (or / 127) is floored here
+SCALE_FLOOR = 2.0 ** -126
+
+
+def scale_of(amax: float, qmax: float) -> float:
+    """fp32(amax / qmax) floored at 2^-126; 1 for an all-zero block."""
+    return max(float(f32(amax / qmax)), SCALE_FLOOR) if amax > 0 else 1.0
+
+
+def expcast_bytes(S32: np.ndarray, A: float, B: np.ndarray, top: float = 56.0) -> np.ndarray:
+    """Bytes = clamp(rne(fma_f32(S32, A, B)), 0, top).  B broadcasts per row."""
     x = fma_f32(S32, A, B)
     with np.errstate(invalid="ignore"):
-        c = np.clip(np.rint(x), 0.0, 56.0)
+        c = np.clip(np.rint(x), 0.0, top)
     c = np.where(np.isnan(c), 0.0, c)
     return c.astype(np.uint8)
 
@@ -74,7 +96,7 @@ def quantize_q_tile(Q: np.ndarray):
     """Per 128-row query tile: s_q = fp32(max|Q|/448) (1 if all zero),
     codes = E4M3(fp32(Q / s_q))."""
     amax = float(np.max(np.abs(Q))) if Q.size else 0.0
-    s_q = float(f32(amax / 448.0)) if amax > 0 else 1.0
+    s_q = scale_of(amax, 448.0)
     codes = e4m3_encode(f32(Q / s_q))
     return codes, s_q
 
@@ -85,8 +107,9 @@ def attend_tile(Q: np.ndarray, kdec: np.ndarray, k_scale: np.ndarray, vres: np.n
                 trace: dict | None = None, mode: str = "expcast") -> np.ndarray:
     """One query tile (rows of Q, fp64 bf16 values) against all KV blocks.
     kdec / vres: decoded permuted keys and residuals [nblk*kv_block, d].
-    mode: "expcast" (probability bytes from one FMA) or "exp2" (ExpCast off)."""
-    if mode not in ("expcast", "exp2"):
+    mode: "expcast" (probability bytes from one FMA), "expcast_shifted" (the
+    same, 64 codes up) or "exp2" (ExpCast off)."""
+    if mode not in ("expcast", "exp2", "expcast_shifted"):
         raise ValueError(mode)
     nblk = k_scale.shape[0]
     n, d = Q.shape
@@ -95,7 +118,8 @@ def attend_tile(Q: np.ndarray, kdec: np.ndarray, k_scale: np.ndarray, vres: np.n
         qc, s_q = quantize_q_tile(Q)
         qdec = e4m3_decode(qc)
         cq = float(f32(f32(s_q * scale) * f32(LOG2E)))
-        Kc = float(f32(56.0 + float(f32(beta))))   # beta is a binary32 parameter
+        base = EXPCAST_BASE.get(mode, 56.0)
+        Kc = float(f32(base + float(f32(beta))))   # beta is a binary32 parameter
     else:
         qdec = Q
         cq = scale * LOG2E
@@ -113,10 +137,10 @@ def attend_tile(Q: np.ndarray, kdec: np.ndarray, k_scale: np.ndarray, vres: np.n
             S32[:, nvalid:] = -np.inf
             t_max = f32(c * np.max(S32, axis=1))
             m_new = np.maximum(m, t_max)
-            if mode == "expcast":
+            if mode != "exp2":
                 A = 8.0 * c
                 Brow = f32(Kc - 8.0 * m_new)
-                codes = expcast_bytes(S32, A, Brow[:, None])
+                codes = expcast_bytes(S32, A, Brow[:, None], base)
             else:
                 A = c
                 Brow = -m_new

@@ -143,12 +143,13 @@ NV_TENSOR_MAX = E2M1_MAX * E4M3_MAX     # 2688: largest element times block scal
 def nv_tensor_exponent(amax) -> np.ndarray:
     """Second-level (per tensor) scale of the NVFP4-style residual, taken as a
     power of two: the smallest t with amax <= 6 * 448 * 2^t, so that every
-    16-element block scale amax16 / (6 * 2^t) fits E4M3 without saturating.
-    An all-zero tensor uses 2^0."""
+    16-element block scale amax16 / (6 * 2^t) fits E4M3 without saturating;
+    t >= -126, so 2^t is a normal fp32.  An all-zero tensor uses 2^0."""
     a = np.asarray(amax, dtype=np.float64)
     _, ex = np.frexp(np.where(a > 0, a, 1.0))         # a = f * 2^ex, f in [0.5, 1)
     t0 = (ex - 1) - 11                                # 2688 * 2^t0 = 1.3125 * 2^(ex-1)
     t = np.where(a > NV_TENSOR_MAX * np.ldexp(1.0, t0), t0 + 1, t0)
+    t = np.maximum(t, -126)                           # 2^t stays a normal fp32
     return np.where(a > 0, t, 0).astype(np.int64)
 
 

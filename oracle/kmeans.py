@@ -10,8 +10,10 @@ iteration count.  The readings used here (all stated as readings):
   sV = fp32(max|V| / 127), code = clamp(rne(fp32(x / sV)), -127, 127), for both
   tokens and centroids, as D = |c|^2 - 2 v.c in exact integers.  "Lightweight"
   is read as: cheap enough to run inside the attention call.
-* Initial centroids are the value rows at k distinct token indices that the
-  caller supplies (drawn at random by the input generator), or, warm-started
+* Initial centroids are the value rows at k distinct token indices, either
+  supplied by the caller or drawn from a seed (``seeded_init``: a partial
+  Fisher-Yates shuffle of the token indices driven by splitmix64, one stream
+  per head), or, warm-started
   across denoising steps (the pages run the clustering step by step and call
   its cost a scheduling trade), the centroids the previous call ended with.
 * The centroids a call ends with are the member means of its final clusters
@@ -44,9 +46,45 @@ import numpy as np
 from .formats import f32
 
 
+GOLDEN_GAMMA = 0x9E3779B97F4A7C15
+_MASK64 = (1 << 64) - 1
+
+
+def splitmix64(state: int):
+    """The splitmix64 generator (Steele, Lea and Flood, "Fast splittable
+    pseudorandom number generators", OOPSLA 2014): the state advances by the
+    golden-ratio gamma, and each output is the state passed through the
+    variant-13 finaliser.  Yields 64-bit integers."""
+    state &= _MASK64
+    while True:
+        state = (state + GOLDEN_GAMMA) & _MASK64
+        z = state
+        z = ((z ^ (z >> 30)) * 0xBF58476D1CE4E5B9) & _MASK64
+        z = ((z ^ (z >> 27)) * 0x94D049BB133111EB) & _MASK64
+        yield z ^ (z >> 31)
+
+
+def partial_fisher_yates(N: int, k: int, draws) -> np.ndarray:
+    """The first k entries of a Fisher-Yates shuffle of 0..N-1: for
+    i = 0..k-1, j = i + (next draw mod (N - i)), swap entries i and j."""
+    a = list(range(N))
+    for i in range(k):
+        j = i + next(draws) % (N - i)
+        a[i], a[j] = a[j], a[i]
+    return np.array(a[:k], dtype=np.int32)
+
+
+def seeded_init(seed: int, bh: int, N: int, k: int) -> np.ndarray:
+    """k distinct initial token indices of head bh = b*H + h: a partial
+    Fisher-Yates shuffle driven by splitmix64 seeded with
+    seed + 0x9E3779B97F4A7C15 * bh (mod 2^64)."""
+    return partial_fisher_yates(N, k, splitmix64(seed + GOLDEN_GAMMA * bh))
+
+
 def int8_scale(V: np.ndarray) -> float:
+    """sV = fp32(max|V| / 127), floored at 2^-126 (1 if V == 0)."""
     amax = float(np.max(np.abs(V))) if V.size else 0.0
-    return float(f32(amax / 127.0)) if amax > 0 else 1.0
+    return max(float(f32(amax / 127.0)), 2.0 ** -126) if amax > 0 else 1.0
 
 
 def quant_i8(X: np.ndarray, sV: float) -> np.ndarray:

@@ -15,7 +15,8 @@ Readings (the pages leave these open):
   * mean_b = fp32(fp64 mean over the block's real tokens);
     r = fp32(v - mean_b).
   * E4M3 residual scale: one per (head, channel), s_v = fp32(max|r| / 448)
-    over the head's real tokens (1 when the channel's residual is all zero);
+    over the head's real tokens (1 when the channel's residual is all zero;
+    floored at 2^-126, so its reciprocal stays finite);
     code = E4M3(fp32(r / s_v)).  The per-channel scale factors out of P.V.
   * MXFP4 residuals: per 32 consecutive sorted tokens x channel, E8M0 scale
     2^(floor(log2 amax) - 2) and E2M1 elements (OCP MX rule).
@@ -34,7 +35,7 @@ Readings (the pages leave these open):
   * K smoothing (prior art the pages contrast V-Smooth with: "earlier
     low-bit methods ... smoothed queries and keys"): mu_K = fp32(fp64 mean over
     all tokens, per channel); K' = fp32(K - mu_K); per block
-    s_k = fp32(max|K'_blk| / 448); Kq = E4M3(fp32(K' / s_k)).
+    s_k = fp32(max|K'_blk| / 448) (floored at 2^-126); Kq = E4M3(fp32(K' / s_k)).
   * padded tail rows hold code 0.
 
 ``quantize=False`` keeps every value in fp64 with no rounding (for the
@@ -44,6 +45,7 @@ from __future__ import annotations
 
 import numpy as np
 
+from .attention import scale_of
 from .formats import (f32, e4m3_encode, e4m3_decode, e2m1_encode, e2m1_decode, mx_shared_exponent,
                       e4m3_group_exponent, nv_tensor_exponent)
 
@@ -100,7 +102,7 @@ def vsmooth_values(V: np.ndarray, perm: np.ndarray, kv_block: int, fmt: str = "e
         return out
     if fmt == "e4m3":
         amax = np.max(np.abs(r[:N]), axis=0)
-        s_v = np.where(amax > 0, f32(amax / 448.0), 1.0)
+        s_v = np.array([scale_of(float(a), 448.0) for a in amax])
         codes = e4m3_encode(f32(r / s_v[None, :]))
         codes[N:] = 0
         out.update(codes=codes, vres=e4m3_decode(codes), col_scale=s_v, e8m0=None)
@@ -157,7 +159,7 @@ def ksmooth(K: np.ndarray, perm: np.ndarray, kv_block: int, vsmooth: bool = True
     for b in range(nblk):
         lo, hi = b * kv_block, min((b + 1) * kv_block, N)
         amax = np.max(np.abs(Kp[lo:hi]))
-        s = float(f32(amax / 448.0)) if amax > 0 else 1.0
+        s = scale_of(float(amax), 448.0)
         k_scale[b] = s
         codes[lo:hi] = e4m3_encode(f32(Kp[lo:hi] / s))
     return {"mu": mu, "codes": codes, "kdec": e4m3_decode(codes), "k_scale": k_scale}

@@ -194,7 +194,7 @@ def test_exp2cast_is_closer_to_exact_than_expcast():
     assert oracle.psnr(off, ref) > oracle.psnr(on, ref)
 
 
-@pytest.mark.parametrize("mode,window", [("expcast", 6), ("exp2", 9)])
+@pytest.mark.parametrize("mode,window", [("expcast", 6), ("exp2", 9), ("expcast_shifted", 14)])
 def test_integer_log2_scores_give_exact_base2_softmax(mode, window):
     """Closed form for the whole quantised composition (bytes from the FMA,
     decode, online rescaling across blocks, row sums, mean restoration, column
@@ -202,7 +202,9 @@ def test_integer_log2_scores_give_exact_base2_softmax(mode, window):
     `window` of the running maximum, the probability bytes are exactly
     2^(t - m): ExpCast's 8z + 56 + beta rounds to 8z + 56 for |beta| < 0.5 and
     z in [-6, 0], which is the E4M3 code of 2^z; the exp2 path is exact down to
-    the smallest subnormal 2^-9.  The output must then equal the base-2 softmax
+    the smallest subnormal 2^-9; the range-shifted ExpCast's 8z + 120 + beta
+    is the code of 2^(z+8) for z in [-14, 0], and the common 2^8 cancels.
+    The output must then equal the base-2 softmax
     of the scores applied to col_scale * vres + mean, computed here in exact
     rationals from that definition alone."""
     rng = np.random.default_rng(7)
@@ -211,6 +213,8 @@ def test_integer_log2_scores_give_exact_base2_softmax(mode, window):
     n = 5
     # channel 0 carries 448 in one query row (so s_q = 1) and is zero in every key
     Q = rng.integers(-2, 3, size=(n, d)).astype(np.float64)
+    if window > 9:
+        Q = rng.integers(-4, 5, size=(n, d)).astype(np.float64)
     Q[:, 0] = 0.0
     Q[0, 0] = 448.0
     kdec = np.zeros((nblk * kvb, d))
@@ -224,6 +228,8 @@ def test_integer_log2_scores_give_exact_base2_softmax(mode, window):
     assert np.all(S.max(axis=1, keepdims=True) - S <= window)
     assert np.any(S[:, :kvb].max(axis=1) < S.max(axis=1))
     assert np.any((Q @ kdec[N:].T).max(axis=1) >= S.max(axis=1) - 6)
+    if window > 9:                               # the shifted mode reaches further down
+        assert np.any(S.max(axis=1, keepdims=True) - S > 9)
     vres = np.zeros((nblk * kvb, d))
     vres[:N] = rng.integers(-16, 17, size=(N, d)) / 8.0
     vres[N:] = 123.0                             # padded rows must not contribute
@@ -258,3 +264,83 @@ def test_integer_score_inputs_through_the_whole_oracle(mode):
     O = np.concatenate([rows[t] for t in tiles])
     want = base2_softmax(S, V)
     assert np.max(np.abs(O - want)) <= 1e-12 * np.max(np.abs(want))
+
+
+# ---- small pins of the helpers every check uses ----
+
+def test_softmax_scale_default_and_explicit():
+    # 1/sqrt(64) = 0.125 exactly; 1/sqrt(128) = 2^-3 / sqrt(2), whose binary32
+    # pattern is 0x3DB504F3 (the binary32 1/sqrt(2), 0x3F3504F3, three binades
+    # down); an explicit scale is used as its binary32 value
+    assert softmax_scale(64) == 0.125
+    assert np.float32(softmax_scale(128)).view(np.uint32) == 0x3DB504F3
+    assert softmax_scale(64, 0.07) == float(np.float32(0.07))
+
+
+def test_psnr_worked_example():
+    # peak |O_ref| = 4, squared 16; two of four entries off by 0.1, so
+    # MSE = 0.02 / 4 = 0.005 and PSNR = 10 log10(3200) = 35.0515 dB
+    ref = np.array([[1.0, -2.0], [0.0, 4.0]])
+    out = ref + np.array([[0.1, 0.0], [0.0, -0.1]])
+    assert abs(oracle.psnr(out, ref) - 35.05149978) < 1e-6
+    assert oracle.psnr(ref.copy(), ref) == float("inf")
+    # the peak is taken from the reference, not from the output
+    assert abs(oracle.psnr(ref + 10.0, ref) - 10 * np.log10(16 / 100.0)) < 1e-9
+
+
+# ---- the parity bound is tight enough to see a wrong ExpCast offset ----
+
+TIGHT_REL_L2 = 1e-3       # the tighter O bound of the GPU parity tests (fp32 output)
+
+
+def test_beta_and_mode_changes_exceed_the_tight_bound():
+    """A mid-shaped head (N = 4096, d = 128, 64-key blocks): the oracle's O
+    with a different ExpCast offset, or with ExpCast off, moves by more than
+    twice the tight rel-L2 bound the GPU parity tests apply, so a kernel with
+    a wrong beta, a wrong FMA addend or the wrong probability mode fails
+    them."""
+    w = inputs.small(inputs.WORKLOADS["mid"], N=4096, k=64)
+    q, kk, v, init = inputs.gen_head(w, 0, 0)
+    Q, K, V = (oracle.bf16_to_f64(a) for a in (q, kk, v))
+    prep = oracle.prepare_head(K, V, init, 64, 3, 64)
+    tiles = list(range(0, oracle.n_q_tiles(4096), 4))
+
+    def run(beta=oracle.DEFAULT_BETA, mode="expcast"):
+        o = oracle.attend_rows(Q, prep, tiles, 0.0, beta, mode=mode)
+        return np.concatenate([o[t] for t in tiles])
+
+    base = run()
+    for other in (run(beta=0.0), run(beta=0.3), run(mode="exp2"), run(mode="expcast_shifted")):
+        rel = np.linalg.norm(other - base) / np.linalg.norm(base)
+        assert rel > 2 * TIGHT_REL_L2, rel
+
+
+# ---- tiny nonzero inputs: every quantiser scale is floored at 2^-126 ----
+
+def test_scale_floor():
+    from oracle.attention import scale_of
+    assert scale_of(0.0, 448.0) == 1.0
+    assert scale_of(448.0, 448.0) == 1.0
+    assert scale_of(1e-40, 448.0) == 2.0 ** -126          # would be subnormal
+    assert scale_of(448.0 * 2.0 ** -126, 448.0) == 2.0 ** -126
+    assert scale_of(448.0 * 2.0 ** -125, 448.0) == 2.0 ** -125
+
+
+def test_tiny_value_channel_keeps_a_finite_scale():
+    # one channel of V holds values near 1e-37 (normal fp32, but max/448 is
+    # subnormal): its residual scale is floored at 2^-126, its codes stay
+    # finite, and O for that channel matches exact attention to the
+    # quantisation error of the other channels, relative to the channel
+    w, Q, K, V, init = _head(512, 64, 64)
+    rng = np.random.default_rng(9)
+    V = V.copy()
+    V[:, 5] = F.f32(rng.standard_normal(512) * 1e-37)
+    V[:, 5] = np.asarray(V[:, 5], np.float32).astype(np.float64)
+    prep = oracle.prepare_head(K, V, init, w.k, w.iters, 64)
+    assert prep["v"]["col_scale"][5] == 2.0 ** -126
+    O = _all_rows(Q, prep)
+    assert np.all(np.isfinite(O))
+    ref = exact_attention(Q, K, V, softmax_scale(64))
+    rel5 = np.linalg.norm(O[:, 5] - ref[:, 5]) / np.linalg.norm(ref[:, 5])
+    rel_all = np.linalg.norm(O - ref) / np.linalg.norm(ref)
+    assert rel5 < 0.2 and rel_all < 0.2

@@ -72,3 +72,50 @@ def test_monotone_and_clamped():
     S = np.array([10.0, -np.inf, np.nan, -1e30], np.float64)
     out = expcast_bytes(S, 8.0, np.full(4, 56.0))
     assert list(out) == [56, 0, 0, 0]
+
+
+# ---- range-shifted ExpCast: the same FMA with the addend 120 + beta ----
+
+def shifted_bytes_for_z(z, beta=DEFAULT_BETA):
+    z = np.asarray(z, np.float32)
+    B = np.float32(F.f32(120.0 + beta))
+    return expcast_bytes(z.astype(np.float64), 8.0, np.full(z.shape, B, np.float64), 120.0)
+
+
+def test_shifted_bytes_are_exact_powers_down_to_z_minus_14():
+    # byte 8z + 120 has exponent field z + 15 and mantissa 0: the E4M3 value
+    # 2^(z+8), normal for z >= -14 (torch's float8 cast gives the same code)
+    z = np.arange(-14, 1)
+    for beta in (DEFAULT_BETA, 0.0, -0.49, 0.3):
+        got = shifted_bytes_for_z(z.astype(np.float32), beta).astype(np.int64)
+        assert list(got) == list(8 * z + 120)
+    assert list(exact_e4m3_of_exp2(z + 8)) == list(8 * z + 120)
+    assert np.array_equal(F.e4m3_decode(8 * z + 120), np.exp2(z + 8.0))
+    # the literal mode loses these below z = -6
+    assert list(bytes_for_z(np.float32([-7, -10, -14]))) == [0, 0, 0]
+
+
+def test_shifted_is_literal_plus_64_codes_in_the_normal_range():
+    # on z in [-6, 0] the two FMAs differ by 64 before rounding, so the bytes
+    # differ by 64 except where x lies within an fp32 ulp (2^-17 above 64) of
+    # a rounding midpoint; no point of this grid (step 2^-12) does
+    z = -np.arange(0, 6 * 4096 + 1, dtype=np.float64) / 4096.0
+    lit = bytes_for_z(z).astype(np.int64)
+    sh = shifted_bytes_for_z(z).astype(np.int64)
+    ok = lit > 0
+    assert np.array_equal(sh[ok], lit[ok] + 64)
+
+
+def test_shifted_dense_grid_against_exact_exp2_cast():
+    # against the exact E4M3 byte of 2^(z+8): within one code for z >= -14
+    z = -np.arange(0, 14 * 4096 + 1, dtype=np.float64) / 4096.0
+    got = shifted_bytes_for_z(z).astype(np.int64)
+    ref = exact_e4m3_of_exp2(z + 8.0)
+    assert np.abs(got - ref).max() == 1
+    assert got.max() <= 120 and got.min() >= 8
+
+
+def test_shifted_clamps_at_120():
+    S = np.array([10.0, -np.inf, np.nan, -1e30, 0.0], np.float64)
+    out = expcast_bytes(S, 8.0, np.full(5, 120.0), 120.0)
+    assert list(out) == [120, 0, 0, 0, 120]

@@ -5,6 +5,7 @@ import itertools
 from fractions import Fraction
 
 import numpy as np
+import pytest
 
 from oracle import kmeans as KM
 from oracle import vsmooth as VS
@@ -429,3 +430,49 @@ def test_ordered_kmeans_renumbers_the_unordered_result():
     perm1 = oracle.prepare_head(oracle.bf16_to_f64(k[0, 0]), V, init[0, 0], w.k, w.iters, w.kv_block,
                                 cluster_order=True)["perm"]
     assert np.all(np.diff(lab1[perm1]) >= 0)
+
+
+# ---- seeded initialisation: splitmix64 + partial Fisher-Yates ----
+
+def test_splitmix64_published_outputs():
+    # reference outputs of splitmix64 (Steele, Lea and Flood 2014; the
+    # generator's published test values from state 0 and state 1234567)
+    from oracle.kmeans import splitmix64
+    g = splitmix64(0)
+    assert [next(g) for _ in range(3)] == [0xE220A8397B1DCDAF, 0x6E789E6AA1B965F4, 0x06C45D188009454F]
+    assert next(splitmix64(1234567)) == 0x599ED017FB08FC85
+
+
+def test_partial_fisher_yates_worked_example():
+    # N = 5, k = 3 with draws 7, 2, 9 (worked by hand):
+    #   i = 0: j = 0 + 7 mod 5 = 2 -> [2, 1, 0, 3, 4]
+    #   i = 1: j = 1 + 2 mod 4 = 3 -> [2, 3, 0, 1, 4]
+    #   i = 2: j = 2 + 9 mod 3 = 2 -> unchanged; result [2, 3, 0]
+    from oracle.kmeans import partial_fisher_yates
+    assert partial_fisher_yates(5, 3, iter([7, 2, 9])).tolist() == [2, 3, 0]
+    # k = N is a whole permutation; a zero draw never moves anything
+    assert partial_fisher_yates(4, 4, iter([0, 0, 0, 0])).tolist() == [0, 1, 2, 3]
+
+
+@pytest.mark.parametrize("N,k", [(1024, 16), (4096, 4096), (75600, 1024), (7, 7), (1, 1)])
+def test_seeded_init_draws_distinct_tokens(N, k):
+    from oracle.kmeans import seeded_init
+    a = seeded_init(1002, 0, N, k)
+    b = seeded_init(1002, 1, N, k)
+    assert a.dtype == np.int32 and a.shape == (k,)
+    assert np.unique(a).size == k and a.min() >= 0 and a.max() < N
+    if k == N:
+        assert np.array_equal(np.sort(a), np.arange(N))
+    if k > 4:
+        assert not np.array_equal(a, b)          # every head has its own stream
+    assert np.array_equal(a, seeded_init(1002, 0, N, k))
+
+
+def test_seeded_init_is_uniform_over_tokens():
+    # every token is equally likely to be drawn: over 2000 heads with N = 20,
+    # k = 5, each token is drawn ~500 times (binomial sd ~19)
+    from oracle.kmeans import seeded_init
+    cnt = np.zeros(20)
+    for bh in range(2000):
+        cnt[seeded_init(7, bh, 20, 5)] += 1
+    assert np.all(np.abs(cnt - 500) < 100)
