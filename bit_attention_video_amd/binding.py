@@ -22,7 +22,8 @@ LIB_PATH = os.environ.get("VCATTN_LIBRARY") or os.path.join(_HERE, "libvcattn.so
 DEFAULT_BETA = 8.0 / math.log(2.0) - 12.0
 
 E4M3, MXFP4, MXFP8, NVFP4 = 0, 1, 2, 3    # residual formats (NVFP4: 16-token E4M3 scales, emulated)
-EXPCAST, EXP2_CAST = 0, 1      # p_mode: ExpCast-FP8 bytes, or exp2 then E4M3 cast
+# p_mode: ExpCast-FP8 bytes; exp2 then E4M3 cast (ExpCast off); ExpCast moved up by 64 codes
+EXPCAST, EXP2_CAST, EXPCAST_SHIFTED = 0, 1, 2
 
 
 class VcConfig(ctypes.Structure):
@@ -30,7 +31,7 @@ class VcConfig(ctypes.Structure):
                 ("kv_block", ctypes.c_int32), ("n_clusters", ctypes.c_int32), ("iters", ctypes.c_int32),
                 ("vsmooth", ctypes.c_int32), ("v_format", ctypes.c_int32), ("out_fp32", ctypes.c_int32),
                 ("softmax_scale", ctypes.c_float), ("beta", ctypes.c_float), ("p_mode", ctypes.c_int32),
-                ("cluster_order", ctypes.c_int32)]
+                ("cluster_order", ctypes.c_int32), ("seed", ctypes.c_uint64)]
 
 
 _lib = None
@@ -69,6 +70,11 @@ def lib() -> ctypes.CDLL:
         L.vc_dbg_kmeans_assign.restype = ctypes.c_int
         L.vc_dbg_sort.argtypes = [cfgp, _P, _P, _P, ctypes.c_size_t, _P]
         L.vc_dbg_sort.restype = ctypes.c_int
+        L.vc_dbg_attn_trace.argtypes = [cfgp, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int32, ctypes.c_int32, _P, _P,
+                                        _P, _P, _P, _P]
+        L.vc_dbg_attn_trace.restype = ctypes.c_int
+        L.vc_dbg_init_tokens.argtypes = [cfgp, _P, _P]
+        L.vc_dbg_init_tokens.restype = ctypes.c_int
         L.vc_mfma_loop.argtypes = [ctypes.c_int32, ctypes.c_int32, _P, _P]
         L.vc_mfma_loop.restype = ctypes.c_int
         _lib = L
@@ -90,9 +96,10 @@ def _check(status: int, what: str):
 def make_config(B: int, H: int, N: int, d: int, kv_block: int, n_clusters: int = 1, iters: int = 1,
                 vsmooth: bool = True, v_format: int = E4M3, out_fp32: bool = False,
                 softmax_scale: float = 0.0, beta: float = DEFAULT_BETA, p_mode: int = EXPCAST,
-                cluster_order: bool = False) -> VcConfig:
+                cluster_order: bool = False, seed: int = 0) -> VcConfig:
     return VcConfig(B, H, N, d, kv_block, n_clusters, iters, int(bool(vsmooth)), int(v_format),
-                    int(bool(out_fp32)), softmax_scale, beta, int(p_mode), int(bool(cluster_order)))
+                    int(bool(out_fp32)), softmax_scale, beta, int(p_mode), int(bool(cluster_order)),
+                    int(seed) & (2 ** 64 - 1))
 
 
 def _stream():
@@ -172,11 +179,13 @@ def _check_prepared(cfg: VcConfig, prep: Prepared):
 
 
 def _workspace(ws: torch.Tensor | None, nbytes: int, device) -> torch.Tensor:
-    if ws is not None:
-        _need(ws, torch.uint8, (ws.numel(),), "ws")
-        if ws.numel() >= nbytes:
-            return ws
-    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+    """The caller's workspace, checked; a new one only when none is given."""
+    if ws is None:
+        return torch.empty(nbytes, dtype=torch.uint8, device=device)
+    _need(ws, torch.uint8, (ws.numel(),), "ws")
+    if ws.numel() < nbytes:
+        raise ValueError(f"ws holds {ws.numel()} bytes; this configuration needs {nbytes}")
+    return ws
 
 
 def vsmooth_prepare(cfg: VcConfig, K: torch.Tensor, V: torch.Tensor, init_idx: torch.Tensor | None,
@@ -185,7 +194,7 @@ def vsmooth_prepare(cfg: VcConfig, K: torch.Tensor, V: torch.Tensor, init_idx: t
     shp = (cfg.B, cfg.H, cfg.N, cfg.d)
     _need(K, torch.bfloat16, shp, "K")
     _need(V, torch.bfloat16, shp, "V")
-    if cfg.vsmooth:
+    if cfg.vsmooth and init_idx is not None:
         _need(init_idx, torch.int32, (cfg.B, cfg.H, cfg.n_clusters), "init_idx")
     if out is None:
         out = alloc_prepared(cfg, K.device, with_labels)
@@ -204,8 +213,9 @@ def vsmooth_prepare_warm(cfg: VcConfig, K: torch.Tensor, V: torch.Tensor, *,
                          perm_in: torch.Tensor | None = None, centroids_out: torch.Tensor | None = None,
                          out: Prepared | None = None, ws: torch.Tensor | None = None,
                          with_labels: bool = True) -> Prepared:
-    """vsmooth_prepare carried across calls (include/vcattn.h): exactly one of
-    init_idx (cold start), init_centroids (warm start) or perm_in (reuse)."""
+    """vsmooth_prepare carried across calls (include/vcattn.h): at most one of
+    init_idx (cold start), init_centroids (warm start) or perm_in (reuse);
+    none is a cold start from cfg.seed."""
     shp = (cfg.B, cfg.H, cfg.N, cfg.d)
     _need(K, torch.bfloat16, shp, "K")
     _need(V, torch.bfloat16, shp, "V")
@@ -254,11 +264,13 @@ def vc_attn_fwd(cfg: VcConfig, Q: torch.Tensor, prep: Prepared, out: torch.Tenso
     return out
 
 
-def vc_attention(cfg: VcConfig, Q, K, V, init_idx, out=None, ws=None) -> torch.Tensor:
+def vc_attention(cfg: VcConfig, Q, K, V, init_idx=None, out=None, ws=None) -> torch.Tensor:
+    """(Q, K, V) -> O with the clustering inside the call; init_idx None draws
+    the k-means start from cfg.seed."""
     shp = (cfg.B, cfg.H, cfg.N, cfg.d)
     for t, n in ((Q, "Q"), (K, "K"), (V, "V")):
         _need(t, torch.bfloat16, shp, n)
-    if cfg.vsmooth:
+    if cfg.vsmooth and init_idx is not None:
         _need(init_idx, torch.int32, (cfg.B, cfg.H, cfg.n_clusters), "init_idx")
     out = _output(cfg, out, Q.device)
     ws = _workspace(ws, workspace_bytes(cfg, attention=True), Q.device)
@@ -266,6 +278,29 @@ def vc_attention(cfg: VcConfig, Q, K, V, init_idx, out=None, ws=None) -> torch.T
                               _ptr(init_idx) if cfg.vsmooth else None, _ptr(out), _ptr(ws), ws.numel(),
                               _stream()), "vc_attention")
     return out
+
+
+TRACE_ROWS = 256     # query rows of one attention workgroup (one traced group)
+
+
+def dbg_attn_trace(cfg: VcConfig, Q: torch.Tensor, prep: Prepared, bh: int, q_group: int,
+                   out: torch.Tensor | None = None) -> tuple[torch.Tensor, dict]:
+    """vc_attn_fwd through the trace instantiation (include/vcattn.h): returns
+    O and the traced workgroup's per-block records S, P, m, c, rowsum."""
+    _need(Q, torch.bfloat16, (cfg.B, cfg.H, cfg.N, cfg.d), "Q")
+    _check_prepared(cfg, prep)
+    out = _output(cfg, out, Q.device)
+    nblk, R, kvb = _nblk(cfg), TRACE_ROWS, cfg.kv_block
+    tr = dict(S=torch.empty((nblk, R, kvb), dtype=torch.float32, device=Q.device),
+              P=torch.empty((nblk, R, kvb), dtype=torch.uint8, device=Q.device),
+              m=torch.empty((nblk, R), dtype=torch.float32, device=Q.device),
+              c=torch.empty((nblk, R), dtype=torch.float32, device=Q.device),
+              rowsum=torch.empty((nblk, R), dtype=torch.float32, device=Q.device))
+    _check(lib().vc_dbg_attn_trace(ctypes.byref(cfg), _ptr(Q), _ptr(prep.Kq), _ptr(prep.k_scale), _ptr(prep.Vres),
+                                   _ptr(prep.v_scale), _ptr(prep.v_mean), _ptr(out), int(bh), int(q_group),
+                                   _ptr(tr["S"]), _ptr(tr["P"]), _ptr(tr["m"]), _ptr(tr["c"]), _ptr(tr["rowsum"]),
+                                   _stream()), "vc_dbg_attn_trace")
+    return out, tr
 
 
 def dbg_expcast(S: torch.Tensor, A: torch.Tensor, B: torch.Tensor) -> torch.Tensor:
@@ -294,6 +329,13 @@ def dbg_kmeans_assign(cfg: VcConfig, V: torch.Tensor, C: torch.Tensor) -> torch.
     _check(lib().vc_dbg_kmeans_assign(ctypes.byref(cfg), _ptr(V), _ptr(C), _ptr(labels), _ptr(ws), ws.numel(),
                                       _stream()), "vc_dbg_kmeans_assign")
     return labels
+
+
+def dbg_init_tokens(cfg: VcConfig, device="cuda") -> torch.Tensor:
+    """The k-means initial token indices drawn from cfg.seed, int32 [B,H,k]."""
+    out = torch.empty((cfg.B, cfg.H, cfg.n_clusters), dtype=torch.int32, device=device)
+    _check(lib().vc_dbg_init_tokens(ctypes.byref(cfg), _ptr(out), _stream()), "vc_dbg_init_tokens")
+    return out
 
 
 def dbg_sort(cfg: VcConfig, labels: torch.Tensor) -> torch.Tensor:

@@ -25,6 +25,8 @@ vc_status hip_fail(hipError_t e, const char* where) {
 
 bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
 
+constexpr int kTraceRows = 256;   // query rows per attention workgroup (one traced group)
+
 struct Dims {
   int B, H, N, d, kvb, k, kpad, iters, nblk, nstat, nsort;
   size_t BH;
@@ -48,7 +50,8 @@ vc_status validate(const vc_config* c, bool need_kmeans, Dims* out) {
   if (!(std::isfinite(c->softmax_scale) && c->softmax_scale >= 0.0f))
     return fail(VC_ERR_INVALID_ARG, "softmax_scale must be finite and >= 0");
   if (!(c->beta >= -0.5f && c->beta <= 0.45f)) return fail(VC_ERR_INVALID_ARG, "beta must lie in [-0.5, 0.45]");
-  if (c->p_mode != 0 && c->p_mode != 1) return fail(VC_ERR_UNSUPPORTED, "p_mode must be 0 (ExpCast) or 1 (exp2 + cast)");
+  if (c->p_mode < 0 || c->p_mode > 2)
+    return fail(VC_ERR_UNSUPPORTED, "p_mode must be 0 (ExpCast), 1 (exp2 + cast) or 2 (range-shifted ExpCast)");
   if (c->cluster_order != 0 && c->cluster_order != 1)
     return fail(VC_ERR_UNSUPPORTED, "cluster_order must be 0 (label order) or 1 (principal-axis order)");
   if (need_kmeans) {
@@ -101,6 +104,7 @@ void carve_prep(Carver& cv, const Dims& D, vc::PrepArgs& a) {
   a.starts = cv.take<int32_t>(BH * D.k);
   a.rank = cv.take<int32_t>(BH * D.k);
   a.Ctmp = cv.take<float>(BH * D.k * D.d);
+  a.init = cv.take<int32_t>(BH * D.k);
 }
 
 struct OutSizes {
@@ -151,8 +155,13 @@ vc_status run_prepare(const vc_config* c, const Dims& D, vc::PrepArgs& a, const 
     if (init_centroids)
       VC_TRY(hipMemcpyAsync(a.C, init_centroids, D.BH * D.k * D.d * sizeof(float), hipMemcpyDeviceToDevice, st),
              "copy centroids");
-    else
+    else {
+      if (!init) {
+        VC_TRY(vc::launch_init_seeded(a, c->seed, a.init, st), "init_seeded");
+        init = a.init;
+      }
       VC_TRY(vc::launch_init_centroids(a, init, st), "init_centroids");
+    }
     for (int it = 0; it < D.iters; ++it) {
       const bool last = it + 1 == D.iters;
       int32_t* lab = (last && user_labels) ? user_labels : a.labels;
@@ -182,8 +191,11 @@ void fill_attn_args(const vc_config* c, const Dims& D, vc::AttnArgs& a) {
   a.v_format = c->v_format; a.out_fp32 = c->out_fp32;
   a.scale = c->softmax_scale == 0.0f ? static_cast<float>(1.0 / std::sqrt(static_cast<double>(D.d)))
                                      : c->softmax_scale;
-  a.kc = 56.0f + c->beta;
-  a.p_mode = c->p_mode;
+  // ExpCast's addend: 56 + beta puts p = 1 at E4M3 byte 56 (1.0); the
+  // range-shifted mode adds 64 codes (p = 1 at byte 120 = 2^8), so the bytes
+  // stay normal E4M3 down to p = 2^-14 (the common factor 2^8 cancels in O)
+  a.kc = (c->p_mode == 2 ? 120.0f : 56.0f) + c->beta;
+  a.pm = c->p_mode == 1 ? 1 : 0;
 }
 
 }  // namespace
@@ -236,7 +248,6 @@ vc_status vsmooth_prepare(const vc_config* cfg, const void* K, const void* V, co
   if (vc_status s = validate(cfg, cfg && cfg->vsmooth, &D)) return s;
   if (!K || !V || !Kq || !k_scale || !Vres || !v_scale || !v_mean || !perm || !ws)
     return fail(VC_ERR_INVALID_ARG, "required pointer is NULL");
-  if (cfg->vsmooth && !init_idx) return fail(VC_ERR_INVALID_ARG, "init_idx is NULL with vsmooth on");
   if (misaligned(K) || misaligned(V) || misaligned(Kq) || misaligned(Vres) || misaligned(v_scale) ||
       misaligned(v_mean) || misaligned(ws))
     return fail(VC_ERR_INVALID_ARG, "tensors and workspace must be 16-byte aligned");
@@ -259,8 +270,8 @@ vc_status vsmooth_prepare_warm(const vc_config* cfg, const void* K, const void* 
   if (!cfg->vsmooth) return fail(VC_ERR_INVALID_ARG, "vsmooth_prepare_warm needs vsmooth on");
   if (!K || !V || !Kq || !k_scale || !Vres || !v_scale || !v_mean || !perm || !ws)
     return fail(VC_ERR_INVALID_ARG, "required pointer is NULL");
-  if ((init_idx != nullptr) + (init_centroids != nullptr) + (perm_in != nullptr) != 1)
-    return fail(VC_ERR_INVALID_ARG, "exactly one of init_idx, init_centroids, perm_in must be given");
+  if ((init_idx != nullptr) + (init_centroids != nullptr) + (perm_in != nullptr) > 1)
+    return fail(VC_ERR_INVALID_ARG, "at most one of init_idx, init_centroids, perm_in may be given");
   if (misaligned(K) || misaligned(V) || misaligned(Kq) || misaligned(Vres) || misaligned(v_scale) ||
       misaligned(v_mean) || misaligned(ws))
     return fail(VC_ERR_INVALID_ARG, "tensors and workspace must be 16-byte aligned");
@@ -293,13 +304,39 @@ vc_status vc_attn_fwd(const vc_config* cfg, const void* Q, const uint8_t* Kq, co
   return VC_OK;
 }
 
+vc_status vc_dbg_attn_trace(const vc_config* cfg, const void* Q, const uint8_t* Kq, const float* k_scale,
+                            const uint8_t* Vres, const void* v_scale, const float* v_mean, void* O, int32_t bh,
+                            int32_t q_group, float* S, uint8_t* P, float* m, float* c, float* rowsum,
+                            hipStream_t stream) {
+  g_err.clear();
+  Dims D;
+  if (vc_status s = validate(cfg, false, &D)) return s;
+  if (!cfg->out_fp32) return fail(VC_ERR_UNSUPPORTED, "the trace runs with fp32 output only (out_fp32 = 1)");
+  if (cfg->v_format > 1) return fail(VC_ERR_UNSUPPORTED, "the trace runs with E4M3 or MXFP4 residuals only");
+  if (!Q || !Kq || !k_scale || !Vres || !v_scale || !v_mean || !O || !S || !P || !m || !c || !rowsum)
+    return fail(VC_ERR_INVALID_ARG, "required pointer is NULL");
+  if (misaligned(Q) || misaligned(Kq) || misaligned(Vres) || misaligned(v_scale) || misaligned(v_mean) ||
+      misaligned(O) || misaligned(S) || misaligned(P))
+    return fail(VC_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
+  const int groups = (D.N + kTraceRows - 1) / kTraceRows;
+  if (bh < 0 || static_cast<size_t>(bh) >= D.BH || q_group < 0 || q_group >= groups)
+    return fail(VC_ERR_INVALID_ARG, "bh or q_group out of range");
+  vc::AttnArgs a{};
+  fill_attn_args(cfg, D, a);
+  a.Q = static_cast<const uint16_t*>(Q);
+  a.Kq = Kq; a.k_scale = k_scale; a.Vres = Vres; a.v_scale = v_scale; a.v_mean = v_mean; a.O = O;
+  a.tr_wg = bh * groups + q_group;
+  a.tr_S = S; a.tr_P = P; a.tr_m = m; a.tr_c = c; a.tr_l = rowsum;
+  VC_TRY(vc::launch_attn(a, stream), "attn_fwd trace");
+  return VC_OK;
+}
+
 vc_status vc_attention(const vc_config* cfg, const void* Q, const void* K, const void* V,
                        const int32_t* init_idx, void* O, void* ws, size_t ws_bytes, hipStream_t stream) {
   g_err.clear();
   Dims D;
   if (vc_status s = validate(cfg, cfg && cfg->vsmooth, &D)) return s;
   if (!Q || !K || !V || !O || !ws) return fail(VC_ERR_INVALID_ARG, "required pointer is NULL");
-  if (cfg->vsmooth && !init_idx) return fail(VC_ERR_INVALID_ARG, "init_idx is NULL with vsmooth on");
   if (misaligned(Q) || misaligned(K) || misaligned(V) || misaligned(O) || misaligned(ws))
     return fail(VC_ERR_INVALID_ARG, "tensors and workspace must be 16-byte aligned");
   if (ws_bytes < vc_attention_workspace_bytes(cfg)) return fail(VC_ERR_WORKSPACE, "workspace too small");
@@ -369,6 +406,17 @@ vc_status vc_dbg_kmeans_assign(const vc_config* cfg, const void* V, const float*
   VC_TRY(vc::launch_stats(a, stream), "stats");
   VC_TRY(vc::launch_quant_v_i8(a, stream), "quant_v_i8");
   VC_TRY(vc::launch_assign(a, labels, stream), "kmeans_assign");
+  return VC_OK;
+}
+
+vc_status vc_dbg_init_tokens(const vc_config* cfg, int32_t* init, hipStream_t stream) {
+  g_err.clear();
+  Dims D;
+  if (vc_status s = validate(cfg, true, &D)) return s;
+  if (!init) return fail(VC_ERR_INVALID_ARG, "init is NULL");
+  vc::PrepArgs a{};
+  fill_prep_args(cfg, D, nullptr, nullptr, a);
+  VC_TRY(vc::launch_init_seeded(a, cfg->seed, init, stream), "init_seeded");
   return VC_OK;
 }
 

@@ -68,7 +68,8 @@ __global__ __launch_bounds__(256) void k_stats_partial(const uint16_t* __restric
   }
 }
 
-// mu_K = fp32(sum / N) per channel; sV = fp32(max|V| / 127) (1 if V == 0).
+// mu_K = fp32(sum / N) per channel; sV = fp32(max|V| / 127) floored at 2^-126
+// (1 if V == 0).
 template <int D>
 __global__ void k_stats_final(const double* __restrict__ kpart, const uint32_t* __restrict__ vamax,
                               int N, int nch, float* __restrict__ mu, float* __restrict__ sV) {
@@ -78,7 +79,7 @@ __global__ void k_stats_final(const double* __restrict__ kpart, const uint32_t* 
   mu[static_cast<size_t>(bh) * D + c] = static_cast<float>(s / static_cast<double>(N));
   if (c == 0) {
     const float a = __uint_as_float(vamax[bh]);
-    sV[bh] = a > 0.0f ? a / 127.0f : 1.0f;
+    sV[bh] = a > 0.0f ? fmaxf(a / 127.0f, kScaleFloor) : 1.0f;
   }
 }
 
@@ -101,6 +102,62 @@ __global__ void k_quant_v_i8(const uint16_t* __restrict__ V, const float* __rest
   *reinterpret_cast<uint2*>(Vq + i8) = make_uint2(out[0], out[1]);
 }
 
+// ---- seeded initial centroids --------------------------------------------------
+// The k initial tokens of head bh are a partial Fisher-Yates shuffle of 0..N-1
+// driven by splitmix64 (Steele, Lea and Flood, "Fast splittable pseudorandom
+// number generators", 2014) seeded with seed + 0x9E3779B97F4A7C15 * bh: draw
+// r_i (i = 0..k-1), j_i = i + r_i mod (N - i), swap positions i and j_i; the
+// first k positions are the result.  The swaps are resolved in parallel: the
+// value at position i just before step i is v(i) = v(i'') for the last earlier
+// step i'' with j_i'' = i (i itself if none), and the value step i takes is
+// v(i') for the last earlier step i' with j_i' = j_i (j_i itself if none;
+// j_i = i gives v(i)).  One workgroup per head; k <= kMaxClusters.
+constexpr int kInitThreads = 1024;
+
+__device__ __forceinline__ uint64_t splitmix64_at(uint64_t seed, uint64_t i) {
+  // output i (from 0) of the generator started at state `seed`
+  uint64_t z = seed + (i + 1) * 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+__global__ __launch_bounds__(kInitThreads) void k_init_seeded(uint64_t seed, int N, int k,
+                                                              int32_t* __restrict__ init) {
+  __shared__ int32_t sJ[kMaxClusters];
+  __shared__ int32_t sPrev[kMaxClusters];    // last earlier step whose j is this step's position i
+  __shared__ int32_t sSame[kMaxClusters];    // last earlier step with the same j
+  __shared__ int32_t sV[kMaxClusters];       // value at position i just before step i
+  const int bh = blockIdx.x;
+  const uint64_t hs = seed + 0x9E3779B97F4A7C15ull * static_cast<uint64_t>(bh);
+  for (int i = threadIdx.x; i < k; i += kInitThreads)
+    sJ[i] = i + static_cast<int>(splitmix64_at(hs, static_cast<uint64_t>(i)) % static_cast<uint64_t>(N - i));
+  __syncthreads();
+  for (int i = threadIdx.x; i < k; i += kInitThreads) {
+    const int ji = sJ[i];
+    int prev = -1, same = -1;
+    for (int t = 0; t < i; ++t) {
+      const int jt = sJ[t];
+      prev = jt == i ? t : prev;
+      same = jt == ji ? t : same;
+    }
+    sPrev[i] = prev;
+    sSame[i] = same;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < k; i += kInitThreads) {
+    int t = i;
+    while (sPrev[t] >= 0) t = sPrev[t];     // strictly decreasing chain
+    sV[i] = t;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < k; i += kInitThreads) {
+    const int ji = sJ[i];
+    const int val = ji == i ? sV[i] : (sSame[i] >= 0 ? sV[sSame[i]] : ji);
+    init[static_cast<size_t>(bh) * k + i] = val;
+  }
+}
+
 template <int D>
 __global__ void k_init_centroids(const uint16_t* __restrict__ V, const int32_t* __restrict__ init,
                                  int N, int k, float* __restrict__ C) {
@@ -111,7 +168,7 @@ __global__ void k_init_centroids(const uint16_t* __restrict__ V, const int32_t* 
 }
 
 // int8 centroid codes and the packed score offsets cn32 = (31 - row % 32) - 32*|c|^2;
-// rows k..kpad-1 are padding (codes 0, offset INT_MAX: never the minimum).
+// rows k..kpad-1 are padding (codes 0, offset INT_MIN: their key is never the maximum).
 template <int D>
 __global__ __launch_bounds__(256) void k_quant_centroids(const float* __restrict__ C,
                                                          const float* __restrict__ sV, int k,
@@ -275,7 +332,7 @@ __global__ __launch_bounds__(1024) void k_sort_scan(int32_t* __restrict__ hist, 
   part[threadIdx.x] = mysum;
   __syncthreads();
   for (int o = 1; o < 1024; o <<= 1) {         // inclusive Hillis-Steele scan
-    const int v = threadIdx.x >= o ? part[threadIdx.x - o] : 0;
+    const int v = static_cast<int>(threadIdx.x) >= o ? part[threadIdx.x - o] : 0;
     __syncthreads();
     part[threadIdx.x] += v;
     __syncthreads();
@@ -487,7 +544,7 @@ __global__ __launch_bounds__(256) void k_vres_e4m3(const uint16_t* __restrict__ 
   const int cg = threadIdx.x % BR::CG, q = threadIdx.x / BR::CG;
   if (threadIdx.x < D) {
     const float am = __uint_as_float(vramax[static_cast<size_t>(bh) * D + threadIdx.x]);
-    const float sc = am > 0.0f ? am / 448.0f : 1.0f;
+    const float sc = am > 0.0f ? fmaxf(am / 448.0f, kScaleFloor) : 1.0f;
     sS[threadIdx.x] = sc;
     sY[threadIdx.x] = 1.0f / sc;
     sMean[threadIdx.x] = v_mean[(static_cast<size_t>(bh) * nblk + b) * D + threadIdx.x];
@@ -580,6 +637,7 @@ __global__ __launch_bounds__(256) void k_vres_mx(const uint16_t* __restrict__ V,
           frexpf(m, &fe);                  // m = f * 2^fe, f in [0.5, 1); 2688 * 2^(fe-12) = 1.3125 * 2^(fe-1)
           t = fe - 12;
           if (m > ldexpf(2688.0f, t)) ++t;
+          t = max(t, -126);   // 2^t stays a normal fp32
         }
         sTx = t;
       }
@@ -754,7 +812,7 @@ __global__ __launch_bounds__(256) void k_ksmooth(const uint16_t* __restrict__ K,
   if ((threadIdx.x & 63) == 0) sMax[threadIdx.x >> 6] = am;
   __syncthreads();
   const float bm = fmaxf(fmaxf(sMax[0], sMax[1]), fmaxf(sMax[2], sMax[3]));
-  const float s = bm > 0.0f ? bm / 448.0f : 1.0f;
+  const float s = bm > 0.0f ? fmaxf(bm / 448.0f, kScaleFloor) : 1.0f;
   const float y = 1.0f / s;
   if (threadIdx.x == 0) k_scale[static_cast<size_t>(bh) * nblk + b] = s;
   uint8_t* dst = Kq + (static_cast<size_t>(bh) * nblk * KVB + p0) * D + cg * 8;
@@ -965,6 +1023,11 @@ static hipError_t init_t(const PrepArgs& a, const int32_t* init, hipStream_t st)
   hipLaunchKernelGGL(k_init_centroids<D>, dim3(a.k, a.B * a.H), dim3(D), 0, st, a.V, init, a.N, a.k, a.C);
   return hipGetLastError();
 }
+hipError_t launch_init_seeded(const PrepArgs& a, uint64_t seed, int32_t* init, hipStream_t st) {
+  hipLaunchKernelGGL(k_init_seeded, dim3(a.B * a.H), dim3(kInitThreads), 0, st, seed, a.N, a.k, init);
+  return hipGetLastError();
+}
+
 hipError_t launch_init_centroids(const PrepArgs& a, const int32_t* init, hipStream_t st) {
   return a.d == 64 ? init_t<64>(a, init, st) : init_t<128>(a, init, st);
 }

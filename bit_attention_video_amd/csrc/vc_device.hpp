@@ -13,6 +13,10 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v2f __attribute__((ext_vector_type(2)));
 
 constexpr int kQTile = 128;          // query rows per tile (one scale per tile)
+// Smallest quantiser scale (the smallest normal fp32, 2^-126): amax / 448 or
+// amax / 127 is floored here so that the reciprocal every quantiser uses
+// stays finite for tiny nonzero inputs.
+constexpr float kScaleFloor = 0x1p-126f;
 constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {

@@ -32,6 +32,7 @@ struct PrepArgs {
   uint32_t* vramax;    // [BH,d]     residual channel max bits
   int32_t* rank;       // [BH,k]     cluster order (renumbering before the final pass)
   float* Ctmp;         // [BH,k,d]   renumbered centroids
+  int32_t* init;       // [BH,k]     seeded initial token indices
 };
 
 struct PrepOut {
@@ -44,8 +45,9 @@ struct PrepOut {
 };
 
 struct AttnArgs {
-  int B, H, N, d, kvb, nblk, v_format, out_fp32, p_mode;
-  float scale, kc;     // softmax scale, fp32(56 + beta)
+  int B, H, N, d, kvb, nblk, v_format, out_fp32;
+  int pm;              // kernel probability mode: 0 ExpCast (byte from one FMA), 1 exp2 + E4M3 cast
+  float scale, kc;     // softmax scale; ExpCast addend fp32(56 + beta), or fp32(120 + beta) range-shifted
   const uint16_t* Q;
   const uint8_t* Kq;
   const float* k_scale;
@@ -53,11 +55,19 @@ struct AttnArgs {
   const void* v_scale;
   const float* v_mean;
   void* O;
+  // test-only trace of one workgroup (tr_S null: the production kernels)
+  int tr_wg;
+  float* tr_S;
+  uint8_t* tr_P;
+  float* tr_m;
+  float* tr_c;
+  float* tr_l;
 };
 
 hipError_t launch_fill(uint32_t* p, uint32_t v, size_t n, hipStream_t st);
 hipError_t launch_stats(const PrepArgs& a, hipStream_t st);
 hipError_t launch_quant_v_i8(const PrepArgs& a, hipStream_t st);
+hipError_t launch_init_seeded(const PrepArgs& a, uint64_t seed, int32_t* init, hipStream_t st);
 hipError_t launch_init_centroids(const PrepArgs& a, const int32_t* init, hipStream_t st);
 hipError_t launch_assign(const PrepArgs& a, int32_t* labels, hipStream_t st);
 hipError_t launch_sort(const PrepArgs& a, const int32_t* labels, int32_t* perm, hipStream_t st);
@@ -66,6 +76,8 @@ hipError_t launch_update(const PrepArgs& a, const int32_t* perm, hipStream_t st)
 hipError_t launch_iota(int32_t* perm, int N, size_t total, hipStream_t st);
 hipError_t launch_vres_ksmooth(const PrepArgs& a, const int32_t* perm, const PrepOut& o, hipStream_t st);
 hipError_t launch_attn(const AttnArgs& a, hipStream_t st);
+template <int D, int KVB, int VF>
+hipError_t launch_attn_cfg(const AttnArgs& a, hipStream_t st);
 hipError_t launch_dbg_expcast(const float* S, const float* A, const float* B, int64_t n, uint8_t* out,
                               hipStream_t st);
 hipError_t launch_dbg_exp2cast(const float* S, const float* A, const float* B, int64_t n, uint8_t* out,

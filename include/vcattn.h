@@ -99,10 +99,20 @@ typedef struct {
   float softmax_scale;      /* 0 selects fp32(1/sqrt(d))                           */
   float beta;               /* ExpCast offset, -0.5 <= beta <= 0.45                */
   int32_t p_mode;           /* 0: ExpCast-FP8 probability bytes; 1: ExpCast off,   */
-                            /*    p = E4M3(exp2(x)) (see below)                    */
+                            /*    p = E4M3(exp2(x)) (see below); 2: ExpCast moved  */
+                            /*    up by 64 codes, round(8z + 120 + beta), so that  */
+                            /*    p = 2^8 * 2^z stays a normal E4M3 value down to  */
+                            /*    z = -14 (the factor 2^8 cancels in O)            */
   int32_t cluster_order;    /* 0: clusters in k-means label order; 1: renumbered   */
                             /*    along the principal axis of their int8 codes     */
                             /*    before the final pass (see vsmooth_prepare)      */
+  uint64_t seed;            /* k-means initialisation when no init_idx is given:   */
+                            /*    per head (b, h) the k initial tokens are a       */
+                            /*    partial Fisher-Yates shuffle of 0..N-1 driven by */
+                            /*    splitmix64 seeded with                           */
+                            /*    seed + 0x9E3779B97F4A7C15 * (b*H + h): draw r_i, */
+                            /*    j = i + r_i mod (N - i), swap positions i and j, */
+                            /*    for i = 0..k-1; the first k positions are used   */
 } vc_config;
 
 /* Bytes of workspace vsmooth_prepare needs (k-means and sort scratch). */
@@ -114,8 +124,9 @@ size_t vc_attention_workspace_bytes(const vc_config* cfg);
  * vsmooth_prepare: V-Smooth and K smoothing (chooseai.io brief, "V-Smooth").
  *   K, V      bf16 [B,H,N,d]
  *   init_idx  int32 [B,H,k]  initial centroid token indices, distinct, in
- *             [0, N) (the method's random initialisation, drawn by the caller;
- *             ignored when vsmooth == 0, may be NULL then)
+ *             [0, N), or NULL: the library draws them from cfg->seed (see
+ *             vc_config; the method clusters inside the attention call,
+ *             theclarity.today story).  Ignored when vsmooth == 0.
  *   outputs   Kq, k_scale, Vres, v_scale, v_mean, perm in the layouts above;
  *             labels int32 [B,H,N] final cluster labels (nullable)
  *   ws        device workspace of at least vc_prepare_workspace_bytes(cfg)
@@ -138,7 +149,7 @@ vc_status vsmooth_prepare(const vc_config* cfg, const void* K, const void* V,
  * vsmooth_prepare_warm: vsmooth_prepare that carries the clustering across
  * calls (denoising steps: the runtimewire article and the chooseai.io brief
  * describe running V-Smooth step by step and treating its cost as a
- * scheduling trade).  cfg->vsmooth must be 1.  Exactly one of
+ * scheduling trade).  cfg->vsmooth must be 1.  At most one of
  *   init_idx        int32 [B,H,k]   cold start, as in vsmooth_prepare;
  *   init_centroids  fp32 [B,H,k,d]  warm start, e.g. the centroids_out of the
  *                   previous step; cfg->iters passes (1 is the usual choice);
@@ -147,7 +158,8 @@ vc_status vsmooth_prepare(const vc_config* cfg, const void* K, const void* V,
  *                   entries outside [0, N) are clamped, so a bad perm_in
  *                   gives meaningless output but reads nothing outside K, V.
  *                   perm may equal perm_in.
- * is non-NULL.  centroids_out (nullable, fp32 [B,H,k,d]) receives the member
+ * is non-NULL; with none, the cold start draws its tokens from cfg->seed.
+ * centroids_out (nullable, fp32 [B,H,k,d]) receives the member
  * means of the final clusters (a cluster with no members keeps its
  * centroid); it is left untouched when perm_in is given, and labels too.
  * Other arguments as vsmooth_prepare.
@@ -172,9 +184,34 @@ vc_status vc_attn_fwd(const vc_config* cfg, const void* Q, const uint8_t* Kq,
                       const float* k_scale, const uint8_t* Vres, const void* v_scale,
                       const float* v_mean, void* O, hipStream_t stream);
 
+/*
+ * vc_dbg_attn_trace: test entry point.  Runs vc_attn_fwd (same arguments, O
+ * written in full) with a trace instantiation of the same kernel, in which
+ * the workgroup of query rows [256*q_group, 256*q_group + 256) of head
+ * bh = b*H + h also records, for every KV block b in the order it is visited
+ * (chooseai.io brief, "ExpCast-FP8": the byte comes from one FMA on the
+ * log2-domain score relative to the running maximum):
+ *   S       fp32  [nblk][256][kv_block]  the fp32 scores Qq.Kq^T of the block
+ *                 after masking (padded keys -inf), key index = sorted
+ *                 position inside the block;
+ *   P       uint8 [nblk][256][kv_block]  the probability bytes, same order;
+ *   m       fp32  [nblk][256]  running log2-domain maximum after the block;
+ *   c       fp32  [nblk][256]  the block's log2-domain score scale
+ *                 c = fp32(cq * k_scale[b]), cq = fp32(fp32(s_q*scale)*log2 e);
+ *   rowsum  fp32  [nblk][256]  the block's row sum of the decoded bytes.
+ * Rows at or beyond N hold the values for zero query codes.  Requires
+ * out_fp32 = 1 and v_format 0 or 1 (VC_ERR_UNSUPPORTED otherwise); bh and
+ * q_group out of range give VC_ERR_INVALID_ARG.  The caller owns all buffers.
+ */
+vc_status vc_dbg_attn_trace(const vc_config* cfg, const void* Q, const uint8_t* Kq,
+                            const float* k_scale, const uint8_t* Vres, const void* v_scale,
+                            const float* v_mean, void* O, int32_t bh, int32_t q_group, float* S,
+                            uint8_t* P, float* m, float* c, float* rowsum, hipStream_t stream);
+
 /* vc_attention: vsmooth_prepare + vc_attn_fwd with the blocked K/V kept in the
  * workspace (the clustering happens inside the attention call, as the
- * theclarity.today story describes).  ws >= vc_attention_workspace_bytes. */
+ * theclarity.today story describes).  ws >= vc_attention_workspace_bytes.
+ * init_idx may be NULL (initial tokens drawn from cfg->seed). */
 vc_status vc_attention(const vc_config* cfg, const void* Q, const void* K, const void* V,
                        const int32_t* init_idx, void* O, void* ws, size_t ws_bytes,
                        hipStream_t stream);
@@ -200,6 +237,10 @@ vc_status vc_dbg_kmeans_assign(const vc_config* cfg, const void* V, const float*
                                int32_t* labels, void* ws, size_t ws_bytes, hipStream_t stream);
 vc_status vc_dbg_sort(const vc_config* cfg, const int32_t* labels, int32_t* perm,
                       void* ws, size_t ws_bytes, hipStream_t stream);
+/* vc_dbg_init_tokens: init int32 [B,H,k] = the k initial token indices that
+ *   vsmooth_prepare draws from cfg->seed when it is given no init_idx (the
+ *   seeded partial Fisher-Yates of vc_config.seed). */
+vc_status vc_dbg_init_tokens(const vc_config* cfg, int32_t* init, hipStream_t stream);
 
 /* ---- measurement entry point ------------------------------------------------
  * vc_mfma_loop: the attainable FP8 MFMA rate on this GPU at its sustained

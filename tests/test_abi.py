@@ -35,7 +35,7 @@ def test_header_declares_expected_entry_points():
     for want in ("vsmooth_prepare", "vc_attn_fwd", "vc_attention", "vc_prepare_workspace_bytes",
                  "vc_attention_workspace_bytes", "vc_status_str", "vc_last_error", "vc_dbg_expcast",
                  "vc_dbg_kmeans_assign", "vc_dbg_sort", "vc_mfma_loop", "vc_dbg_exp2cast",
-                 "vsmooth_prepare_warm"):
+                 "vsmooth_prepare_warm", "vc_dbg_attn_trace", "vc_dbg_init_tokens"):
         assert want in names, want
 
 
@@ -66,7 +66,8 @@ def cfg(**kw):
     (dict(beta=0.5), VC_ERR_INVALID_ARG),
     (dict(beta=-0.6), VC_ERR_INVALID_ARG),
     (dict(v_format=4), VC_ERR_UNSUPPORTED),
-    (dict(p_mode=2), VC_ERR_UNSUPPORTED),
+    (dict(p_mode=3), VC_ERR_UNSUPPORTED),
+    (dict(p_mode=-1), VC_ERR_UNSUPPORTED),
     (dict(cluster_order=2), VC_ERR_UNSUPPORTED),
     (dict(N=(1 << 24), d=128, n_clusters=16), VC_ERR_UNSUPPORTED),     # 2^31 bytes of blocked keys per head
 ])
@@ -86,7 +87,7 @@ def test_null_and_misaligned_pointers_rejected(lib):
     bad = ctypes.c_void_p(258)
     assert lib.vc_attn_fwd(ctypes.byref(c), bad, P, P, P, P, P, P, None) == VC_ERR_INVALID_ARG
     assert "aligned" in lib.vc_last_error().decode()
-    assert lib.vc_attention(ctypes.byref(c), P, P, P, None, P, P, 1 << 40, None) == VC_ERR_INVALID_ARG  # no init
+    assert lib.vc_attention(ctypes.byref(c), P, P, P, None, None, P, 1 << 40, None) == VC_ERR_INVALID_ARG  # no O
     assert lib.vc_dbg_expcast(None, None, None, -1, None, None) == VC_ERR_INVALID_ARG
     assert lib.vc_mfma_loop(0, 10, P, None) == VC_ERR_INVALID_ARG
     assert lib.vc_mfma_loop(4, 10, None, None) == VC_ERR_INVALID_ARG
@@ -108,14 +109,38 @@ def test_workspace_sizes_grow_with_problem(lib):
     assert big > 3 * small
 
 
-def test_warm_prepare_needs_exactly_one_start(lib):
+def test_warm_prepare_takes_at_most_one_start(lib):
+    # (no start at all is a seeded cold start; it passes validation and is
+    # therefore not called here with placeholder pointers)
     c = cfg()
     P = ctypes.c_void_p(256)
     args = lambda init, cent, perm_in: (ctypes.byref(c), P, P, init, cent, perm_in, None, P, P, P, P, P, P, None, P,
                                          1 << 40, None)
-    assert lib.vsmooth_prepare_warm(*args(None, None, None)) == VC_ERR_INVALID_ARG
-    assert "exactly one" in lib.vc_last_error().decode()
     assert lib.vsmooth_prepare_warm(*args(P, P, None)) == VC_ERR_INVALID_ARG
+    assert "at most one" in lib.vc_last_error().decode()
+    assert lib.vsmooth_prepare_warm(*args(None, P, P)) == VC_ERR_INVALID_ARG
     assert lib.vsmooth_prepare_warm(*args(P, P, P)) == VC_ERR_INVALID_ARG
     c.vsmooth = 0
     assert lib.vsmooth_prepare_warm(*args(P, None, None)) == VC_ERR_INVALID_ARG
+
+
+def test_trace_and_init_entry_points_validate(lib):
+    c = cfg()
+    P = ctypes.c_void_p(256)
+    tr = lambda cc, bh, g: lib.vc_dbg_attn_trace(ctypes.byref(cc), P, P, P, P, P, P, P, bh, g, P, P, P, P, P, None)
+    assert tr(c, 0, 0) == VC_ERR_UNSUPPORTED            # bf16 output: the trace needs fp32 output
+    c.out_fp32 = 1
+    assert tr(c, 2, 0) == VC_ERR_INVALID_ARG            # bh = B*H is out of range
+    assert tr(c, 0, 4) == VC_ERR_INVALID_ARG            # N = 1000 has 4 groups of 256 rows
+    assert tr(c, -1, 0) == VC_ERR_INVALID_ARG
+    c.v_format = 2
+    assert tr(c, 0, 0) == VC_ERR_UNSUPPORTED            # MXFP8 and NVFP4 style are not traced
+    assert lib.vc_dbg_init_tokens(ctypes.byref(cfg()), None, None) == VC_ERR_INVALID_ARG
+    assert lib.vc_dbg_init_tokens(ctypes.byref(cfg(n_clusters=0)), P, None) == VC_ERR_INVALID_ARG
+
+
+def test_seed_field_is_last_and_64_bit():
+    # the ABI appends the seed after the 32-bit fields (8-byte aligned)
+    assert vb.VcConfig.seed.offset == 56 and ctypes.sizeof(vb.VcConfig) == 64
+    c = vb.make_config(1, 1, 10, 64, 64, seed=-1)
+    assert c.seed == 2 ** 64 - 1
