@@ -58,6 +58,10 @@ def lib() -> ctypes.CDLL:
         L.vc_attn_fwd.restype = ctypes.c_int
         L.vc_attention.argtypes = [cfgp, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
         L.vc_attention.restype = ctypes.c_int
+        L.vc_attention_noalloc.argtypes = [cfgp, _P, _P, _P, _P, _P, _P]
+        L.vc_attention_noalloc.restype = ctypes.c_int
+        L.vc_noalloc_scratch_bytes.argtypes = []
+        L.vc_noalloc_scratch_bytes.restype = ctypes.c_size_t
         L.vc_status_str.argtypes = [ctypes.c_int]
         L.vc_status_str.restype = ctypes.c_char_p
         L.vc_last_error.argtypes = []
@@ -278,6 +282,26 @@ def vc_attention(cfg: VcConfig, Q, K, V, init_idx=None, out=None, ws=None) -> to
                               _ptr(init_idx) if cfg.vsmooth else None, _ptr(out), _ptr(ws), ws.numel(),
                               _stream()), "vc_attention")
     return out
+
+
+def vc_attention_noalloc(cfg: VcConfig, Q, K, V, init_idx=None, out=None) -> torch.Tensor:
+    """vc_attention with the library's static scratch in place of a workspace
+    (include/vcattn.h): the library allocates nothing; pass `out` to keep the
+    call free of allocations on this side too."""
+    shp = (cfg.B, cfg.H, cfg.N, cfg.d)
+    for t, n in ((Q, "Q"), (K, "K"), (V, "V")):
+        _need(t, torch.bfloat16, shp, n)
+    if cfg.vsmooth and init_idx is not None:
+        _need(init_idx, torch.int32, (cfg.B, cfg.H, cfg.n_clusters), "init_idx")
+    out = _output(cfg, out, Q.device)
+    _check(lib().vc_attention_noalloc(ctypes.byref(cfg), _ptr(Q), _ptr(K), _ptr(V),
+                                      _ptr(init_idx) if cfg.vsmooth else None, _ptr(out), _stream()),
+           "vc_attention_noalloc")
+    return out
+
+
+def noalloc_scratch_bytes() -> int:
+    return int(lib().vc_noalloc_scratch_bytes())
 
 
 TRACE_ROWS = 256     # query rows of one attention workgroup (one traced group)

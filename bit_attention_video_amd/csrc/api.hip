@@ -4,6 +4,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "../../include/vcattn.h"
@@ -331,9 +332,12 @@ vc_status vc_dbg_attn_trace(const vc_config* cfg, const void* Q, const uint8_t* 
   return VC_OK;
 }
 
-vc_status vc_attention(const vc_config* cfg, const void* Q, const void* K, const void* V,
-                       const int32_t* init_idx, void* O, void* ws, size_t ws_bytes, hipStream_t stream) {
-  g_err.clear();
+}  // extern "C"
+
+namespace {
+
+vc_status attention_impl(const vc_config* cfg, const void* Q, const void* K, const void* V,
+                         const int32_t* init_idx, void* O, void* ws, size_t ws_bytes, hipStream_t stream) {
   Dims D;
   if (vc_status s = validate(cfg, cfg && cfg->vsmooth, &D)) return s;
   if (!Q || !K || !V || !O || !ws) return fail(VC_ERR_INVALID_ARG, "required pointer is NULL");
@@ -359,6 +363,64 @@ vc_status vc_attention(const vc_config* cfg, const void* Q, const void* K, const
   at.Kq = o.Kq; at.k_scale = o.k_scale; at.Vres = o.Vres; at.v_scale = o.v_scale; at.v_mean = o.v_mean; at.O = O;
   VC_TRY(vc::launch_attn(at, stream), "attn_fwd");
   return VC_OK;
+}
+
+// ---- vc_attention_noalloc: the library's own scratch in place of a workspace ----
+// One file-scope device array per GPU (each GPU the library runs on holds its
+// own copy until the process ends).  In host code `scratch` only names the
+// symbol: its device address comes from hipGetSymbolAddress, once per device
+// with that device current, and only that address is ever handed to kernels.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+}  // namespace
+
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+
+vc_status scratch_of_current_device(void** out) {
+  int dev = 0;
+  VC_TRY(hipGetDevice(&dev), "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(VC_ERR_UNSUPPORTED, "device index must be below 64");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    VC_TRY(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(VC_ERR_HIP, "hipGetSymbolAddress(scratch) gave a null address");
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return VC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+vc_status vc_attention(const vc_config* cfg, const void* Q, const void* K, const void* V,
+                       const int32_t* init_idx, void* O, void* ws, size_t ws_bytes, hipStream_t stream) {
+  g_err.clear();
+  return attention_impl(cfg, Q, K, V, init_idx, O, ws, ws_bytes, stream);
+}
+
+size_t vc_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+vc_status vc_attention_noalloc(const vc_config* cfg, const void* Q, const void* K, const void* V,
+                               const int32_t* init_idx, void* O, hipStream_t stream) {
+  g_err.clear();
+  Dims D;
+  if (vc_status s = validate(cfg, cfg && cfg->vsmooth, &D)) return s;
+  const size_t need = vc_attention_workspace_bytes(cfg);
+  if (need > kScratchBytes)
+    return fail(VC_ERR_WORKSPACE, "this configuration needs " + std::to_string(need) +
+                                      " bytes of scratch; vc_attention_noalloc holds " +
+                                      std::to_string(kScratchBytes) + " (use vc_attention with a workspace)");
+  void* ws = nullptr;
+  if (vc_status s = scratch_of_current_device(&ws)) return s;
+  return attention_impl(cfg, Q, K, V, init_idx, O, ws, kScratchBytes, stream);
 }
 
 vc_status vc_dbg_expcast(const float* S, const float* A, const float* B, int64_t n, uint8_t* out,

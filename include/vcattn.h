@@ -216,6 +216,23 @@ vc_status vc_attention(const vc_config* cfg, const void* Q, const void* K, const
                        const int32_t* init_idx, void* O, void* ws, size_t ws_bytes,
                        hipStream_t stream);
 
+/*
+ * vc_attention_noalloc: vc_attention for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same computation and kernels, with the workspace
+ * taken from a static device array inside the library, vc_noalloc_scratch_bytes()
+ * = 64 MiB per GPU, held by every GPU the library runs on until the process
+ * ends.  The caller still passes Q, K, V (and init_idx, nullable) and O.
+ * Nothing is allocated or freed.  A configuration whose
+ * vc_attention_workspace_bytes exceeds the scratch returns VC_ERR_WORKSPACE
+ * before anything runs.  Every call on one GPU uses that GPU's one array and
+ * leaves its contents behind: calls that overlap on one GPU (other streams or
+ * threads) race and must be serialised by the caller.
+ */
+vc_status vc_attention_noalloc(const vc_config* cfg, const void* Q, const void* K, const void* V,
+                               const int32_t* init_idx, void* O, hipStream_t stream);
+size_t vc_noalloc_scratch_bytes(void);
+
 const char* vc_status_str(vc_status s);
 /* Message of the last failure on the calling thread ("" if none). */
 const char* vc_last_error(void);
