@@ -28,12 +28,14 @@ def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
 def prepare_head(K: np.ndarray, V: np.ndarray, init_idx: np.ndarray | None, k: int, iters: int,
                  kv_block: int, fmt: str = "e4m3", vsmooth_on: bool = True,
                  quantize: bool = True, init_centroids: np.ndarray | None = None,
-                 perm: np.ndarray | None = None, cluster_order: bool = False) -> dict:
+                 perm: np.ndarray | None = None, cluster_order: bool = False, balanced: bool = False) -> dict:
     """K, V: [N, d] fp64 bf16 values of one head.  With V-Smooth on, the
     clustering starts from V[init_idx] or, warm-started, from init_centroids
     (fp32 [k, d]); a given perm is reused as is (no clustering, no sort).
     cluster_order renumbers the clusters along their principal axis before
     the final pass (kmeans.order_clusters), so the blocks follow that order.
+    balanced: k = ceil(N / kv_block) clusters with capacities kv_block (the
+    last the tail), so every block is one cluster (kmeans.capped_assign).
     "final_centroids" are the member means of the final clusters."""
     N = V.shape[0]
     final = None
@@ -41,7 +43,10 @@ def prepare_head(K: np.ndarray, V: np.ndarray, init_idx: np.ndarray | None, k: i
         labels, cents = None, []
         perm = np.asarray(perm, np.int32)
     elif vsmooth_on:
-        labels, cents, final = kmeans.kmeans(V, init_idx, iters, init_centroids, cluster_order)
+        cap = kmeans.block_capacities(N, kv_block) if balanced else None
+        if balanced:
+            assert k == cap.size, "balanced clusters: k must be ceil(N / kv_block)"
+        labels, cents, final = kmeans.kmeans(V, init_idx, iters, init_centroids, cluster_order, cap)
         perm = vsmooth.stable_sort_perm(labels, k)
     else:
         labels, cents = None, []

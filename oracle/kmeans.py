@@ -24,6 +24,17 @@ iteration count.  The readings used here (all stated as readings):
 * Update: the fp32 rounding of the fp64 mean of the members' original values;
   a cluster with no members keeps its centroid.
 
+Optional balanced clusters (a blocking variant; [brief] "V-Smooth" asks that
+similar tokens share one hardware block): k = ceil(N / kv_block) clusters
+with capacities kv_block (the last one the tail, N - (k-1) * kv_block), so
+that after the stable sort every block holds exactly one cluster.  Each
+assignment pass is capped (``capped_assign``): in rounds, every unassigned
+token proposes to its nearest cluster that still has room (ties to the
+lowest cluster index), and a cluster with r places left takes the r nearest
+of its proposers (ties to the lowest token index); tokens still unassigned
+after BALANCED_ROUNDS rounds fill the remaining places in token order,
+clusters in index order.  Distances are the same exact int8 scores.
+
 Optional cluster ordering (a blocking variant; [brief] "V-Smooth" asks that
 similar tokens share a hardware block but says nothing of the order of the
 clusters): before the final assignment pass the centroids are renumbered by
@@ -99,6 +110,45 @@ def assign(Vq: np.ndarray, Cq: np.ndarray) -> np.ndarray:
     return np.argmin(D, axis=1).astype(np.int32)
 
 
+BALANCED_ROUNDS = 12
+
+
+def block_capacities(N: int, kv_block: int) -> np.ndarray:
+    """Capacities of the balanced clusters: kv_block each, the last one the
+    tail of the sequence."""
+    k = (N + kv_block - 1) // kv_block
+    cap = np.full(k, kv_block, dtype=np.int64)
+    cap[-1] = N - (k - 1) * kv_block
+    return cap
+
+
+def capped_assign(Vq: np.ndarray, Cq: np.ndarray, cap: np.ndarray, rounds: int = BALANCED_ROUNDS) -> np.ndarray:
+    """Assignment with cluster capacities cap (sum(cap) == N), see the module
+    notes.  Squared distances |v|^2 + |c|^2 - 2 v.c of the int8 codes are
+    exact integers."""
+    N, k = Vq.shape[0], Cq.shape[0]
+    assert int(np.sum(cap)) == N
+    dist = np.sum(Vq * Vq, axis=1)[:, None] + np.sum(Cq * Cq, axis=1)[None, :] - 2.0 * (Vq @ Cq.T)
+    labels = np.full(N, -1, dtype=np.int64)
+    rem = np.asarray(cap, dtype=np.int64).copy()
+    for _ in range(rounds):
+        un = np.nonzero(labels < 0)[0]
+        if un.size == 0:
+            break
+        dc = np.where(rem[None, :] > 0, dist[un], np.inf)
+        prop = np.argmin(dc, axis=1)                 # first minimum: lowest cluster index
+        for c in np.unique(prop):
+            ts = un[prop == c]                       # proposers in token order
+            order = np.lexsort((ts, dist[ts, c]))    # nearest first, then lowest token index
+            take = ts[order][:rem[c]]
+            labels[take] = c
+            rem[c] -= take.size
+    un = np.nonzero(labels < 0)[0]
+    slots = np.repeat(np.arange(k), rem)             # the places left, clusters in index order
+    labels[un] = slots[:un.size]
+    return labels.astype(np.int32)
+
+
 def update(V: np.ndarray, labels: np.ndarray, C_old: np.ndarray) -> np.ndarray:
     k = C_old.shape[0]
     sums = np.zeros_like(C_old, dtype=np.float64)
@@ -147,11 +197,12 @@ def order_clusters(q: np.ndarray) -> np.ndarray:
 
 
 def kmeans(V: np.ndarray, init_idx: np.ndarray | None, iters: int, init_centroids: np.ndarray | None = None,
-           order: bool = False):
+           order: bool = False, capacities: np.ndarray | None = None):
     """V: [N, d] float64 holding the bf16 values of one head.  Starts from the
     rows V[init_idx], or from init_centroids (fp32 [k, d]) when given.
     order: renumber the centroids along their principal axis before the final
-    pass.  Returns (labels int32 [N], centroids_per_pass: the centroids each
+    pass.  capacities: capped assignment passes (balanced clusters).
+    Returns (labels int32 [N], centroids_per_pass: the centroids each
     assignment pass used, final: the member means of the final clusters)."""
     sV = int8_scale(V)
     Vq = quant_i8(V, sV)
@@ -168,7 +219,10 @@ def kmeans(V: np.ndarray, init_idx: np.ndarray | None, iters: int, init_centroid
             Cn[rank] = C
             C = Cn
         used.append(C.copy())
-        labels = assign(Vq, quant_i8(C, sV))
+        if capacities is None:
+            labels = assign(Vq, quant_i8(C, sV))
+        else:
+            labels = capped_assign(Vq, quant_i8(C, sV), capacities)
         if it + 1 < iters:
             C = update(V, labels, C)
     return labels, used, update(V, labels, C)

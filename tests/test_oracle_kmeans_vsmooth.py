@@ -476,3 +476,75 @@ def test_seeded_init_is_uniform_over_tokens():
     for bh in range(2000):
         cnt[seeded_init(7, bh, 20, 5)] += 1
     assert np.all(np.abs(cnt - 500) < 100)
+
+
+# ---- balanced clusters: capped assignment ----
+
+def test_capped_assign_worked_examples():
+    # worked by hand on one channel (codes as given, scale irrelevant):
+    # tokens 0 1 2 3 10 11, centroids 1 and 11, three places each.  Round 1:
+    # tokens 0..3 propose to centroid 1 (distances 1 0 1 4), which takes
+    # token 1, then 0 and 2 (a distance tie, lower token first); 10 and 11
+    # go to centroid 11.  Round 2: token 3 proposes to the only cluster with
+    # room left.
+    Vq = np.array([[0.0], [1.0], [2.0], [3.0], [10.0], [11.0]])
+    Cq = np.array([[1.0], [11.0]])
+    assert KM.capped_assign(Vq, Cq, np.array([3, 3])).tolist() == [0, 0, 0, 1, 1, 1]
+    # a distance tie between two tokens for one place goes to the lower token
+    assert KM.capped_assign(np.array([[0.0], [2.0], [48.0]]), np.array([[1.0], [49.0]]),
+                            np.array([1, 2])).tolist() == [0, 1, 1]
+    # a token equidistant from two clusters proposes to the lower index
+    assert KM.capped_assign(np.array([[5.0], [9.0]]), np.array([[3.0], [7.0]]),
+                            np.array([1, 1])).tolist() == [0, 1]
+    # with no rounds the places are filled in token order, clusters in index order
+    assert KM.capped_assign(np.zeros((5, 1)), np.zeros((2, 1)), np.array([2, 3]), rounds=0).tolist() == \
+        [0, 0, 1, 1, 1]
+
+
+def test_capped_assign_is_plain_assignment_when_nothing_overflows():
+    # capacities equal to the sizes of the unconstrained assignment: every
+    # proposal is accepted in the first round, so the result is the plain
+    # argmin with lowest-index ties
+    rng = np.random.default_rng(31)
+    Vq = rng.integers(-20, 21, (300, 6)).astype(np.float64)
+    Cq = rng.integers(-20, 21, (9, 6)).astype(np.float64)
+    plain = KM.assign(Vq, Cq)
+    cap = np.bincount(plain, minlength=9)
+    assert np.array_equal(KM.capped_assign(Vq, Cq, cap), plain)
+
+
+@pytest.mark.parametrize("N,kvb", [(1000, 64), (300, 128), (64, 64), (77, 64)])
+def test_capped_assign_fills_every_cluster_exactly(N, kvb):
+    rng = np.random.default_rng(N)
+    cap = KM.block_capacities(N, kvb)
+    assert cap.sum() == N and np.all(cap[:-1] == kvb) and 1 <= cap[-1] <= kvb
+    Vq = rng.integers(-127, 128, (N, 8)).astype(np.float64)
+    Cq = Vq[rng.choice(N, cap.size, replace=False)]
+    lab = KM.capped_assign(Vq, Cq, cap)
+    assert np.array_equal(np.bincount(lab, minlength=cap.size), cap)
+
+
+def test_balanced_kmeans_recovers_groups_of_block_size():
+    # four well separated groups of exactly 64 tokens (one block each): the
+    # balanced clustering puts every group in one cluster, whatever the start
+    rng = np.random.default_rng(4)
+    centers = np.array([[60.0, 0], [-60, 0], [0, 60], [0, -60]])
+    grp = rng.permutation(np.repeat(np.arange(4), 64))
+    V = F.f32(centers[grp] + rng.standard_normal((256, 2)))
+    init = np.array([0, 1, 2, 3], dtype=np.int32)          # possibly two starts in one group
+    lab, _, _ = KM.kmeans(V, init, 4, capacities=KM.block_capacities(256, 64))
+    for g in range(4):
+        assert np.unique(lab[grp == g]).size == 1
+    assert np.unique(lab).size == 4
+
+
+@pytest.mark.parametrize("N,kvb", [(1024, 64), (1000, 128), (333, 64)])
+def test_balanced_prepare_gives_one_cluster_per_block(N, kvb):
+    w = inputs.small(inputs.WORKLOADS["tiny"], N=N, kv_block=kvb)
+    q, k, v, _ = inputs.gen_head(w, 0, 0)
+    nblk = (N + kvb - 1) // kvb
+    init = KM.seeded_init(5, 0, N, nblk)
+    prep = oracle.prepare_head(oracle.bf16_to_f64(k), oracle.bf16_to_f64(v), init, nblk, 3, kvb, balanced=True)
+    sorted_labels = prep["labels"][prep["perm"]]
+    for b in range(nblk):
+        assert np.all(sorted_labels[b * kvb:(b + 1) * kvb] == b)
