@@ -31,7 +31,7 @@ class VcConfig(ctypes.Structure):
                 ("kv_block", ctypes.c_int32), ("n_clusters", ctypes.c_int32), ("iters", ctypes.c_int32),
                 ("vsmooth", ctypes.c_int32), ("v_format", ctypes.c_int32), ("out_fp32", ctypes.c_int32),
                 ("softmax_scale", ctypes.c_float), ("beta", ctypes.c_float), ("p_mode", ctypes.c_int32),
-                ("cluster_order", ctypes.c_int32), ("seed", ctypes.c_uint64)]
+                ("cluster_order", ctypes.c_int32), ("seed", ctypes.c_uint64), ("balanced", ctypes.c_int32)]
 
 
 _lib = None
@@ -100,10 +100,17 @@ def _check(status: int, what: str):
 def make_config(B: int, H: int, N: int, d: int, kv_block: int, n_clusters: int = 1, iters: int = 1,
                 vsmooth: bool = True, v_format: int = E4M3, out_fp32: bool = False,
                 softmax_scale: float = 0.0, beta: float = DEFAULT_BETA, p_mode: int = EXPCAST,
-                cluster_order: bool = False, seed: int = 0) -> VcConfig:
+                cluster_order: bool = False, seed: int = 0, balanced: bool = False) -> VcConfig:
+    """balanced: clusters sized to the blocks (n_clusters must then be
+    ceil(N / kv_block); balanced_clusters() gives it)."""
     return VcConfig(B, H, N, d, kv_block, n_clusters, iters, int(bool(vsmooth)), int(v_format),
                     int(bool(out_fp32)), softmax_scale, beta, int(p_mode), int(bool(cluster_order)),
-                    int(seed) & (2 ** 64 - 1))
+                    int(seed) & (2 ** 64 - 1), int(bool(balanced)))
+
+
+def balanced_clusters(N: int, kv_block: int) -> int:
+    """The cluster count of the balanced blocking variant: one cluster per block."""
+    return (N + kv_block - 1) // kv_block
 
 
 def _stream():

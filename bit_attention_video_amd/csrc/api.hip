@@ -29,7 +29,7 @@ bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) !
 constexpr int kTraceRows = 256;   // query rows per attention workgroup (one traced group)
 
 struct Dims {
-  int B, H, N, d, kvb, k, kpad, iters, nblk, nstat, nsort;
+  int B, H, N, d, kvb, k, kpad, iters, nblk, nstat, nsort, balanced;
   size_t BH;
 };
 
@@ -55,11 +55,15 @@ vc_status validate(const vc_config* c, bool need_kmeans, Dims* out) {
     return fail(VC_ERR_UNSUPPORTED, "p_mode must be 0 (ExpCast), 1 (exp2 + cast) or 2 (range-shifted ExpCast)");
   if (c->cluster_order != 0 && c->cluster_order != 1)
     return fail(VC_ERR_UNSUPPORTED, "cluster_order must be 0 (label order) or 1 (principal-axis order)");
+  if (c->balanced != 0 && c->balanced != 1) return fail(VC_ERR_INVALID_ARG, "balanced must be 0 or 1");
   if (need_kmeans) {
     if (c->n_clusters < 1 || c->n_clusters > c->N || c->n_clusters > vc::kMaxClusters)
       return fail(VC_ERR_INVALID_ARG, "n_clusters must lie in [1, min(N, 4096)]");
     if (c->iters < 1 || c->iters > 16) return fail(VC_ERR_INVALID_ARG, "iters must lie in [1, 16]");
+    if (c->balanced && c->n_clusters != (c->N + c->kv_block - 1) / c->kv_block)
+      return fail(VC_ERR_INVALID_ARG, "balanced clusters need n_clusters = ceil(N / kv_block)");
   }
+  if (c->balanced && !c->vsmooth) return fail(VC_ERR_INVALID_ARG, "balanced clusters need vsmooth on");
   Dims& D = *out;
   D.B = c->B; D.H = c->H; D.N = c->N; D.d = c->d; D.kvb = c->kv_block;
   D.k = need_kmeans ? c->n_clusters : 1;
@@ -69,6 +73,7 @@ vc_status validate(const vc_config* c, bool need_kmeans, Dims* out) {
   D.nstat = (c->N + 1023) / 1024;
   D.nsort = (c->N + vc::kSortChunk - 1) / vc::kSortChunk;
   D.BH = static_cast<size_t>(c->B) * c->H;
+  D.balanced = c->balanced;
   return VC_OK;
 }
 
@@ -106,6 +111,11 @@ void carve_prep(Carver& cv, const Dims& D, vc::PrepArgs& a) {
   a.rank = cv.take<int32_t>(BH * D.k);
   a.Ctmp = cv.take<float>(BH * D.k * D.d);
   a.init = cv.take<int32_t>(BH * D.k);
+  if (D.balanced) {
+    a.prop = cv.take<int32_t>(BH * D.N);
+    a.pdist = cv.take<int32_t>(BH * D.N);
+    a.rem = cv.take<int32_t>(BH * D.k);
+  }
 }
 
 struct OutSizes {
@@ -167,7 +177,8 @@ vc_status run_prepare(const vc_config* c, const Dims& D, vc::PrepArgs& a, const 
       const bool last = it + 1 == D.iters;
       int32_t* lab = (last && user_labels) ? user_labels : a.labels;
       if (last && c->cluster_order) VC_TRY(vc::launch_cluster_order(a, st), "cluster_order");
-      VC_TRY(vc::launch_assign(a, lab, st), "kmeans_assign");
+      if (c->balanced) VC_TRY(vc::launch_bal_assign(a, lab, st), "kmeans_assign (balanced)");
+      else VC_TRY(vc::launch_assign(a, lab, st), "kmeans_assign");
       if (!last) {
         VC_TRY(vc::launch_sort(a, lab, a.perm_tmp, st), "sort");
         VC_TRY(vc::launch_update(a, a.perm_tmp, st), "kmeans_update");

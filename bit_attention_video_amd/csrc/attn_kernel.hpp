@@ -802,10 +802,12 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_fwd(AttnArgs p) {
       for (int i = 0; i < 4; ++i) {
         const int c0 = 32 * T + 8 * i + 4 * g;
         const float4 cs = *reinterpret_cast<const float4*>(sCol + c0);
-        const float o0 = st.acc[T][4 * i + 0] * cs.x * inv_l;
-        const float o1 = st.acc[T][4 * i + 1] * cs.y * inv_l;
-        const float o2 = st.acc[T][4 * i + 2] * cs.z * inv_l;
-        const float o3 = st.acc[T][4 * i + 3] * cs.w * inv_l;
+        // 1/l first: acc / l is of the order of the residual codes, so the
+        // column scale (as small as 2^-126) does not push it into subnormals
+        const float o0 = st.acc[T][4 * i + 0] * inv_l * cs.x;
+        const float o1 = st.acc[T][4 * i + 1] * inv_l * cs.y;
+        const float o2 = st.acc[T][4 * i + 2] * inv_l * cs.z;
+        const float o3 = st.acc[T][4 * i + 3] * inv_l * cs.w;
         const size_t off = (static_cast<size_t>(bh) * N + qrow) * D + c0;
         if constexpr (O32) {
           *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.O) + off) = make_float4(o0, o1, o2, o3);

@@ -204,11 +204,19 @@ __global__ __launch_bounds__(256) void k_quant_centroids(const float* __restrict
 // (score, index).
 // A workgroup covers 256 tokens (4 waves x 2 column tiles of 32); centroids
 // stream through LDS in chunks of 128.
-template <int D>
+// BAL (balanced clusters, one proposal round): only tokens whose label in
+// `labels` is still -1 take part; full clusters carry zero codes and the
+// offset INT_MIN, so they are never chosen; the kernel writes each active
+// token's proposal (nearest cluster with room, lowest index on ties) to
+// `prop` and its exact squared distance |v|^2 - score to `pdist`, and -1 to
+// `prop` for every other token.
+template <int D, bool BAL = false>
 __global__ __launch_bounds__(256, 2) void k_kmeans_assign(const int8_t* __restrict__ Vq,
                                                        const int8_t* __restrict__ Cq,
                                                        const int32_t* __restrict__ cn32, int N,
-                                                       int kpad, int32_t* __restrict__ labels) {
+                                                       int kpad, int32_t* __restrict__ labels,
+                                                       int32_t* __restrict__ prop = nullptr,
+                                                       int32_t* __restrict__ pdist = nullptr) {
   constexpr int NDC = D / 32;
   constexpr int CSTR = D + 16;
   constexpr int CCH = 128;
@@ -220,6 +228,22 @@ __global__ __launch_bounds__(256, 2) void k_kmeans_assign(const int8_t* __restri
   const int8_t* cq = Cq + static_cast<size_t>(bh) * kpad * D;
   const int32_t* cn = cn32 + static_cast<size_t>(bh) * kpad;
   const int tok0 = blockIdx.x * 256 + wave * 64;
+  bool active[2] = {true, true};
+  if constexpr (BAL) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int tok = tok0 + j * 32 + col;
+      active[j] = tok < N && labels[static_cast<size_t>(bh) * N + tok] < 0;
+    }
+    if (!__syncthreads_or(active[0] || active[1])) {      // every token of the workgroup is placed
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int tok = tok0 + j * 32 + col;
+        if (g == 0 && tok < N) prop[static_cast<size_t>(bh) * N + tok] = -1;
+      }
+      return;
+    }
+  }
 
   v4i bop[2][NDC];
 #pragma unroll
@@ -281,9 +305,195 @@ __global__ __launch_bounds__(256, 2) void k_kmeans_assign(const int8_t* __restri
     const int idx = btile[j] * 32 + (31 - (best[j] & 31));
     const int ps = __shfl_xor(score, 32, 64);
     const int pi = __shfl_xor(idx, 32, 64);
-    const int lab = (ps > score || (ps == score && pi < idx)) ? pi : idx;
+    const bool other = ps > score || (ps == score && pi < idx);
+    const int lab = other ? pi : idx;
     const int tok = tok0 + j * 32 + col;
-    if (g == 0 && tok < N) labels[static_cast<size_t>(bh) * N + tok] = lab;
+    if constexpr (BAL) {
+      // |v|^2 of the token: this lane holds half of its codes, the lane 32
+      // apart the other half
+      int vn = 0;
+#pragma unroll
+      for (int c = 0; c < NDC; ++c)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) vn = __builtin_amdgcn_sdot4(bop[j][c][q], bop[j][c][q], vn, false);
+      vn += __shfl_xor(vn, 32, 64);
+      if (g == 0 && tok < N) {
+        prop[static_cast<size_t>(bh) * N + tok] = active[j] ? lab : -1;
+        pdist[static_cast<size_t>(bh) * N + tok] = vn - (other ? ps : score);
+      }
+    } else {
+      if (g == 0 && tok < N) labels[static_cast<size_t>(bh) * N + tok] = lab;
+    }
+  }
+}
+
+// ---- balanced clusters (capped assignment) ------------------------------------
+// Capacities: kv_block places per cluster, the last cluster the tail of the
+// sequence, so that after the stable sort every block holds one cluster.
+// Per pass: rem = capacities and labels = -1; then kBalRounds rounds of
+// (proposals by k_kmeans_assign<D, true>; proposals grouped by cluster with
+// the stable counting sort; k_bal_accept); then k_bal_fill places whatever
+// is left in token order, clusters in index order.
+constexpr int kBalRounds = 12;
+constexpr int kBalThreads = 256;
+
+__global__ void k_bal_init(int N, int k, int kvb, int32_t* __restrict__ rem, int32_t* __restrict__ labels) {
+  const int bh = blockIdx.y;
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < N) labels[static_cast<size_t>(bh) * N + i] = -1;
+  if (i < k) rem[static_cast<size_t>(bh) * k + i] = i + 1 < k ? kvb : N - (k - 1) * kvb;
+}
+
+// sum of v over the workgroup (every thread gets it)
+__device__ __forceinline__ int bal_block_sum(int v, int* red) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  int t = 0;
+  for (int w = 0; w < kBalThreads / 64; ++w) t += red[w];
+  return t;
+}
+
+// maximum of v over the workgroup (every thread gets it)
+__device__ __forceinline__ int bal_block_max(int v, int* red) {
+  for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o, 64));
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  int m = red[0];
+  for (int w = 1; w < kBalThreads / 64; ++w) m = max(m, red[w]);
+  return m;
+}
+
+// Cluster c (one workgroup) takes the rem_c nearest of its proposers (by
+// exact squared distance, ties to the lowest token index; the proposers
+// arrive in token order); a cluster that fills up gets zero codes and the
+// offset INT_MIN, so the next rounds never propose to it.
+template <int D>
+__global__ __launch_bounds__(kBalThreads) void k_bal_accept(const int32_t* __restrict__ list_all,
+                                                            const int32_t* __restrict__ counts,
+                                                            const int32_t* __restrict__ starts,
+                                                            const int32_t* __restrict__ pdist, int N, int k,
+                                                            int kpad, int32_t* __restrict__ rem,
+                                                            int32_t* __restrict__ labels, int8_t* __restrict__ Cq,
+                                                            int32_t* __restrict__ cn32) {
+  __shared__ int red[kBalThreads / 64];
+  const int c = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
+  const int cnt = counts[static_cast<size_t>(bh) * k + c];
+  int r = rem[static_cast<size_t>(bh) * k + c];
+  if (cnt == 0 || r == 0) return;
+  const int32_t* list = list_all + static_cast<size_t>(bh) * N + starts[static_cast<size_t>(bh) * k + c];
+  const int32_t* dist = pdist + static_cast<size_t>(bh) * N;
+  int32_t* lab = labels + static_cast<size_t>(bh) * N;
+  if (cnt <= r) {
+    for (int i = t; i < cnt; i += kBalThreads) lab[list[i]] = c;
+    r -= cnt;
+  } else {
+    // theta = the r-th smallest distance: the smallest value with
+    // #(dist <= theta) >= r (binary search over the exact integers)
+    int lo = INT_MAX, hi = INT_MIN;
+    for (int i = t; i < cnt; i += kBalThreads) {
+      const int dv = dist[list[i]];
+      lo = min(lo, dv);
+      hi = max(hi, dv);
+    }
+    lo = -bal_block_max(-lo, red);
+    hi = bal_block_max(hi, red);
+    while (lo < hi) {                                   // uniform across the workgroup
+      const int mid = lo + (hi - lo) / 2;
+      int n = 0;
+      for (int i = t; i < cnt; i += kBalThreads) n += dist[list[i]] <= mid;
+      if (bal_block_sum(n, red) >= r) hi = mid;
+      else lo = mid + 1;
+    }
+    const int theta = lo;
+    int nl = 0;
+    for (int i = t; i < cnt; i += kBalThreads) nl += dist[list[i]] < theta;
+    const int need = r - bal_block_sum(nl, red);       // >= 1 proposers at distance theta, in token order
+    const int lane = t & 63, wave = t >> 6;
+    int run = 0;
+    for (int base = 0; base < cnt; base += kBalThreads) {
+      const int i = base + t;
+      const int dv = i < cnt ? dist[list[i]] : INT_MAX;
+      const bool eq = dv == theta;
+      const uint64_t bal = __ballot(eq);
+      __syncthreads();
+      if (lane == 0) red[wave] = __popcll(bal);
+      __syncthreads();
+      int before = run + __popcll(bal & ((1ull << lane) - 1ull));
+      for (int w = 0; w < wave; ++w) before += red[w];
+      if (i < cnt && (dv < theta || (eq && before < need))) lab[list[i]] = c;
+      for (int w = 0; w < kBalThreads / 64; ++w) run += red[w];
+    }
+    r = 0;
+  }
+  __syncthreads();
+  if (t == 0) rem[static_cast<size_t>(bh) * k + c] = r;
+  if (r == 0) {
+    int8_t* row = Cq + (static_cast<size_t>(bh) * kpad + c) * D;
+    for (int i = t; i < D / 4; i += kBalThreads) reinterpret_cast<int32_t*>(row)[i] = 0;
+    if (t == 0) cn32[static_cast<size_t>(bh) * kpad + c] = INT_MIN;
+  }
+}
+
+// Tokens left after the rounds take the remaining places: the u-th
+// unassigned token (token order) goes to the cluster holding place u when
+// the clusters' remaining places are laid out in index order.
+constexpr int kFillThreads = 1024;
+__global__ __launch_bounds__(kFillThreads) void k_bal_fill(const int32_t* __restrict__ rem, int N, int k,
+                                                           int32_t* __restrict__ labels) {
+  constexpr int PER = kMaxClusters / kFillThreads;
+  __shared__ int cum[kMaxClusters];
+  __shared__ int part[kFillThreads];
+  __shared__ int red[kFillThreads / 64];
+  const int bh = blockIdx.x, t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  int32_t* lab = labels + static_cast<size_t>(bh) * N;
+  // cum = exclusive prefix sum of rem over the clusters (PER per thread, then
+  // an inclusive Hillis-Steele scan of the per-thread totals)
+  int mine[PER];
+  int tot = 0;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    const int c = t * PER + e;
+    mine[e] = c < k ? rem[static_cast<size_t>(bh) * k + c] : 0;
+    tot += mine[e];
+  }
+  part[t] = tot;
+  __syncthreads();
+  for (int o = 1; o < kFillThreads; o <<= 1) {
+    const int v = t >= o ? part[t - o] : 0;
+    __syncthreads();
+    part[t] += v;
+    __syncthreads();
+  }
+  int acc = part[t] - tot;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    cum[t * PER + e] = acc;
+    acc += mine[e];
+  }
+  __syncthreads();
+  int run = 0;
+  for (int base = 0; base < N; base += kFillThreads) {
+    const int i = base + t;
+    const bool un = i < N && lab[i] < 0;
+    const uint64_t bal = __ballot(un);
+    __syncthreads();
+    if (lane == 0) red[wave] = __popcll(bal);
+    __syncthreads();
+    int u = run + __popcll(bal & ((1ull << lane) - 1ull));
+    for (int w = 0; w < wave; ++w) u += red[w];
+    if (un) {
+      int a = 0, b = k - 1;                 // the last cluster with cum <= u
+      while (a < b) {
+        const int m = (a + b + 1) / 2;
+        if (cum[m] <= u) a = m;
+        else b = m - 1;
+      }
+      lab[i] = a;
+    }
+    for (int w = 0; w < kFillThreads / 64; ++w) run += red[w];
   }
 }
 
@@ -1043,6 +1253,27 @@ static hipError_t assign_t(const PrepArgs& a, int32_t* labels, hipStream_t st) {
 }
 hipError_t launch_assign(const PrepArgs& a, int32_t* labels, hipStream_t st) {
   return a.d == 64 ? assign_t<64>(a, labels, st) : assign_t<128>(a, labels, st);
+}
+
+template <int D>
+static hipError_t bal_assign_t(const PrepArgs& a, int32_t* labels, hipStream_t st) {
+  const int BH = a.B * a.H;
+  hipLaunchKernelGGL(k_quant_centroids<D>, dim3((a.kpad + 3) / 4, BH), dim3(256), 0, st, a.C, a.sV, a.k, a.kpad,
+                     a.Cq, a.cn32);
+  hipLaunchKernelGGL(k_bal_init, dim3((std::max(a.N, a.k) + 255) / 256, BH), dim3(256), 0, st, a.N, a.k, a.kvb,
+                     a.rem, labels);
+  for (int r = 0; r < kBalRounds; ++r) {
+    hipLaunchKernelGGL((k_kmeans_assign<D, true>), dim3((a.N + 255) / 256, BH), dim3(256), 0, st, a.Vq, a.Cq, a.cn32,
+                       a.N, a.kpad, labels, a.prop, a.pdist);
+    if (hipError_t e = launch_sort(a, a.prop, a.perm_tmp, st)) return e;
+    hipLaunchKernelGGL(k_bal_accept<D>, dim3(a.k, BH), dim3(kBalThreads), 0, st, a.perm_tmp, a.counts, a.starts,
+                       a.pdist, a.N, a.k, a.kpad, a.rem, labels, a.Cq, a.cn32);
+  }
+  hipLaunchKernelGGL(k_bal_fill, dim3(BH), dim3(kFillThreads), 0, st, a.rem, a.N, a.k, labels);
+  return hipGetLastError();
+}
+hipError_t launch_bal_assign(const PrepArgs& a, int32_t* labels, hipStream_t st) {
+  return a.d == 64 ? bal_assign_t<64>(a, labels, st) : bal_assign_t<128>(a, labels, st);
 }
 
 template <int D>

@@ -33,6 +33,10 @@ struct PrepArgs {
   int32_t* rank;       // [BH,k]     cluster order (renumbering before the final pass)
   float* Ctmp;         // [BH,k,d]   renumbered centroids
   int32_t* init;       // [BH,k]     seeded initial token indices
+  // balanced clusters (capped assignment)
+  int32_t* prop;       // [BH,N]     proposed cluster of each token in a round (-1: none)
+  int32_t* pdist;      // [BH,N]     squared int8 distance to it
+  int32_t* rem;        // [BH,k]     places left per cluster
 };
 
 struct PrepOut {
@@ -70,6 +74,7 @@ hipError_t launch_quant_v_i8(const PrepArgs& a, hipStream_t st);
 hipError_t launch_init_seeded(const PrepArgs& a, uint64_t seed, int32_t* init, hipStream_t st);
 hipError_t launch_init_centroids(const PrepArgs& a, const int32_t* init, hipStream_t st);
 hipError_t launch_assign(const PrepArgs& a, int32_t* labels, hipStream_t st);
+hipError_t launch_bal_assign(const PrepArgs& a, int32_t* labels, hipStream_t st);
 hipError_t launch_sort(const PrepArgs& a, const int32_t* labels, int32_t* perm, hipStream_t st);
 hipError_t launch_cluster_order(const PrepArgs& a, hipStream_t st);
 hipError_t launch_update(const PrepArgs& a, const int32_t* perm, hipStream_t st);

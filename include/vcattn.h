@@ -113,6 +113,11 @@ typedef struct {
                             /*    seed + 0x9E3779B97F4A7C15 * (b*H + h): draw r_i, */
                             /*    j = i + r_i mod (N - i), swap positions i and j, */
                             /*    for i = 0..k-1; the first k positions are used   */
+  int32_t balanced;         /* 1: balanced clusters sized to the hardware blocks   */
+                            /*    (a blocking variant): n_clusters must be         */
+                            /*    ceil(N / kv_block), cluster c holds kv_block     */
+                            /*    tokens (the last one the tail), so every block   */
+                            /*    is one cluster; see vsmooth_prepare              */
 } vc_config;
 
 /* Bytes of workspace vsmooth_prepare needs (k-means and sort scratch). */
@@ -139,6 +144,13 @@ size_t vc_attention_workspace_bytes(const vc_config* cfg);
  * axis of their int8 codes (exact integer covariance and power iteration;
  * ties to the lower index), so the blocks follow that order; labels and
  * centroids_out use the new numbering.
+ * cfg->balanced == 1 (a blocking variant; the chooseai.io brief, "V-Smooth",
+ * puts similar tokens into the same hardware block): every assignment pass is
+ * capped.  In up to 12 rounds each unassigned token proposes to its nearest
+ * cluster that still has room (ties to the lowest cluster index) and a
+ * cluster with r places left takes the r nearest proposers (exact int8
+ * squared distances, ties to the lowest token index); tokens left after the
+ * rounds fill the remaining places in token order, clusters in index order.
  */
 vc_status vsmooth_prepare(const vc_config* cfg, const void* K, const void* V,
                           const int32_t* init_idx, uint8_t* Kq, float* k_scale,

@@ -46,7 +46,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def cfg(**kw):
-    raw = {f: kw.pop(f) for f in ("cluster_order",) if f in kw}    # set as given, not as a flag
+    raw = {f: kw.pop(f) for f in ("cluster_order", "balanced") if f in kw and kw[f] not in (True, False)}
     base = dict(B=1, H=2, N=1000, d=64, kv_block=64, n_clusters=16, iters=3)
     base.update(kw)
     c = vb.make_config(**base)
@@ -70,6 +70,9 @@ def cfg(**kw):
     (dict(p_mode=-1), VC_ERR_UNSUPPORTED),
     (dict(cluster_order=2), VC_ERR_UNSUPPORTED),
     (dict(N=(1 << 24), d=128, n_clusters=16), VC_ERR_UNSUPPORTED),     # 2^31 bytes of blocked keys per head
+    (dict(balanced=True, n_clusters=15), VC_ERR_INVALID_ARG),           # n_clusters != ceil(N / kv_block) = 16
+    (dict(balanced=2), VC_ERR_INVALID_ARG),
+    (dict(balanced=True, n_clusters=16, vsmooth=False), VC_ERR_INVALID_ARG),
 ])
 def test_invalid_config_rejected_before_launch(lib, kw, status):
     c = cfg(**kw)
@@ -139,8 +142,9 @@ def test_trace_and_init_entry_points_validate(lib):
     assert lib.vc_dbg_init_tokens(ctypes.byref(cfg(n_clusters=0)), P, None) == VC_ERR_INVALID_ARG
 
 
-def test_seed_field_is_last_and_64_bit():
-    # the ABI appends the seed after the 32-bit fields (8-byte aligned)
-    assert vb.VcConfig.seed.offset == 56 and ctypes.sizeof(vb.VcConfig) == 64
+def test_seed_and_balanced_fields():
+    # the seed follows the 32-bit fields (8-byte aligned), then the balanced switch
+    assert vb.VcConfig.seed.offset == 56 and vb.VcConfig.balanced.offset == 64
+    assert ctypes.sizeof(vb.VcConfig) == 72
     c = vb.make_config(1, 1, 10, 64, 64, seed=-1)
     assert c.seed == 2 ** 64 - 1

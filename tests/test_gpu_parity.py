@@ -654,7 +654,67 @@ def test_tiny_value_channel():
     tiles = list(range(oracle.n_q_tiles(700)))
     rows = oracle_rows(w, host, 0, 0, o, tiles)
     ref = np.concatenate([rows[t] for t in tiles])
-    rel5 = np.linalg.norm(O[:, 5] - ref[:, 5]) / np.linalg.norm(ref[:, 5])
-    log(f"  tiny channel: rel-L2 {rel5:.2e} of the channel")
-    assert rel5 <= TIGHT_REL_L2
+    # the channel's values have random signs, so its O is small next to its
+    # inputs: the error is measured against the channel's own max|V|
+    err5 = float(np.max(np.abs(O[:, 5] - ref[:, 5])))
+    vmax5 = float(np.max(np.abs(V[:, 5])))
+    log(f"  tiny channel: max-abs {err5:.3e} = {err5 / vmax5:.2e} of the channel's max|V| ({vmax5:.2e})")
+    assert err5 <= TIGHT_MAXABS_FRAC * vmax5
     check_close(O, ref, float(np.max(np.abs(V))), "tiny channel, all channels")
+
+
+# ------------------------------------------------------------------ balanced clusters (blocking variant)
+@pytest.mark.parametrize("name,H,N,kvb,fmt", [("tiny", 2, None, None, "e4m3"), ("tiny", 1, 1000, 128, "e4m3"),
+                                              ("mid", 1, 5000, None, "mxfp4"), ("tiny", 1, 77, None, "e4m3"),
+                                              ("tiny", 1, 64, None, "e4m3"), ("video", 1, None, None, "e4m3")])
+def test_balanced_prepare_bit_exact(name, H, N, kvb, fmt):
+    """Capped k-means assignment (clusters of kv_block tokens, the last the
+    tail): labels, permutation, blocks, codes and means equal the oracle's
+    bit for bit, every block holds exactly one cluster, and attention on the
+    balanced blocks matches the oracle."""
+    import dataclasses
+    from oracle.kmeans import seeded_init
+    w = inputs.WORKLOADS[name]
+    w = dataclasses.replace(w, kv_block=kvb or w.kv_block)
+    host, dev = gen(w, H=H, N=N)
+    N = N or w.N
+    nblk = vb.balanced_clusters(N, w.kv_block)
+    cfg = vb.make_config(w.B, H, N, w.d, w.kv_block, nblk, w.iters, True, fmt_id(fmt), True, seed=w.seed,
+                         balanced=True)
+    prep = vb.vsmooth_prepare(cfg, dev["K"], dev["V"], None)
+    g = prep_to_numpy(prep, fmt)
+    q, kb, vb_, _ = host
+    O = vb.vc_attn_fwd(cfg, dev["Q"], prep).cpu().numpy()
+    for h in range(H):
+        t0 = time.time()
+        init = seeded_init(w.seed, h, N, nblk)
+        o = oracle.prepare_head(oracle.bf16_to_f64(kb[0, h]), oracle.bf16_to_f64(vb_[0, h]), init, nblk, w.iters,
+                                w.kv_block, fmt, balanced=True)
+        compare_prep(g, o, 0, h, fmt)
+        lab_sorted = g["labels"][0, h][g["perm"][0, h]]
+        assert np.array_equal(lab_sorted, np.arange(N) // w.kv_block), "a block holds more than one cluster"
+        ntile = oracle.n_q_tiles(N)
+        tiles = list(range(ntile)) if ntile <= 8 else [0, ntile // 2, ntile - 1]
+        rows = oracle_rows(w, host, 0, h, o, tiles)
+        vmax = float(np.max(np.abs(oracle.bf16_to_f64(vb_[0, h]))))
+        for t in tiles:
+            check_close(O[0, h, t * 128:min((t + 1) * 128, N)], rows[t], vmax, f"balanced {name} h{h} tile {t}")
+        log(f"  balanced {name} N={N} h{h}: checked in {time.time() - t0:.1f}s")
+
+
+def test_balanced_warm_start_bit_exact():
+    from oracle.kmeans import seeded_init
+    w = inputs.WORKLOADS["tiny"]
+    host, dev = gen(w, H=1, N=900)
+    nblk = vb.balanced_clusters(900, w.kv_block)
+    cfg = vb.make_config(1, 1, 900, w.d, w.kv_block, nblk, w.iters, True, vb.E4M3, True, seed=3, balanced=True)
+    C0 = torch.empty((1, 1, nblk, w.d), dtype=torch.float32, device="cuda")
+    vb.vsmooth_prepare_warm(cfg, dev["K"], dev["V"], centroids_out=C0)
+    cfg1 = vb.make_config(1, 1, 900, w.d, w.kv_block, nblk, 1, True, vb.E4M3, True, seed=3, balanced=True)
+    p1 = vb.vsmooth_prepare_warm(cfg1, dev["K"], dev["V"], init_centroids=C0)
+    g1 = prep_to_numpy(p1, "e4m3")
+    K, V = oracle.bf16_to_f64(host[1][0, 0]), oracle.bf16_to_f64(host[2][0, 0])
+    o0 = oracle.prepare_head(K, V, seeded_init(3, 0, 900, nblk), nblk, w.iters, w.kv_block, balanced=True)
+    assert np.array_equal(C0.cpu().numpy()[0, 0], o0["final_centroids"].astype(np.float32))
+    o1 = oracle.prepare_head(K, V, None, nblk, 1, w.kv_block, init_centroids=C0.cpu().numpy()[0, 0], balanced=True)
+    compare_prep(g1, o1, 0, 0, "e4m3")
