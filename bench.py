@@ -1,10 +1,11 @@
 """Benchmark of the VC-Attention forward pass on one MI355X.
 
 One step = one pass of the whole hot path over the video workload
-(B=1, H=40, N=75,600, d=128; V-Smooth with k=1024, 3 passes, 128-token blocks;
-128-row query tiles; E4M3 residuals): vsmooth_prepare followed by vc_attn_fwd,
-with Q/K/V already resident in HBM.  value = effective attention TFLOPS,
-4*N^2*d*H / (time of one step), prep included.
+(B=1, H=40, N=75,600, d=128; V-Smooth with k=1024 clusters drawn from the
+seed inside the call, 3 passes, 128-token blocks; 128-row query tiles; E4M3
+residuals): vsmooth_prepare followed by vc_attn_fwd, with Q/K/V already
+resident in HBM.  value = effective attention TFLOPS, 4*N^2*d*H / (time of
+one step), prep included.
 
 Also reported: the attention kernel's roofline (FP8 MFMA bound) from HIP
 events on the launch stream, prep time and share, PSNR against fp64 exact
@@ -35,21 +36,28 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def attn_source_sha256() -> str:
+    """SHA-256 over the attention kernel's sources (template header, then the
+    instantiation file)."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("attn_kernel.hpp", "attn_inst.hip"):
+        h.update(open(os.path.join(ROOT, "bit_attention_video_amd", "csrc", f), "rb").read())
+    return h.hexdigest()
+
+
 def traffic_from_profile(workload: str):
     """HBM bytes per attention launch from the committed PMC summary, only if
     it was taken on the current attention kernel source."""
-    import hashlib
     path = os.path.join(ROOT, "profiles", f"attn_fwd_{workload}_hbm_traffic.txt")
-    src = os.path.join(ROOT, "bit_attention_video_amd", "csrc", "attn.hip")
     if not os.path.exists(path):
         return None
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
     vals = {}
     for line in open(path):
         if ":" in line:
             k, v = line.split(":", 1)
             vals[k.strip()] = v.strip()
-    if vals.get("attn_hip_sha256") != sha:
+    if vals.get("attn_kernel_sha256") != attn_source_sha256():
         return None
     try:
         return float(vals["hbm_bytes_per_launch"])
@@ -66,9 +74,10 @@ def cpu_baseline(w, host, n_tiles=32):
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         cores = os.cpu_count() or 1
-    q, k, v, init = host
+    q, k, v, _ = host
     t0 = time.perf_counter()
-    prep = oracle.prepare_head(oracle.bf16_to_f64(k[0, 0]), oracle.bf16_to_f64(v[0, 0]), init[0, 0], w.k,
+    init = oracle.kmeans.seeded_init(w.seed, 0, w.N, w.k)          # the library's draw for head 0
+    prep = oracle.prepare_head(oracle.bf16_to_f64(k[0, 0]), oracle.bf16_to_f64(v[0, 0]), init, w.k,
                                w.iters, w.kv_block, w.v_format)
     t_prep = time.perf_counter() - t0
     ntile = oracle.n_q_tiles(w.N)
@@ -145,11 +154,11 @@ def main():
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
 
     Q, K, V = dev(q), dev(k), dev(v)
-    I = torch.from_numpy(init).cuda()
+    I = None        # the k-means start is drawn from cfg.seed inside the call
     log(f"inputs {w.name} generated and resident in {time.time() - t0:.1f}s")
 
     fmt = vb.E4M3 if w.v_format == "e4m3" else vb.MXFP4
-    cfg = vb.make_config(w.B, w.H, w.N, w.d, w.kv_block, w.k, w.iters, True, fmt, False)
+    cfg = vb.make_config(w.B, w.H, w.N, w.d, w.kv_block, w.k, w.iters, True, fmt, False, seed=w.seed)
     prep = vb.alloc_prepared(cfg, "cuda", with_labels=False)
     ws = torch.empty(vb.workspace_bytes(cfg), dtype=torch.uint8, device="cuda")
     O = vb.alloc_out(cfg)
@@ -203,7 +212,7 @@ def main():
     # reused (no clustering); timed on the same inputs
     cents = torch.empty((w.B, w.H, w.k, w.d), dtype=torch.float32, device="cuda")
     prep_c = vb.vsmooth_prepare_warm(cfg, K, V, init_idx=I, centroids_out=cents, ws=ws, with_labels=False)
-    cfg_w = vb.make_config(w.B, w.H, w.N, w.d, w.kv_block, w.k, 1, True, fmt, False)
+    cfg_w = vb.make_config(w.B, w.H, w.N, w.d, w.kv_block, w.k, 1, True, fmt, False, seed=w.seed)
     cents2 = torch.empty_like(cents)
     perm_keep = prep_c.perm.clone()
 
@@ -228,7 +237,7 @@ def main():
     # ExpCast off (fp32 exp2 + E4M3 cast) on the same prepared blocks: the
     # pages' ablation of ExpCast
     cfg_x = vb.make_config(w.B, w.H, w.N, w.d, w.kv_block, w.k, w.iters, True, fmt, False,
-                           p_mode=vb.EXP2_CAST)
+                           p_mode=vb.EXP2_CAST, seed=w.seed)
     O_x = vb.alloc_out(cfg_x)
     vb.vc_attn_fwd(cfg_x, Q, prep, out=O_x)
     torch.cuda.synchronize()
@@ -243,6 +252,26 @@ def main():
     t_x = float(np.mean(x_ms)) * 1e-3
     log(f"expcast off: attention {t_x * 1e3:.2f} ms")
 
+    # range-shifted ExpCast (the same FMA 64 codes up) on the same blocks
+    cfg_s = vb.make_config(w.B, w.H, w.N, w.d, w.kv_block, w.k, w.iters, True, fmt, False,
+                           p_mode=vb.EXPCAST_SHIFTED, seed=w.seed)
+    O_s = vb.alloc_out(cfg_s)
+    t_s = timed(lambda: vb.vc_attn_fwd(cfg_s, Q, prep, out=O_s))
+    log(f"range-shifted expcast: attention {t_s:.2f} ms")
+
+    # balanced clusters sized to the blocks (one cluster per block): prep and
+    # attention time, PSNR below
+    nb = vb.balanced_clusters(w.N, w.kv_block)
+    cfg_b = vb.make_config(w.B, w.H, w.N, w.d, w.kv_block, nb, w.iters, True, fmt, False, seed=w.seed,
+                           balanced=True)
+    prep_b = vb.alloc_prepared(cfg_b, "cuda", with_labels=False)
+    ws_b = torch.empty(vb.workspace_bytes(cfg_b), dtype=torch.uint8, device="cuda")
+    O_b = vb.alloc_out(cfg_b)
+    t_bp = timed(lambda: vb.vsmooth_prepare(cfg_b, K, V, None, out=prep_b, ws=ws_b))
+    t_ba = timed(lambda: vb.vc_attn_fwd(cfg_b, Q, prep_b, out=O_b))
+    balanced = {"n_clusters": nb, "t_prep_ms": round(t_bp, 3), "t_attn_ms": round(t_ba, 3)}
+    log(f"balanced clusters ({nb}): prep {t_bp:.2f} ms, attention {t_ba:.2f} ms")
+
     # block-scaled residual formats on the same inputs (MX: E8M0 scales per 32
     # sorted tokens and channel, elements E2M1 for MXFP4, E4M3 for MXFP8;
     # NVFP4 style: E4M3 scales per 16 sorted tokens and channel, E2M1
@@ -251,7 +280,7 @@ def main():
     mx, mx_out = {}, {}
     if fmt == vb.E4M3:
         for name, f in (("mxfp4", vb.MXFP4), ("mxfp8", vb.MXFP8), ("nvfp4", vb.NVFP4)):
-            cfg_m = vb.make_config(w.B, w.H, w.N, w.d, w.kv_block, w.k, w.iters, True, f, False)
+            cfg_m = vb.make_config(w.B, w.H, w.N, w.d, w.kv_block, w.k, w.iters, True, f, False, seed=w.seed)
             prep_m = vb.alloc_prepared(cfg_m, "cuda", with_labels=False)
             ws_m = torch.empty(vb.workspace_bytes(cfg_m), dtype=torch.uint8, device="cuda")
             O_m = vb.alloc_out(cfg_m)
@@ -265,7 +294,7 @@ def main():
 
     # clusters renumbered along their principal axis before the final pass
     # (a blocking variant): preparation time, PSNR below
-    cfg_o = vb.make_config(w.B, w.H, w.N, w.d, w.kv_block, w.k, w.iters, True, fmt, False, cluster_order=True)
+    cfg_o = vb.make_config(w.B, w.H, w.N, w.d, w.kv_block, w.k, w.iters, True, fmt, False, cluster_order=True, seed=w.seed)
     prep_o = vb.alloc_prepared(cfg_o, "cuda", with_labels=False)
     O_o = vb.alloc_out(cfg_o)
     t_op = timed(lambda: vb.vsmooth_prepare(cfg_o, K, V, I, out=prep_o, ws=ws))
@@ -287,19 +316,29 @@ def main():
             return O[0, heads].float().cpu().numpy()
 
         O_on = rows(O)
-        cfg_off = vb.make_config(w.B, w.H, w.N, w.d, w.kv_block, w.k, w.iters, False, fmt, False)
+        cfg_off = vb.make_config(w.B, w.H, w.N, w.d, w.kv_block, w.k, w.iters, False, fmt, False, seed=w.seed)
         O_off = rows(vb.vc_attention(cfg_off, Q, K, V, None))
-        outs = {"vsmooth_on": O_on, "vsmooth_off": O_off, "vsmooth_on_expcast_off": rows(O_x)}
+        outs = {"vsmooth_on": O_on, "vsmooth_off": O_off, "vsmooth_on_expcast_off": rows(O_x),
+                "vsmooth_on_expcast_shifted": rows(O_s)}
+        for pm, tag in ((vb.EXP2_CAST, "expcast_off"), (vb.EXPCAST_SHIFTED, "expcast_shifted")):
+            cfg_px = vb.make_config(w.B, w.H, w.N, w.d, w.kv_block, w.k, w.iters, False, fmt, False, p_mode=pm,
+                                    seed=w.seed)
+            outs[f"vsmooth_off_{tag}"] = rows(vb.vc_attention(cfg_px, Q, K, V, None))
+        outs["balanced"] = rows(O_b)
+        for pm, tag in ((vb.EXP2_CAST, "expcast_off"), (vb.EXPCAST_SHIFTED, "expcast_shifted")):
+            cfg_bp = vb.make_config(w.B, w.H, w.N, w.d, w.kv_block, nb, w.iters, True, fmt, False, p_mode=pm,
+                                    seed=w.seed, balanced=True)
+            outs[f"balanced_{tag}"] = rows(vb.vc_attn_fwd(cfg_bp, Q, prep_b))
         outs["vsmooth_on_cluster_order"] = rows(O_o)
         cfg_xo = vb.make_config(w.B, w.H, w.N, w.d, w.kv_block, w.k, w.iters, True, fmt, False,
-                                p_mode=vb.EXP2_CAST, cluster_order=True)
+                                p_mode=vb.EXP2_CAST, cluster_order=True, seed=w.seed)
         outs["vsmooth_on_cluster_order_expcast_off"] = rows(vb.vc_attn_fwd(cfg_xo, Q, prep_o))
         for name, (f, O_m) in mx_out.items():
-            cfg_moff = vb.make_config(w.B, w.H, w.N, w.d, w.kv_block, w.k, w.iters, False, f, False)
+            cfg_moff = vb.make_config(w.B, w.H, w.N, w.d, w.kv_block, w.k, w.iters, False, f, False, seed=w.seed)
             outs[f"{name}_vsmooth_on"] = rows(O_m)
             outs[f"{name}_vsmooth_off"] = rows(vb.vc_attention(cfg_moff, Q, K, V, None))
             cfg_mx = vb.make_config(w.B, w.H, w.N, w.d, w.kv_block, w.k, w.iters, True, f, False,
-                                    p_mode=vb.EXP2_CAST)
+                                    p_mode=vb.EXP2_CAST, seed=w.seed)
             outs[f"{name}_vsmooth_on_expcast_off"] = rows(vb.vc_attention(cfg_mx, Q, K, V, I))
         extra["psnr_db_vs_fp64_exact"] = psnr_report(w, host, outs, heads)
         log(f"psnr {extra['psnr_db_vs_fp64_exact']}")
@@ -341,6 +380,8 @@ def main():
         "pct_mfma_loop_attn": round(100 * achieved / loop_tflops, 2),
         "residual_formats": mx or None,
         "cluster_order": ordered,
+        "expcast_shifted": {"t_attn_ms": round(t_s, 3)},
+        "balanced_clusters": balanced,
         "roofline": {"bound": "mfma", "kernel": "k_attn_fwd", "achieved": round(achieved, 2),
                      "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4),
                      "traffic": traffic},
