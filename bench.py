@@ -133,6 +133,8 @@ def main():
     ap.add_argument("--workload", default="video")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-psnr", action="store_true")
+    ap.add_argument("--no-side", action="store_true",
+                    help="only the timed steps (no MFMA loop, variants, formats or PSNR): for profiler runs")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this size (HBM counter calibration)")
     args = ap.parse_args()
@@ -191,116 +193,120 @@ def main():
     t_prep = float(np.mean(prep_ms)) * 1e-3
     log(f"step {ms_step:.2f} ms (prep {t_prep * 1e3:.2f} ms, attention {t_fwd * 1e3:.2f} ms)")
 
-    # the FP8 MFMA rate this GPU sustains (pure MFMA loop, same launch shape
-    # class): the clock drops under full matrix load, so this is the
-    # attainable ceiling next to the 5.0 PF specification
-    loop_ms = []
-    chk, loop_flops = vb.mfma_loop(2048, 200)
-    torch.cuda.synchronize()
-    for _ in range(3):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        chk, loop_flops = vb.mfma_loop(2048, 2000, chk)
-        e1.record()
+    side = not args.no_side
+    loop_tflops = t_warm = t_reuse = t_x = t_s = None
+    mx, mx_out, ordered, balanced = {}, {}, None, None
+    if side:
+        # the FP8 MFMA rate this GPU sustains (pure MFMA loop, same launch shape
+        # class): the clock drops under full matrix load, so this is the
+        # attainable ceiling next to the 5.0 PF specification
+        loop_ms = []
+        chk, loop_flops = vb.mfma_loop(2048, 200)
         torch.cuda.synchronize()
-        loop_ms.append(e0.elapsed_time(e1))
-    loop_tflops = loop_flops / (min(loop_ms) * 1e-3) / 1e12
-    log(f"fp8 mfma loop {loop_tflops:.1f} TFLOP/s")
-
-    # preparation carried across denoising steps: one warm-started k-means
-    # pass from the previous call's centroids, or the previous permutation
-    # reused (no clustering); timed on the same inputs
-    cents = torch.empty((w.B, w.H, w.k, w.d), dtype=torch.float32, device="cuda")
-    prep_c = vb.vsmooth_prepare_warm(cfg, K, V, init_idx=I, centroids_out=cents, ws=ws, with_labels=False)
-    cfg_w = vb.make_config(w.B, w.H, w.N, w.d, w.kv_block, w.k, 1, True, fmt, False, seed=w.seed)
-    cents2 = torch.empty_like(cents)
-    perm_keep = prep_c.perm.clone()
-
-    def timed(fn, reps=5):
-        fn()
-        torch.cuda.synchronize()
-        ts = []
-        for _ in range(reps):
+        for _ in range(3):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
-            fn()
+            chk, loop_flops = vb.mfma_loop(2048, 2000, chk)
             e1.record()
             torch.cuda.synchronize()
-            ts.append(e0.elapsed_time(e1))
-        return float(np.mean(ts))
+            loop_ms.append(e0.elapsed_time(e1))
+        loop_tflops = loop_flops / (min(loop_ms) * 1e-3) / 1e12
+        log(f"fp8 mfma loop {loop_tflops:.1f} TFLOP/s")
 
-    t_warm = timed(lambda: vb.vsmooth_prepare_warm(cfg_w, K, V, init_centroids=cents, centroids_out=cents2,
-                                                   out=prep_c, ws=ws))
-    t_reuse = timed(lambda: vb.vsmooth_prepare_warm(cfg, K, V, perm_in=perm_keep, out=prep_c, ws=ws))
-    log(f"prep: warm 1 pass {t_warm:.2f} ms, perm reuse {t_reuse:.2f} ms")
+        # preparation carried across denoising steps: one warm-started k-means
+        # pass from the previous call's centroids, or the previous permutation
+        # reused (no clustering); timed on the same inputs
+        cents = torch.empty((w.B, w.H, w.k, w.d), dtype=torch.float32, device="cuda")
+        prep_c = vb.vsmooth_prepare_warm(cfg, K, V, init_idx=I, centroids_out=cents, ws=ws, with_labels=False)
+        cfg_w = vb.make_config(w.B, w.H, w.N, w.d, w.kv_block, w.k, 1, True, fmt, False, seed=w.seed)
+        cents2 = torch.empty_like(cents)
+        perm_keep = prep_c.perm.clone()
 
-    # ExpCast off (fp32 exp2 + E4M3 cast) on the same prepared blocks: the
-    # pages' ablation of ExpCast
-    cfg_x = vb.make_config(w.B, w.H, w.N, w.d, w.kv_block, w.k, w.iters, True, fmt, False,
-                           p_mode=vb.EXP2_CAST, seed=w.seed)
-    O_x = vb.alloc_out(cfg_x)
-    vb.vc_attn_fwd(cfg_x, Q, prep, out=O_x)
-    torch.cuda.synchronize()
-    x_ms = []
-    for _ in range(max(3, args.steps // 2)):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
+        def timed(fn, reps=5):
+            fn()
+            torch.cuda.synchronize()
+            ts = []
+            for _ in range(reps):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                fn()
+                e1.record()
+                torch.cuda.synchronize()
+                ts.append(e0.elapsed_time(e1))
+            return float(np.mean(ts))
+
+        t_warm = timed(lambda: vb.vsmooth_prepare_warm(cfg_w, K, V, init_centroids=cents, centroids_out=cents2,
+                                                       out=prep_c, ws=ws))
+        t_reuse = timed(lambda: vb.vsmooth_prepare_warm(cfg, K, V, perm_in=perm_keep, out=prep_c, ws=ws))
+        log(f"prep: warm 1 pass {t_warm:.2f} ms, perm reuse {t_reuse:.2f} ms")
+
+        # ExpCast off (fp32 exp2 + E4M3 cast) on the same prepared blocks: the
+        # pages' ablation of ExpCast
+        cfg_x = vb.make_config(w.B, w.H, w.N, w.d, w.kv_block, w.k, w.iters, True, fmt, False,
+                               p_mode=vb.EXP2_CAST, seed=w.seed)
+        O_x = vb.alloc_out(cfg_x)
         vb.vc_attn_fwd(cfg_x, Q, prep, out=O_x)
-        e1.record()
         torch.cuda.synchronize()
-        x_ms.append(e0.elapsed_time(e1))
-    t_x = float(np.mean(x_ms)) * 1e-3
-    log(f"expcast off: attention {t_x * 1e3:.2f} ms")
+        x_ms = []
+        for _ in range(max(3, args.steps // 2)):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            vb.vc_attn_fwd(cfg_x, Q, prep, out=O_x)
+            e1.record()
+            torch.cuda.synchronize()
+            x_ms.append(e0.elapsed_time(e1))
+        t_x = float(np.mean(x_ms)) * 1e-3
+        log(f"expcast off: attention {t_x * 1e3:.2f} ms")
 
-    # range-shifted ExpCast (the same FMA 64 codes up) on the same blocks
-    cfg_s = vb.make_config(w.B, w.H, w.N, w.d, w.kv_block, w.k, w.iters, True, fmt, False,
-                           p_mode=vb.EXPCAST_SHIFTED, seed=w.seed)
-    O_s = vb.alloc_out(cfg_s)
-    t_s = timed(lambda: vb.vc_attn_fwd(cfg_s, Q, prep, out=O_s))
-    log(f"range-shifted expcast: attention {t_s:.2f} ms")
+        # range-shifted ExpCast (the same FMA 64 codes up) on the same blocks
+        cfg_s = vb.make_config(w.B, w.H, w.N, w.d, w.kv_block, w.k, w.iters, True, fmt, False,
+                               p_mode=vb.EXPCAST_SHIFTED, seed=w.seed)
+        O_s = vb.alloc_out(cfg_s)
+        t_s = timed(lambda: vb.vc_attn_fwd(cfg_s, Q, prep, out=O_s))
+        log(f"range-shifted expcast: attention {t_s:.2f} ms")
 
-    # balanced clusters sized to the blocks (one cluster per block): prep and
-    # attention time, PSNR below
-    nb = vb.balanced_clusters(w.N, w.kv_block)
-    cfg_b = vb.make_config(w.B, w.H, w.N, w.d, w.kv_block, nb, w.iters, True, fmt, False, seed=w.seed,
-                           balanced=True)
-    prep_b = vb.alloc_prepared(cfg_b, "cuda", with_labels=False)
-    ws_b = torch.empty(vb.workspace_bytes(cfg_b), dtype=torch.uint8, device="cuda")
-    O_b = vb.alloc_out(cfg_b)
-    t_bp = timed(lambda: vb.vsmooth_prepare(cfg_b, K, V, None, out=prep_b, ws=ws_b))
-    t_ba = timed(lambda: vb.vc_attn_fwd(cfg_b, Q, prep_b, out=O_b))
-    balanced = {"n_clusters": nb, "t_prep_ms": round(t_bp, 3), "t_attn_ms": round(t_ba, 3)}
-    log(f"balanced clusters ({nb}): prep {t_bp:.2f} ms, attention {t_ba:.2f} ms")
+        # balanced clusters sized to the blocks (one cluster per block): prep and
+        # attention time, PSNR below
+        nb = vb.balanced_clusters(w.N, w.kv_block)
+        cfg_b = vb.make_config(w.B, w.H, w.N, w.d, w.kv_block, nb, w.iters, True, fmt, False, seed=w.seed,
+                               balanced=True)
+        prep_b = vb.alloc_prepared(cfg_b, "cuda", with_labels=False)
+        ws_b = torch.empty(vb.workspace_bytes(cfg_b), dtype=torch.uint8, device="cuda")
+        O_b = vb.alloc_out(cfg_b)
+        t_bp = timed(lambda: vb.vsmooth_prepare(cfg_b, K, V, None, out=prep_b, ws=ws_b))
+        t_ba = timed(lambda: vb.vc_attn_fwd(cfg_b, Q, prep_b, out=O_b))
+        balanced = {"n_clusters": nb, "t_prep_ms": round(t_bp, 3), "t_attn_ms": round(t_ba, 3)}
+        log(f"balanced clusters ({nb}): prep {t_bp:.2f} ms, attention {t_ba:.2f} ms")
 
-    # block-scaled residual formats on the same inputs (MX: E8M0 scales per 32
-    # sorted tokens and channel, elements E2M1 for MXFP4, E4M3 for MXFP8;
-    # NVFP4 style: E4M3 scales per 16 sorted tokens and channel, E2M1
-    # elements, multiplied as two E4M3 parts): preparation and attention time,
-    # and below the PSNR with V-Smooth on and off
-    mx, mx_out = {}, {}
-    if fmt == vb.E4M3:
-        for name, f in (("mxfp4", vb.MXFP4), ("mxfp8", vb.MXFP8), ("nvfp4", vb.NVFP4)):
-            cfg_m = vb.make_config(w.B, w.H, w.N, w.d, w.kv_block, w.k, w.iters, True, f, False, seed=w.seed)
-            prep_m = vb.alloc_prepared(cfg_m, "cuda", with_labels=False)
-            ws_m = torch.empty(vb.workspace_bytes(cfg_m), dtype=torch.uint8, device="cuda")
-            O_m = vb.alloc_out(cfg_m)
-            t_mp = timed(lambda: vb.vsmooth_prepare(cfg_m, K, V, I, out=prep_m, ws=ws_m))
-            t_ma = timed(lambda: vb.vc_attn_fwd(cfg_m, Q, prep_m, out=O_m))
-            mx[name] = {"t_prep_ms": round(t_mp, 3), "t_attn_ms": round(t_ma, 3),
-                        "attn_tflops": round(w.flops / (t_ma * 1e-3) / 1e12, 2)}
-            mx_out[name] = (f, O_m)
-            del prep_m, ws_m
-            log(f"{name} residuals: prep {t_mp:.2f} ms, attention {t_ma:.2f} ms")
+        # block-scaled residual formats on the same inputs (MX: E8M0 scales per 32
+        # sorted tokens and channel, elements E2M1 for MXFP4, E4M3 for MXFP8;
+        # NVFP4 style: E4M3 scales per 16 sorted tokens and channel, E2M1
+        # elements, multiplied as two E4M3 parts): preparation and attention time,
+        # and below the PSNR with V-Smooth on and off
+        mx, mx_out = {}, {}
+        if fmt == vb.E4M3:
+            for name, f in (("mxfp4", vb.MXFP4), ("mxfp8", vb.MXFP8), ("nvfp4", vb.NVFP4)):
+                cfg_m = vb.make_config(w.B, w.H, w.N, w.d, w.kv_block, w.k, w.iters, True, f, False, seed=w.seed)
+                prep_m = vb.alloc_prepared(cfg_m, "cuda", with_labels=False)
+                ws_m = torch.empty(vb.workspace_bytes(cfg_m), dtype=torch.uint8, device="cuda")
+                O_m = vb.alloc_out(cfg_m)
+                t_mp = timed(lambda: vb.vsmooth_prepare(cfg_m, K, V, I, out=prep_m, ws=ws_m))
+                t_ma = timed(lambda: vb.vc_attn_fwd(cfg_m, Q, prep_m, out=O_m))
+                mx[name] = {"t_prep_ms": round(t_mp, 3), "t_attn_ms": round(t_ma, 3),
+                            "attn_tflops": round(w.flops / (t_ma * 1e-3) / 1e12, 2)}
+                mx_out[name] = (f, O_m)
+                del prep_m, ws_m
+                log(f"{name} residuals: prep {t_mp:.2f} ms, attention {t_ma:.2f} ms")
 
-    # clusters renumbered along their principal axis before the final pass
-    # (a blocking variant): preparation time, PSNR below
-    cfg_o = vb.make_config(w.B, w.H, w.N, w.d, w.kv_block, w.k, w.iters, True, fmt, False, cluster_order=True, seed=w.seed)
-    prep_o = vb.alloc_prepared(cfg_o, "cuda", with_labels=False)
-    O_o = vb.alloc_out(cfg_o)
-    t_op = timed(lambda: vb.vsmooth_prepare(cfg_o, K, V, I, out=prep_o, ws=ws))
-    vb.vc_attn_fwd(cfg_o, Q, prep_o, out=O_o)
-    ordered = {"t_prep_ms": round(t_op, 3)}
-    log(f"cluster order: prep {t_op:.2f} ms")
+        # clusters renumbered along their principal axis before the final pass
+        # (a blocking variant): preparation time, PSNR below
+        cfg_o = vb.make_config(w.B, w.H, w.N, w.d, w.kv_block, w.k, w.iters, True, fmt, False, cluster_order=True, seed=w.seed)
+        prep_o = vb.alloc_prepared(cfg_o, "cuda", with_labels=False)
+        O_o = vb.alloc_out(cfg_o)
+        t_op = timed(lambda: vb.vsmooth_prepare(cfg_o, K, V, I, out=prep_o, ws=ws))
+        vb.vc_attn_fwd(cfg_o, Q, prep_o, out=O_o)
+        ordered = {"t_prep_ms": round(t_op, 3)}
+        log(f"cluster order: prep {t_op:.2f} ms")
 
     if args.calib_copy_mib:
         a = torch.empty(args.calib_copy_mib << 20, dtype=torch.uint8, device="cuda")
@@ -309,7 +315,7 @@ def main():
         torch.cuda.synchronize()
 
     extra = {}
-    if not args.no_psnr:
+    if side and not args.no_psnr:
         heads = [0, w.H - 1]
 
         def rows(O):       # the scored heads only, to the host
@@ -372,15 +378,16 @@ def main():
         "t_prep_ms": round(t_prep * 1e3, 3),
         "t_attn_ms": round(t_fwd * 1e3, 3),
         "prep_over_attn": round(t_prep / t_fwd, 4),
-        "prep_modes_ms": {f"cold_{w.iters}_passes": round(t_prep * 1e3, 3), "warm_1_pass": round(t_warm, 3),
-                          "perm_reuse": round(t_reuse, 3)},
-        "fp8_mfma_loop_tflops": round(loop_tflops, 1),
+        "prep_modes_ms": {f"cold_{w.iters}_passes": round(t_prep * 1e3, 3),
+                          "warm_1_pass": round(t_warm, 3) if side else None,
+                          "perm_reuse": round(t_reuse, 3) if side else None},
+        "fp8_mfma_loop_tflops": round(loop_tflops, 1) if side else None,
         "expcast_off": {"t_attn_ms": round(t_x * 1e3, 3), "attn_tflops": round(flops / t_x / 1e12, 2),
-                        "expcast_speedup": round(t_x / t_fwd, 3)},
-        "pct_mfma_loop_attn": round(100 * achieved / loop_tflops, 2),
+                        "expcast_speedup": round(t_x / t_fwd, 3)} if side else None,
+        "pct_mfma_loop_attn": round(100 * achieved / loop_tflops, 2) if side else None,
         "residual_formats": mx or None,
         "cluster_order": ordered,
-        "expcast_shifted": {"t_attn_ms": round(t_s, 3)},
+        "expcast_shifted": {"t_attn_ms": round(t_s, 3)} if side else None,
         "balanced_clusters": balanced,
         "roofline": {"bound": "mfma", "kernel": "k_attn_fwd", "achieved": round(achieved, 2),
                      "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4),

@@ -135,6 +135,30 @@ def test_vsmooth_and_expcast_fidelity_direction():
     assert oracle.psnr(on, ref) > oracle.psnr(off, ref)
 
 
+def test_vsmooth_direction_with_e4m3_residuals_per_probability_mode():
+    # the headline configuration (E4M3 residuals, d=128, kv_block 128) on a
+    # 2048-token head. With probabilities whose cut-off lies far below the
+    # weights that matter (range-shifted ExpCast, exp2 + E4M3 cast) V-Smooth
+    # raises PSNR, as the pages report. With the literal ExpCast bytes (cut-off
+    # near p = 2^-7 of the running max, p-linear below 2^-6) the per-block
+    # weight error turns coherent once a block is one cluster, and V-Smooth
+    # lowers PSNR on these diffuse synthetic scores.
+    w, Q, K, V, init = _head(2048, 128, 128, k=16)
+    ref = exact_attention(Q, K, V, softmax_scale(128))
+    p = {}
+    for vs in (True, False):
+        prep = oracle.prepare_head(K, V, init, 16, 3, 128, vsmooth_on=vs)
+        for mode in ("expcast", "expcast_shifted", "exp2"):
+            o = oracle.attend_rows(Q, prep, range(oracle.n_q_tiles(2048)), mode=mode)
+            p[vs, mode] = oracle.psnr(np.concatenate([o[t] for t in sorted(o)]), ref)
+    for mode in ("expcast_shifted", "exp2"):
+        assert p[True, mode] > p[False, mode] + 0.5
+    assert p[True, "expcast"] < p[False, "expcast"] - 3.0
+    # shifted bytes cost well under a dB against exp2 + cast; literal ones cost far more
+    assert p[True, "exp2"] - 1.0 < p[True, "expcast_shifted"] <= p[True, "exp2"]
+    assert p[True, "expcast_shifted"] > p[True, "expcast"] + 5.0
+
+
 # ---- ExpCast off: p = E4M3(2^x), x = fma(S, c, -m) ----
 
 def test_exp2cast_bytes_at_integer_exponents():
