@@ -72,5 +72,44 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+# Host-side sanitizers for the validation layer: api.hip holds every check
+# that runs before a launch; its host code is built with AddressSanitizer and
+# UndefinedBehaviorSanitizer (device code unchanged) and linked with the other
+# objects of the last build().
+SAN_FLAGS = ("-Xarch_host -fsanitize=address -Xarch_host -fsanitize=undefined "
+             "-Xarch_host -fno-sanitize-recover=undefined -Xarch_host -fno-omit-frame-pointer").split()
+
+
+def asan_runtime() -> str | None:
+    """The clang AddressSanitizer runtime to preload into an uninstrumented
+    interpreter, or None."""
+    import glob
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    hits = sorted(glob.glob(os.path.join(rocm, "lib", "llvm", "lib", "clang", "*", "lib", "linux",
+                                         "libclang_rt.asan-x86_64.so")))
+    return hits[-1] if hits else None
+
+
+def build_sanitized(out_dir: str) -> str:
+    """libvcattn.so with a sanitized api.hip, into out_dir; needs build() first."""
+    objs = [os.path.join(BUILD_DIR, o) for _, o, _ in _jobs() if o != "api.hip.o"]
+    missing = [o for o in objs if not os.path.exists(o)]
+    if missing:
+        raise FileNotFoundError(f"run build() first: {missing[0]} is missing")
+    os.makedirs(out_dir, exist_ok=True)
+    api = os.path.join(out_dir, "api_san.o")
+    cmd = [hipcc(), *FLAGS, "-O1", "-g", *SAN_FLAGS, "-c", os.path.join(HERE, "csrc", "api.hip"), "-o", api]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for api.hip (sanitized):\n{r.stdout}\n{r.stderr}")
+    lib = os.path.join(out_dir, "libvcattn_san.so")
+    cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *SAN_FLAGS[:4], "-shared-libasan", api, *objs,
+           "-o", lib]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed (sanitized):\n{r.stdout}\n{r.stderr}")
+    return lib
+
+
 if __name__ == "__main__":
     build(verbose=True)
