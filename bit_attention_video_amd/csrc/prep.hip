@@ -616,30 +616,56 @@ __global__ __launch_bounds__(256) void k_sort_scatter(const int32_t* __restrict_
 }
 
 // New centroid = fp32(fp64 mean of the members' values), summed in sorted
-// (= token) order; an empty cluster keeps its centroid.  Member loads are
-// issued 8 at a time (independent), the additions stay in member order.
+// (= token) order; an empty cluster keeps its centroid.  One wave per cluster:
+// lane t owns channels CPL*t .. CPL*t + CPL - 1 (CPL = D / 64) and reads them
+// with one 2- or 4-byte load per member row, so a wave instruction covers a
+// whole 2D-byte row.  Members come in chunks of U: the chunk's U row loads are
+// all issued before its additions, which stay in member order.
 template <int D>
-__global__ __launch_bounds__(D) void k_kmeans_update(const uint16_t* __restrict__ V, const int32_t* __restrict__ perm,
-                                                     const int32_t* __restrict__ counts,
-                                                     const int32_t* __restrict__ starts, int N, int k,
-                                                     float* __restrict__ C) {
-  const int bh = blockIdx.y, i = blockIdx.x, c = threadIdx.x;
+__global__ __launch_bounds__(64) void k_kmeans_update(const uint16_t* __restrict__ V, const int32_t* __restrict__ perm,
+                                                      const int32_t* __restrict__ counts,
+                                                      const int32_t* __restrict__ starts, int N, int k,
+                                                      float* __restrict__ C) {
+  constexpr int CPL = D / 64;
+  constexpr int U = 32;
+  static_assert(CPL == 1 || CPL == 2, "64 or 128 channels");
+  const int bh = blockIdx.y, i = blockIdx.x, t = threadIdx.x;
   const int cnt = counts[static_cast<size_t>(bh) * k + i];
   if (cnt == 0) return;
   const int s = starts[static_cast<size_t>(bh) * k + i];
   const int32_t* pp = perm + static_cast<size_t>(bh) * N + s;
-  const uint16_t* vv = V + static_cast<size_t>(bh) * N * D + c;
-  double sum = 0.0;
+  const uint16_t* vv = V + static_cast<size_t>(bh) * N * D + CPL * t;
+  double sum[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) sum[c] = 0.0;
+  auto row = [&](int j) -> uint32_t {
+    const uint16_t* r = vv + static_cast<size_t>(pp[j]) * D;
+    if constexpr (CPL == 2) return *reinterpret_cast<const uint32_t*>(r);
+    else return *r;
+  };
+  auto add = [&](uint32_t x) {
+    sum[0] += static_cast<double>(bf16_to_f32(static_cast<uint16_t>(x & 0xffffu)));
+    if constexpr (CPL == 2) sum[1] += static_cast<double>(bf16_to_f32(static_cast<uint16_t>(x >> 16)));
+  };
   int j = 0;
-  for (; j + 8 <= cnt; j += 8) {
-    float x[8];
+  for (; j + U <= cnt; j += U) {
+    uint32_t x[U];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) x[u] = bf16_to_f32(vv[static_cast<size_t>(pp[j + u]) * D]);
+    for (int u = 0; u < U; ++u) x[u] = row(j + u);
 #pragma unroll
-    for (int u = 0; u < 8; ++u) sum += static_cast<double>(x[u]);
+    for (int u = 0; u < U; ++u) add(x[u]);
   }
-  for (; j < cnt; ++j) sum += static_cast<double>(bf16_to_f32(vv[static_cast<size_t>(pp[j]) * D]));
-  C[(static_cast<size_t>(bh) * k + i) * D + c] = static_cast<float>(sum / static_cast<double>(cnt));
+  for (; j + 8 <= cnt; j += 8) {
+    uint32_t x[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) x[u] = row(j + u);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) add(x[u]);
+  }
+  for (; j < cnt; ++j) add(row(j));
+  float* out = C + (static_cast<size_t>(bh) * k + i) * D + CPL * t;
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) out[c] = static_cast<float>(sum[c] / static_cast<double>(cnt));
 }
 
 __global__ void k_iota(int32_t* __restrict__ perm, int N, size_t total) {
@@ -1299,7 +1325,7 @@ hipError_t launch_sort(const PrepArgs& a, const int32_t* labels, int32_t* perm, 
 
 template <int D>
 static hipError_t update_t(const PrepArgs& a, const int32_t* perm, hipStream_t st) {
-  hipLaunchKernelGGL((k_kmeans_update<D>), dim3(a.k, a.B * a.H), dim3(D), 0, st, a.V, perm, a.counts, a.starts,
+  hipLaunchKernelGGL((k_kmeans_update<D>), dim3(a.k, a.B * a.H), dim3(64), 0, st, a.V, perm, a.counts, a.starts,
                      a.N, a.k, a.C);
   return hipGetLastError();
 }
