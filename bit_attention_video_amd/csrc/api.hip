@@ -226,6 +226,7 @@ const char* vc_status_str(vc_status s) {
 }
 
 const char* vc_last_error(void) { return g_err.c_str(); }
+const char* vc_last_hip_error(void) { return g_err.c_str(); }
 
 size_t vc_prepare_workspace_bytes(const vc_config* cfg) {
   Dims D;
@@ -251,6 +252,8 @@ size_t vc_attention_workspace_bytes(const vc_config* cfg) {
   cv.take<int32_t>(s.perm);
   return cv.off + 256;
 }
+
+size_t vc_workspace_bytes(const vc_config* cfg) { return vc_attention_workspace_bytes(cfg); }
 
 vc_status vsmooth_prepare(const vc_config* cfg, const void* K, const void* V, const int32_t* init_idx,
                           uint8_t* Kq, float* k_scale, uint8_t* Vres, void* v_scale, float* v_mean,

@@ -124,6 +124,10 @@ typedef struct {
 size_t vc_prepare_workspace_bytes(const vc_config* cfg);
 /* Bytes of workspace vc_attention needs (prepare scratch + blocked K/V). */
 size_t vc_attention_workspace_bytes(const vc_config* cfg);
+/* Bytes of workspace enough for every call that takes one (vsmooth_prepare,
+ * vsmooth_prepare_warm, vc_attention): equals vc_attention_workspace_bytes;
+ * 0 for an invalid configuration. */
+size_t vc_workspace_bytes(const vc_config* cfg);
 
 /*
  * vsmooth_prepare: V-Smooth and K smoothing (chooseai.io brief, "V-Smooth").
@@ -248,6 +252,8 @@ size_t vc_noalloc_scratch_bytes(void);
 const char* vc_status_str(vc_status s);
 /* Message of the last failure on the calling thread ("" if none). */
 const char* vc_last_error(void);
+/* The same message as vc_last_error (HIP failures carry the HIP error string). */
+const char* vc_last_hip_error(void);
 
 /* ---- test entry points (same kernels as the path above) --------------------
  * vc_dbg_expcast: out[i] = the ExpCast byte the attention kernel computes from

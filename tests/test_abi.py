@@ -35,8 +35,23 @@ def test_header_declares_expected_entry_points():
     for want in ("vsmooth_prepare", "vc_attn_fwd", "vc_attention", "vc_prepare_workspace_bytes",
                  "vc_attention_workspace_bytes", "vc_status_str", "vc_last_error", "vc_dbg_expcast",
                  "vc_dbg_kmeans_assign", "vc_dbg_sort", "vc_mfma_loop", "vc_dbg_exp2cast",
-                 "vsmooth_prepare_warm", "vc_dbg_attn_trace", "vc_dbg_init_tokens"):
+                 "vsmooth_prepare_warm", "vc_dbg_attn_trace", "vc_dbg_init_tokens", "vc_workspace_bytes",
+                 "vc_last_hip_error"):
         assert want in names, want
+
+
+def test_workspace_bytes_covers_every_call_and_error_aliases(lib):
+    c = cfg()
+    L = vb.lib()
+    L.vc_workspace_bytes.restype = ctypes.c_size_t
+    L.vc_attention_workspace_bytes.restype = ctypes.c_size_t
+    L.vc_prepare_workspace_bytes.restype = ctypes.c_size_t
+    w = L.vc_workspace_bytes(ctypes.byref(c))
+    assert w == L.vc_attention_workspace_bytes(ctypes.byref(c)) >= L.vc_prepare_workspace_bytes(ctypes.byref(c)) > 0
+    assert L.vc_workspace_bytes(ctypes.byref(cfg(d=96))) == 0
+    L.vc_last_error.restype = ctypes.c_char_p
+    L.vc_last_hip_error.restype = ctypes.c_char_p
+    assert L.vc_last_hip_error() == L.vc_last_error()
 
 
 def test_library_exports_every_declared_symbol(lib):
