@@ -134,7 +134,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-psnr", action="store_true")
     ap.add_argument("--no-side", action="store_true",
-                    help="only the timed steps (no MFMA loop, variants, formats or PSNR): for profiler runs")
+                    help="no side measurements (MFMA loop, variants, formats); PSNR then covers the probability-byte "
+                         "modes only")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this size (HBM counter calibration)")
     args = ap.parse_args()
@@ -315,7 +316,7 @@ def main():
         torch.cuda.synchronize()
 
     extra = {}
-    if side and not args.no_psnr:
+    if not args.no_psnr:
         heads = [0, w.H - 1]
 
         def rows(O):       # the scored heads only, to the host
@@ -324,8 +325,18 @@ def main():
         O_on = rows(O)
         cfg_off = vb.make_config(w.B, w.H, w.N, w.d, w.kv_block, w.k, w.iters, False, fmt, False, seed=w.seed)
         O_off = rows(vb.vc_attention(cfg_off, Q, K, V, None))
-        outs = {"vsmooth_on": O_on, "vsmooth_off": O_off, "vsmooth_on_expcast_off": rows(O_x),
-                "vsmooth_on_expcast_shifted": rows(O_s)}
+        outs = {"vsmooth_on": O_on, "vsmooth_off": O_off}
+        if not side:
+            # the probability-byte modes on the same prepared blocks
+            for pm, tag in ((vb.EXP2_CAST, "expcast_off"), (vb.EXPCAST_SHIFTED, "expcast_shifted")):
+                cfg_pm = vb.make_config(w.B, w.H, w.N, w.d, w.kv_block, w.k, w.iters, True, fmt, False, p_mode=pm,
+                                        seed=w.seed)
+                outs[f"vsmooth_on_{tag}"] = rows(vb.vc_attn_fwd(cfg_pm, Q, prep))
+            extra["psnr_db_vs_fp64_exact"] = psnr_report(w, host, outs, heads)
+            log(f"psnr {extra['psnr_db_vs_fp64_exact']}")
+    if side and not args.no_psnr:
+        outs["vsmooth_on_expcast_off"] = rows(O_x)
+        outs["vsmooth_on_expcast_shifted"] = rows(O_s)
         for pm, tag in ((vb.EXP2_CAST, "expcast_off"), (vb.EXPCAST_SHIFTED, "expcast_shifted")):
             cfg_px = vb.make_config(w.B, w.H, w.N, w.d, w.kv_block, w.k, w.iters, False, fmt, False, p_mode=pm,
                                     seed=w.seed)
