@@ -105,6 +105,11 @@ struct AttnTile {
   static constexpr int SBYTES = VF != 0 ? (KVB / 32) * D : 0;    // E8M0 scales (MX formats)
   static constexpr int STAGE = KBYTES + VBYTES + (SBYTES + 1023) / 1024 * 1024;
   static constexpr int MSLOT = 8;         // blocks per mean-restoration flush
+  // NVFP4-style residuals take two P.V MFMAs per tile; interleaving the next
+  // block's scores with them would keep both score and byte registers live
+  // past the register file, so those blocks run in two phases (scores and
+  // ExpCast, then row sums and P.V) with K and V staged one block ahead
+  static constexpr bool SPLIT = VF == 3;
   static constexpr int NTH = kAttnThreads;
   static constexpr int NWV = NTH / 64;    // waves, 32 query rows each
   static constexpr int ROWS = NWV * 32;   // query rows per workgroup (NWV / 4 scale tiles)
@@ -352,6 +357,49 @@ struct TraceRow {
   int row = 0;            // query row of this lane inside the workgroup
 };
 
+// Masks the padded keys of the tail block, takes the row maximum across the
+// two lane groups, moves the running maximum m (and with it the accumulator,
+// the pending row sums and l) to max(m, c_b * rowmax S), and returns the word
+// arguments of the probability bytes: ExpCast x = fma(S, 8c, 56 + beta - 8m),
+// ExpCast off x = fma(S, c, -m), then exp2.  pmax: the per-lane maximum of S
+// (recomputed here for the tail block).
+template <int D, int KVB, int VF, int PM, bool MASK>
+__device__ __forceinline__ void softmax_update(SoftmaxState<D / 32, AttnTile<D, KVB, VF>::MSLOT>& st, v16f* S,
+                                               float& pmax, float cb, float kc, int nvalid, int g, float& A8,
+                                               float& Bq) {
+  using TT = AttnTile<D, KVB, VF>;
+  constexpr int NKT = TT::NKT, NDT = TT::NDT, MS = TT::MSLOT;
+  if constexpr (MASK) {
+#pragma unroll
+    for (int kt = 0; kt < NKT; ++kt) {
+      const int lim = nvalid - ((kt >> 1) * 64 + (kt & 1) * 32 + 16 * g);   // keep r < lim
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (r >= lim) S[kt][r] = -__builtin_inff();
+    }
+    pmax = tile_max(S[0]);
+#pragma unroll
+    for (int kt = 1; kt < NKT; ++kt) pmax = tile_max(S[kt], pmax);
+  }
+  const float mx = max_xor32(pmax);
+  const float m_new = fmaxf(st.m_run, cb * mx);
+  Bq = PM == 0 ? __builtin_fmaf(-8.0f, m_new, kc) : -m_new;
+  A8 = PM == 0 ? 8.0f * cb : cb;
+
+  // the accumulator moves to the new maximum before this block's P.V lands
+  if (__builtin_amdgcn_ballot_w64(m_new > st.m_run)) {
+    const float alpha = exp2f(st.m_run - m_new);
+#pragma unroll
+    for (int T = 0; T < NDT; ++T)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st.acc[T][r] *= alpha;
+#pragma unroll
+    for (int i = 0; i < MS; ++i) st.RS[i] *= alpha;
+    st.l_run *= alpha;
+  }
+  st.m_run = m_new;
+}
+
 // Row maximum, ExpCast, row sums and P.V of block b from its scores S, with
 // the next block's S^T (into the same registers, tile by tile) interleaved
 // as planned above.  pmax: per-lane maximum of S (before the cross-lane
@@ -380,37 +428,9 @@ __device__ __forceinline__ void block_step(
   const int lo_one = rb ? 0 : 0x22222222, hi_one = rb ? 0x22222222 : 0;
   const v8i ones = {lo_one, lo_one, hi_one, hi_one, 0, 0, 0, 0};
 
-  if constexpr (MASK) {
-#pragma unroll
-    for (int kt = 0; kt < NKT; ++kt) {
-      const int lim = nvalid - ((kt >> 1) * 64 + (kt & 1) * 32 + 16 * g);   // keep r < lim
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (r >= lim) S[kt][r] = -__builtin_inff();
-    }
-    pmax = tile_max(S[0]);
-#pragma unroll
-    for (int kt = 1; kt < NKT; ++kt) pmax = tile_max(S[kt], pmax);
-  }
-  const float mx = max_xor32(pmax);
-  const float m_new = fmaxf(st.m_run, cb * mx);
-  // word arguments: ExpCast x = fma(S, 8c, 56 + beta - 8m); ExpCast off
-  // x = fma(S, c, -m), then exp2
-  const float Bq = PM == 0 ? __builtin_fmaf(-8.0f, m_new, kc) : -m_new;
-  const float A8 = PM == 0 ? 8.0f * cb : cb;
-
-  // the accumulator moves to the new maximum before this block's P.V lands
-  if (__builtin_amdgcn_ballot_w64(m_new > st.m_run)) {
-    const float alpha = exp2f(st.m_run - m_new);
-#pragma unroll
-    for (int T = 0; T < NDT; ++T)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) st.acc[T][r] *= alpha;
-#pragma unroll
-    for (int i = 0; i < MS; ++i) st.RS[i] *= alpha;
-    st.l_run *= alpha;
-  }
-  st.m_run = m_new;
+  float A8, Bq;
+  softmax_update<D, KVB, VF, PM, MASK>(st, S, pmax, cb, kc, nvalid, g, A8, Bq);
+  [[maybe_unused]] const float m_new = st.m_run;
   // lane (g, col) holds key 32*kt + 16*g + r of block b in S[kt][r] (sorted order)
   [[maybe_unused]] const size_t trow = static_cast<size_t>(b) * TT::ROWS + tr.row;
   if constexpr (TR) {
@@ -551,11 +571,91 @@ __device__ __forceinline__ void block_step(
   for (int i = 0; i < MS; ++i) st.RS[i] = i == slot ? rs : st.RS[i];
 }
 
+// Block b in two phases (the NVFP4-style residuals): S^T of block b from its
+// staged K, the softmax update and ExpCast of all its scores, then the row
+// sums and P.V (two scaled MFMAs per channel tile and 64 keys: the high and
+// the low E4M3 parts under one E8M0 byte).  Only the accumulator, the bytes
+// and one operand pair stay live in the second phase.  hook(i) runs right
+// after matrix instruction i is issued (QK^T: 0 .. NKT*NDC-1, then per 64
+// keys the row sum and the P.V MFMAs).
+template <int D, int KVB, int VF, int PM, bool MASK, typename Hook>
+__device__ __forceinline__ void block_step_split(
+    Hook&& hook, SoftmaxState<D / 32, AttnTile<D, KVB, VF>::MSLOT>& st, v16f* S, const uint8_t* sV,
+    const uint8_t* sK, const LaneOffsets<D, KVB, VF>& lo, const v8i* qb, float cb, float kc, int b, int nvalid,
+    int g, int col) {
+  using TT = AttnTile<D, KVB, VF>;
+  constexpr int NKT = TT::NKT, NKS = TT::NKS, NDT = TT::NDT, NDC = TT::NDC, VROW = TT::VROW, MS = TT::MSLOT;
+  constexpr int NQK = NKT * NDC, NPV = 2 * NDT;
+  static_assert(VF == 3, "the two-phase step serves the two-part residuals");
+  const uint8_t* sS = sV + TT::VBYTES;
+  // row-sum operand: see block_step
+  const int rb = (col >> 2) & 1;
+  const int lo_one = rb ? 0 : 0x22222222, hi_one = rb ? 0x22222222 : 0;
+  const v8i ones = {lo_one, lo_one, hi_one, hi_one, 0, 0, 0, 0};
+
+  // phase 1: scores, softmax update, bytes
+  static_for<NQK>([&](auto ic) {
+    constexpr int i = decltype(ic)::value, kt = i / NDC, c = i % NDC;
+    const v8i a = join8(*reinterpret_cast<const uint4*>(sK + kt * 32 * D + lo.k_rd[c][0]),
+                        *reinterpret_cast<const uint4*>(sK + kt * 32 * D + lo.k_rd[c][1]));
+    S[kt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qb[c], c == 0 ? v16f{} : S[kt], 0, 0, 0, 0, 0, 0);
+    hook(ic);
+  });
+  float pmax = tile_max(S[0]);
+#pragma unroll
+  for (int kt = 1; kt < NKT; ++kt) pmax = tile_max(S[kt], pmax);
+  float A8, Bq;
+  softmax_update<D, KVB, VF, PM, MASK>(st, S, pmax, cb, kc, nvalid, g, A8, Bq);
+  v8i P[NKS];
+#pragma unroll
+  for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      P[kt / 2][4 * (kt % 2) + q] = static_cast<int>(
+          pword4<PM>(S[kt][4 * q], S[kt][4 * q + 1], S[kt][4 * q + 2], S[kt][4 * q + 3], A8, Bq));
+
+  // phase 2: row sums and P.V; operand u of a 64-key step is channel tile
+  // u/2, part u%2 (0 high, 1 low), loaded one MFMA ahead
+  v4f rsum;
+  auto vopnd = [&](int sj, int u) __attribute__((always_inline)) -> v8i {
+    const uint8_t* vb = sV + (u % 2) * TT::VHALF + (sj * D + 32 * (u / 2)) * VROW;
+    return join8(*reinterpret_cast<const uint4*>(vb + lo.v_rd[0]), *reinterpret_cast<const uint4*>(vb + lo.v_rd[1]));
+  };
+  static_for<NKS>([&](auto sc) {
+    constexpr int sj = decltype(sc)::value;
+    // lane group g's E8M0 bytes cover sorted positions [32g, 32g+32) of the
+    // step, one byte per channel tile (op_sel picks it)
+    const uint8_t* scp = sS + (2 * sj + g) * D + col * NDT;
+    int osc;
+    if constexpr (NDT == 4) osc = *reinterpret_cast<const int*>(scp);
+    else osc = *reinterpret_cast<const uint16_t*>(scp);
+    v8i cur = vopnd(sj, 0);
+    constexpr int base = NQK + sj * (1 + NPV);
+    rsum = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ones, P[sj], sj == 0 ? v4f{} : rsum, 4, 0, 0, 127, 0,
+                                                            127);
+    hook(std::integral_constant<int, base>{});
+    static_for<NPV>([&](auto uc) {
+      constexpr int u = decltype(uc)::value, T = u / 2;
+      const v8i nxt = u + 1 < NPV ? vopnd(sj, u + 1) : cur;
+      st.acc[T] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cur, P[sj], st.acc[T], 0, 0, T, osc, 0, 127);
+      hook(std::integral_constant<int, base + 1 + u>{});
+      cur = nxt;
+    });
+  });
+  const float rs = rsum[0];
+  st.l_run += rs;
+  const int slot = b & (MS - 1);
+#pragma unroll
+  for (int i = 0; i < MS; ++i) st.RS[i] = i == slot ? rs : st.RS[i];
+}
+
 // The fused forward.  Per workgroup 256 query rows (8 waves x 32 rows, two
 // 128-row tiles with a query scale each), so every staged K/V block serves
 // 256 queries.  Block b+1's S^T MFMAs run inside block b's step, so each block
 // starts with its scores ready: K is staged two blocks ahead and V one block
-// ahead, each in a two-slot LDS ring filled by direct buffer->LDS loads.
+// ahead, each in a two-slot LDS ring filled by direct buffer->LDS loads.  The
+// NVFP4-style residuals (two P.V MFMAs per tile) take the two-phase step
+// instead, with K and V both staged one block ahead.
 // TR = 1: the test-only trace instantiation (same arithmetic; the workgroup
 // with logical index p.tr_wg also writes its TraceRow entries).
 template <int D, int KVB, int VF, int O32, int PM, int TR>
@@ -638,7 +738,9 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_fwd(AttnArgs p) {
   using RB = std::integral_constant<int, 64>;
   stage_k(0, P0{}, RA{}, RB{});
   stage_v(0, P0{}, RA{}, RB{});
-  if (nblk > 1) stage_k(1, P1{}, RA{}, RB{});
+  if constexpr (!TT::SPLIT) {
+    if (nblk > 1) stage_k(1, P1{}, RA{}, RB{});
+  }
 
   for (int i = threadIdx.x; i < 2 * 2 * D * MS; i += TT::NTH) sM[i] = 0;
   float colv = 1.0f;
@@ -716,12 +818,15 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_fwd(AttnArgs p) {
   __syncthreads();
 
   v16f S[NKT];
-  qk_block<D, KVB, VF>(S, sK0, lo, qb);
-  float pmax = tile_max(S[0]);
+  float pmax = 0.0f;
+  if constexpr (!TT::SPLIT) {
+    qk_block<D, KVB, VF>(S, sK0, lo, qb);
+    pmax = tile_max(S[0]);
 #pragma unroll
-  for (int kt = 1; kt < NKT; ++kt) pmax = tile_max(S[kt], pmax);
-  // every wave has read K_0 before the first step refills its slot
-  __syncthreads();
+    for (int kt = 1; kt < NKT; ++kt) pmax = tile_max(S[kt], pmax);
+    // every wave has read K_0 before the first step refills its slot
+    __syncthreads();
+  }
 
   const int ntail = N - (nblk - 1) * KVB;            // real keys of the last block
   const int nfull = ntail < KVB ? nblk - 1 : nblk;   // blocks without padded keys
@@ -745,28 +850,53 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_fwd(AttnArgs p) {
       k_next = ks[b + 1];
       if (threadIdx.x < D) mnext = vm[static_cast<size_t>(b + 1) * D + threadIdx.x];
     }
-    // K round r behind matrix instruction 4r, V round r behind 4r+2
-    auto hook = [&](auto ic) {
-      constexpr int i = decltype(ic)::value;
-      static_for<LO::KR>([&](auto rc) {
-        constexpr int r = decltype(rc)::value;
-        constexpr int at = 4 * r;
-        if constexpr (i == (at < PL::M ? at : PL::M - 1)) {
-          if (b + 2 < nblk) stage_k(b + 2, par, rc, std::integral_constant<int, r + 1>{});
-        }
-      });
-      static_for<LO::VR>([&](auto rc) {
-        constexpr int r = decltype(rc)::value;
-        constexpr int at = 4 * r + 2;
-        if constexpr (i == (at < PL::M ? at : PL::M - 1)) {
-          if (b + 1 < nblk) stage_v(b + 1, Q{}, rc, std::integral_constant<int, r + 1>{});
-        }
-      });
-    };
-    // softmax and P.V of block b, with block b+1's scores made in between
-    // (for the last block they come from a stale slot and are discarded)
-    block_step<D, KVB, VF, PM, MASK, TR != 0>(hook, st, S, pmax, vslot(par), kslot(Q{}), lo, qb, cq * k_cur, p.kc,
-                                              b, MASK ? ntail : KVB, g, col, tr);
+    if constexpr (TT::SPLIT) {
+      // two-phase step: K_{b+1} and V_{b+1} into the other slots, K round r
+      // behind matrix instruction 4r, V round r behind 4r+2
+      constexpr int M = NKT * NDC + TT::NKS * (1 + 2 * NDT);
+      auto hook = [&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        static_for<LO::KR>([&](auto rc) {
+          constexpr int r = decltype(rc)::value;
+          constexpr int at = 4 * r;
+          if constexpr (i == (at < M ? at : M - 1)) {
+            if (b + 1 < nblk) stage_k(b + 1, Q{}, rc, std::integral_constant<int, r + 1>{});
+          }
+        });
+        static_for<LO::VR>([&](auto rc) {
+          constexpr int r = decltype(rc)::value;
+          constexpr int at = 4 * r + 2;
+          if constexpr (i == (at < M ? at : M - 1)) {
+            if (b + 1 < nblk) stage_v(b + 1, Q{}, rc, std::integral_constant<int, r + 1>{});
+          }
+        });
+      };
+      block_step_split<D, KVB, VF, PM, MASK>(hook, st, S, vslot(par), kslot(par), lo, qb, cq * k_cur, p.kc, b,
+                                             MASK ? ntail : KVB, g, col);
+    } else {
+      // K round r behind matrix instruction 4r, V round r behind 4r+2
+      auto hook = [&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        static_for<LO::KR>([&](auto rc) {
+          constexpr int r = decltype(rc)::value;
+          constexpr int at = 4 * r;
+          if constexpr (i == (at < PL::M ? at : PL::M - 1)) {
+            if (b + 2 < nblk) stage_k(b + 2, par, rc, std::integral_constant<int, r + 1>{});
+          }
+        });
+        static_for<LO::VR>([&](auto rc) {
+          constexpr int r = decltype(rc)::value;
+          constexpr int at = 4 * r + 2;
+          if constexpr (i == (at < PL::M ? at : PL::M - 1)) {
+            if (b + 1 < nblk) stage_v(b + 1, Q{}, rc, std::integral_constant<int, r + 1>{});
+          }
+        });
+      };
+      // softmax and P.V of block b, with block b+1's scores made in between
+      // (for the last block they come from a stale slot and are discarded)
+      block_step<D, KVB, VF, PM, MASK, TR != 0>(hook, st, S, pmax, vslot(par), kslot(Q{}), lo, qb, cq * k_cur,
+                                                p.kc, b, MASK ? ntail : KVB, g, col, tr);
+    }
     if ((b & (MS - 1)) == MS - 1 || b == nblk - 1)
       mean_flush<D, KVB, VF>(st, sM + ((b >> 3) & 1) * 2 * D * MS, g, col);
     if (b + 1 < nblk && threadIdx.x < D) {
