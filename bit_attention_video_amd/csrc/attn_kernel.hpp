@@ -382,13 +382,15 @@ __device__ __forceinline__ void softmax_update(SoftmaxState<D / 32, AttnTile<D, 
     for (int kt = 1; kt < NKT; ++kt) pmax = tile_max(S[kt], pmax);
   }
   const float mx = max_xor32(pmax);
-  const float m_new = fmaxf(st.m_run, cb * mx);
+  const float m_new = fmax_ieee(st.m_run, cb * mx);   // neither is NaN
   Bq = PM == 0 ? __builtin_fmaf(-8.0f, m_new, kc) : -m_new;
   A8 = PM == 0 ? 8.0f * cb : cb;
 
   // the accumulator moves to the new maximum before this block's P.V lands
   if (__builtin_amdgcn_ballot_w64(m_new > st.m_run)) {
-    const float alpha = exp2f(st.m_run - m_new);
+    // the hardware exponential (one instruction; for a step below 2^-126
+    // it may return 0 where a correctly rounded exp2 gives a subnormal)
+    const float alpha = __builtin_amdgcn_exp2f(st.m_run - m_new);
 #pragma unroll
     for (int T = 0; T < NDT; ++T)
 #pragma unroll
@@ -409,7 +411,7 @@ template <int D, int KVB, int VF, int PM, bool MASK, bool TR, typename Hook>
 __device__ __forceinline__ void block_step(
     Hook&& hook, SoftmaxState<D / 32, AttnTile<D, KVB, VF>::MSLOT>& st, v16f* S, float& pmax,
     const uint8_t* sV, const uint8_t* sKn, const LaneOffsets<D, KVB, VF>& lo, const v8i* qb,
-    float cb, float kc, int b, int nvalid, int g, int col, const TraceRow& tr) {
+    float cb, float kc, int b, int slot, int nvalid, int g, int col, const TraceRow& tr) {
   using TT = AttnTile<D, KVB, VF>;
   using PL = StepPlan<D, KVB, VF>;
   static_assert(PL::valid(), "step plan overwrites a score tile before its bytes are made");
@@ -566,7 +568,6 @@ __device__ __forceinline__ void block_step(
     }
   }
   st.l_run += rs;
-  const int slot = b & (MS - 1);
 #pragma unroll
   for (int i = 0; i < MS; ++i) st.RS[i] = i == slot ? rs : st.RS[i];
 }
@@ -581,7 +582,7 @@ __device__ __forceinline__ void block_step(
 template <int D, int KVB, int VF, int PM, bool MASK, typename Hook>
 __device__ __forceinline__ void block_step_split(
     Hook&& hook, SoftmaxState<D / 32, AttnTile<D, KVB, VF>::MSLOT>& st, v16f* S, const uint8_t* sV,
-    const uint8_t* sK, const LaneOffsets<D, KVB, VF>& lo, const v8i* qb, float cb, float kc, int b, int nvalid,
+    const uint8_t* sK, const LaneOffsets<D, KVB, VF>& lo, const v8i* qb, float cb, float kc, int slot, int nvalid,
     int g, int col) {
   using TT = AttnTile<D, KVB, VF>;
   constexpr int NKT = TT::NKT, NKS = TT::NKS, NDT = TT::NDT, NDC = TT::NDC, VROW = TT::VROW, MS = TT::MSLOT;
@@ -644,7 +645,6 @@ __device__ __forceinline__ void block_step_split(
   });
   const float rs = rsum[0];
   st.l_run += rs;
-  const int slot = b & (MS - 1);
 #pragma unroll
   for (int i = 0; i < MS; ++i) st.RS[i] = i == slot ? rs : st.RS[i];
 }
@@ -839,7 +839,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_fwd(AttnArgs p) {
   // step, one round (one instruction per wave) behind every second matrix
   // instruction: issued together at the step's start, the eight waves' loads
   // queue up and hold the waves back.
-  auto step = [&](const int b, auto par, auto masked) {
+  auto step = [&](const int b, auto par, auto masked, const int slot) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(masked)::value;
     constexpr int PAR = decltype(par)::value;
     using Q = std::integral_constant<int, 1 - PAR>;
@@ -871,7 +871,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_fwd(AttnArgs p) {
           }
         });
       };
-      block_step_split<D, KVB, VF, PM, MASK>(hook, st, S, vslot(par), kslot(par), lo, qb, cq * k_cur, p.kc, b,
+      block_step_split<D, KVB, VF, PM, MASK>(hook, st, S, vslot(par), kslot(par), lo, qb, cq * k_cur, p.kc, slot,
                                              MASK ? ntail : KVB, g, col);
     } else {
       // K round r behind matrix instruction 4r, V round r behind 4r+2
@@ -895,17 +895,17 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_fwd(AttnArgs p) {
       // softmax and P.V of block b, with block b+1's scores made in between
       // (for the last block they come from a stale slot and are discarded)
       block_step<D, KVB, VF, PM, MASK, TR != 0>(hook, st, S, pmax, vslot(par), kslot(Q{}), lo, qb, cq * k_cur,
-                                                p.kc, b, MASK ? ntail : KVB, g, col, tr);
+                                                p.kc, b, slot, MASK ? ntail : KVB, g, col, tr);
     }
-    if ((b & (MS - 1)) == MS - 1 || b == nblk - 1)
+    if (slot == MS - 1 || b == nblk - 1)
       mean_flush<D, KVB, VF>(st, sM + ((b >> 3) & 1) * 2 * D * MS, g, col);
     if (b + 1 < nblk && threadIdx.x < D) {
       const int nb = b + 1;
       uint32_t hi, lo;
       bf16_split2(mnext * sRcol[threadIdx.x], 0.0f, hi, lo);
       uint16_t* mh = sM + ((nb >> 3) & 1) * 2 * D * MS;
-      mh[(0 * D + threadIdx.x) * MS + (nb & (MS - 1))] = static_cast<uint16_t>(hi);
-      mh[(1 * D + threadIdx.x) * MS + (nb & (MS - 1))] = static_cast<uint16_t>(lo);
+      mh[(0 * D + threadIdx.x) * MS + ((slot + 1) & (MS - 1))] = static_cast<uint16_t>(hi);
+      mh[(1 * D + threadIdx.x) * MS + ((slot + 1) & (MS - 1))] = static_cast<uint16_t>(lo);
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -914,13 +914,16 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_fwd(AttnArgs p) {
 
   int b = 0;
   for (; b + 2 <= nfull; b += 2) {
-    step(b, P0{}, std::false_type{});
-    step(b + 1, P1{}, std::false_type{});
+    step(b, P0{}, std::false_type{}, b & (MS - 1));
+    step(b + 1, P1{}, std::false_type{}, (b + 1) & (MS - 1));
   }
-  if (b < nfull) step(b++, P0{}, std::false_type{});
+  if (b < nfull) {
+    step(b, P0{}, std::false_type{}, b & (MS - 1));
+    ++b;
+  }
   if (nfull < nblk) {      // b == nblk - 1
-    if (b & 1) step(b, P1{}, std::true_type{});
-    else step(b, P0{}, std::true_type{});
+    if (b & 1) step(b, P1{}, std::true_type{}, b & (MS - 1));
+    else step(b, P0{}, std::true_type{}, b & (MS - 1));
   }
 
   // ---- O = s_v * acc / l ----
