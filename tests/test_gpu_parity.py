@@ -9,6 +9,7 @@ on sampled heads and query tiles in the launch configuration the benchmark
 times (all heads launched together).
 """
 import sys
+import dataclasses
 import time
 
 import numpy as np
@@ -288,7 +289,6 @@ def oracle_rows(w, host, b, h, prep_o, tiles, beta=DEFAULT_BETA, mode="expcast")
     ("tiny", 1, 77, True, "nvfp4", 64, None, "shifted"),
 ])
 def test_attention_parity(name, H, N, vsmooth, fmt, kvb, d, mode):
-    import dataclasses
     w = inputs.WORKLOADS[name]
     w = dataclasses.replace(w, kv_block=kvb or w.kv_block, d=d or w.d)
     host, dev = gen(w, H=H, N=N)
@@ -313,7 +313,6 @@ def test_attention_parity(name, H, N, vsmooth, fmt, kvb, d, mode):
 def test_batch_of_two_and_explicit_parameters(fmt):
     """B = 2 (every (b, h) pair prepared and attended in one call), with an
     explicit softmax scale and ExpCast bias instead of the defaults."""
-    import dataclasses
     w = dataclasses.replace(inputs.WORKLOADS["tiny"], B=2)
     H, N, scale, beta = 2, 700, 0.07, 0.3
     host, dev = gen(w, H=H, N=N)
@@ -558,9 +557,14 @@ def test_cluster_order_warm_start_and_attention():
 
 
 # ------------------------------------------------------------------ full-size workloads, sampled
-@pytest.mark.parametrize("name", ["video", "mxfp4", "long"])
+FULL_SIZE = dict(inputs.WORKLOADS)
+# the video shape with NVFP4-style residuals (the two-phase block step at 591 blocks)
+FULL_SIZE["video_nvfp4"] = dataclasses.replace(inputs.WORKLOADS["video"], name="video_nvfp4", v_format="nvfp4")
+
+
+@pytest.mark.parametrize("name", ["video", "mxfp4", "long", "video_nvfp4"])
 def test_full_size_sampled(name):
-    w = inputs.WORKLOADS[name]
+    w = FULL_SIZE[name]
     t0 = time.time()
     host, dev = gen(w)
     log(f"  generated {name} in {time.time() - t0:.1f}s")
@@ -672,7 +676,6 @@ def test_balanced_prepare_bit_exact(name, H, N, kvb, fmt):
     tail): labels, permutation, blocks, codes and means equal the oracle's
     bit for bit, every block holds exactly one cluster, and attention on the
     balanced blocks matches the oracle."""
-    import dataclasses
     from oracle.kmeans import seeded_init
     w = inputs.WORKLOADS[name]
     w = dataclasses.replace(w, kv_block=kvb or w.kv_block)
