@@ -287,8 +287,9 @@ __device__ __forceinline__ void pin(float& v) { asm volatile("" : "+v"(v)); }
 template <int D, int KVB, int VF>
 struct StepPlan {
   using TT = AttnTile<D, KVB, VF>;
+  static_assert(!TT::SPLIT, "the two-part residuals take the two-phase step");
   static constexpr int NDC = TT::NDC, NKT = TT::NKT, NKS = TT::NKS, NDT = TT::NDT;
-  static constexpr int NPV = VF == 3 ? 2 * NDT : NDT;   // P.V MFMAs per 64 keys (NVFP4 emulation: high, low)
+  static constexpr int NPV = NDT;                 // P.V MFMAs per 64 keys
   static constexpr int PER_S = 2 * NDC + 1 + NPV;
   static constexpr int M = NKS * PER_S;          // MFMAs per step
   static constexpr int NW = (NKT - 1) * 4;       // ExpCast words behind the MFMAs
@@ -300,8 +301,7 @@ struct StepPlan {
   static constexpr int qk_kt(int i) { return 2 * step_of(i) + (i % PER_S) / NDC; }
   static constexpr int qk_c(int i) { return (i % PER_S) % NDC; }
   static constexpr int pv_u(int i) { return i % PER_S - 2 * NDC - 1; }
-  static constexpr int pv_T(int i) { return VF == 3 ? pv_u(i) / 2 : pv_u(i); }   // channel tile
-  static constexpr int pv_half(int i) { return VF == 3 ? pv_u(i) % 2 : 0; }    // 1: low parts
+  static constexpr int pv_T(int i) { return pv_u(i); }   // channel tile
   static constexpr int qk_slot(int kt) { return (kt / 2) * PER_S + (kt % 2) * NDC; }
   static constexpr int wbeg(int i) {
     const int w = i < NDC ? i * (4 / NDC) : 4 + (i - NDC) * RATE;
@@ -453,10 +453,10 @@ __device__ __forceinline__ void block_step(
 
   v8i P[NKS];
   v4f rsum;
-  // operand ring: loads run RD-1 matrix instructions ahead (two for most
-  // formats; one for MXFP8 and the NVFP4 emulation, whose per-lane scales
-  // would otherwise push the step past the register file)
-  constexpr int RD = VF >= 2 ? 2 : 3;
+  // operand ring: loads run RD-1 matrix instructions ahead (two for E4M3 and
+  // MXFP4; one for MXFP8, whose per-lane scales would otherwise push the
+  // step past the register file)
+  constexpr int RD = VF == 2 ? 2 : 3;
   v8i opnd[RD];
   // MX formats: the E8M0 scales of this lane for the NDT channel tiles of a
   // 64-key step, one byte each (stored adjacent), op_sel picks the tile's
@@ -471,8 +471,8 @@ __device__ __forceinline__ void block_step(
         opnd[j % RD] = join8(*reinterpret_cast<const uint4*>(sKn + kt * 32 * D + lo.k_rd[c][0]),
                             *reinterpret_cast<const uint4*>(sKn + kt * 32 * D + lo.k_rd[c][1]));
       } else if constexpr (PL::kind(j) == 2) {
-        constexpr int sj = PL::step_of(j), T = PL::pv_T(j), hl = PL::pv_half(j);
-        const uint8_t* vb = sV + hl * TT::VHALF + (sj * D + 32 * T) * VROW;
+        constexpr int sj = PL::step_of(j), T = PL::pv_T(j);
+        const uint8_t* vb = sV + (sj * D + 32 * T) * VROW;
         if constexpr (VF != 1) {
           opnd[j % RD] = join8(*reinterpret_cast<const uint4*>(vb + lo.v_rd[0]),
                               *reinterpret_cast<const uint4*>(vb + lo.v_rd[1]));
@@ -525,9 +525,6 @@ __device__ __forceinline__ void block_step(
         st.acc[T] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(opnd[i % RD], P[sj], st.acc[T], 0, 0, 0, 0, 0,
                                                                    0);
       else if constexpr (VF == 2)
-        st.acc[T] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(opnd[i % RD], P[sj], st.acc[T], 0, 0, T,
-                                                                   osc[sj], 0, 127);
-      else if constexpr (VF == 3)   // residual = (high + low) * 2^scale: one slot each
         st.acc[T] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(opnd[i % RD], P[sj], st.acc[T], 0, 0, T,
                                                                    osc[sj], 0, 127);
       else
