@@ -516,47 +516,65 @@ __global__ __launch_bounds__(256) void k_sort_hist(const int32_t* __restrict__ l
 
 // hist[ch][L] <- first sorted position of chunk ch's tokens with label L;
 // counts[L] = cluster size, starts[L] = first sorted position of cluster L.
+// Thread t owns labels t, t + 1024, ... (consecutive threads read consecutive
+// words of a chunk's row); each label's chunk counts are read in batches of
+// eight before they are added, so the loads overlap.  The label prefix is
+// one workgroup scan per group of 1024 labels, in label order.
 __global__ __launch_bounds__(1024) void k_sort_scan(int32_t* __restrict__ hist, int k, int nch,
                                                     int32_t* __restrict__ counts,
                                                     int32_t* __restrict__ starts) {
+  constexpr int PER = kMaxClusters / 1024;
+  constexpr int CB = 8;                        // chunk counts read per batch
   __shared__ int32_t part[1024];
   const int bh = blockIdx.x;
   int32_t* h = hist + static_cast<size_t>(bh) * nch * k;
-  constexpr int PER = kMaxClusters / 1024;
   int tot[PER];
-  int mysum = 0;
 #pragma unroll
   for (int e = 0; e < PER; ++e) {
-    const int L = threadIdx.x * PER + e;
+    const int L = e * 1024 + static_cast<int>(threadIdx.x);
     int run = 0;
     if (L < k) {
-      for (int ch = 0; ch < nch; ++ch) {
-        const int v = h[static_cast<size_t>(ch) * k + L];
-        h[static_cast<size_t>(ch) * k + L] = run;
-        run += v;
+      for (int c0 = 0; c0 < nch; c0 += CB) {
+        int v[CB];
+#pragma unroll
+        for (int u = 0; u < CB; ++u) v[u] = c0 + u < nch ? h[static_cast<size_t>(c0 + u) * k + L] : 0;
+#pragma unroll
+        for (int u = 0; u < CB; ++u) {
+          if (c0 + u < nch) h[static_cast<size_t>(c0 + u) * k + L] = run;
+          run += v[u];
+        }
       }
     }
     tot[e] = run;
-    mysum += run;
   }
-  part[threadIdx.x] = mysum;
-  __syncthreads();
-  for (int o = 1; o < 1024; o <<= 1) {         // inclusive Hillis-Steele scan
-    const int v = static_cast<int>(threadIdx.x) >= o ? part[threadIdx.x - o] : 0;
-    __syncthreads();
-    part[threadIdx.x] += v;
-    __syncthreads();
-  }
-  int run = part[threadIdx.x] - mysum;         // exclusive prefix of this thread
+  int base = 0;                                // labels of the earlier groups
 #pragma unroll
   for (int e = 0; e < PER; ++e) {
-    const int L = threadIdx.x * PER + e;
+    if (e * 1024 >= k) break;                  // uniform: k is a kernel argument
+    part[threadIdx.x] = tot[e];
+    __syncthreads();
+    for (int o = 1; o < 1024; o <<= 1) {       // inclusive Hillis-Steele scan
+      const int v = static_cast<int>(threadIdx.x) >= o ? part[threadIdx.x - o] : 0;
+      __syncthreads();
+      part[threadIdx.x] += v;
+      __syncthreads();
+    }
+    const int run = base + part[threadIdx.x] - tot[e];   // exclusive prefix of label L
+    const int L = e * 1024 + static_cast<int>(threadIdx.x);
     if (L < k) {
       counts[static_cast<size_t>(bh) * k + L] = tot[e];
       starts[static_cast<size_t>(bh) * k + L] = run;
-      for (int ch = 0; ch < nch; ++ch) h[static_cast<size_t>(ch) * k + L] += run;
+      for (int c0 = 0; c0 < nch; c0 += CB) {
+        int v[CB];
+#pragma unroll
+        for (int u = 0; u < CB; ++u) v[u] = c0 + u < nch ? h[static_cast<size_t>(c0 + u) * k + L] : 0;
+#pragma unroll
+        for (int u = 0; u < CB; ++u)
+          if (c0 + u < nch) h[static_cast<size_t>(c0 + u) * k + L] = v[u] + run;
+      }
     }
-    run += tot[e];
+    base += part[1023];
+    __syncthreads();                           // part is rewritten by the next group
   }
 }
 
@@ -576,7 +594,7 @@ __global__ __launch_bounds__(256) void k_sort_scatter(const int32_t* __restrict_
   const int t0 = ch * kSortChunk, t1 = min(N, t0 + kSortChunk);
   const int w0 = t0 + wave * QW, w1 = min(t1, w0 + QW);
   const int32_t* lab = labels + static_cast<size_t>(bh) * N;
-  for (int i = threadIdx.x; i < 4 * kMaxClusters; i += 256) (&base[0][0])[i] = 0;
+  for (int i = threadIdx.x; i < 4 * k; i += 256) base[i / k][i % k] = 0;   // the k labels in use
   __syncthreads();
   for (int t = w0 + lane; t < w1; t += 64) {
     const int L = lab[t];
