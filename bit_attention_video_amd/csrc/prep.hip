@@ -259,15 +259,38 @@ __global__ __launch_bounds__(256, 2) void k_kmeans_assign(const int8_t* __restri
   }
   int best[2] = {INT_MIN, INT_MIN};
   int btile[2] = {0, 0};
+  // Centroid chunks are prefetched into registers one chunk ahead: the
+  // global loads of chunk c+1 are issued before chunk c's tiles are scored
+  // and written to LDS after them.
+  constexpr int PF = CCH * (D / 16) / 256;     // 16-byte pieces per thread and chunk
+  static_assert(CCH * (D / 16) % 256 == 0 && CCH <= 256, "chunk pieces spread evenly over the threads");
+  uint4 pf[PF];
+  int32_t pfn = INT_MIN;
+#pragma unroll
+  for (int i = 0; i < PF; ++i) {   // chunk 0
+    const int p = static_cast<int>(threadIdx.x) + 256 * i;
+    const int r = p / (D / 16), q16 = p % (D / 16);
+    pf[i] = r < kpad ? *reinterpret_cast<const uint4*>(cq + static_cast<size_t>(r) * D + q16 * 16) : uint4{};
+  }
+  if (static_cast<int>(threadIdx.x) < min(CCH, kpad)) pfn = cn[threadIdx.x];
   for (int c0 = 0; c0 < kpad; c0 += CCH) {
     const int rows = min(CCH, kpad - c0);
-    __syncthreads();
-    for (int p = threadIdx.x; p < rows * (D / 16); p += 256) {
+    __syncthreads();                 // the previous chunk's tiles are scored
+#pragma unroll
+    for (int i = 0; i < PF; ++i) {
+      const int p = static_cast<int>(threadIdx.x) + 256 * i;
       const int r = p / (D / 16), q16 = p % (D / 16);
-      *reinterpret_cast<uint4*>(sC + r * CSTR + q16 * 16) =
-          *reinterpret_cast<const uint4*>(cq + static_cast<size_t>(c0 + r) * D + q16 * 16);
+      if (r < rows) *reinterpret_cast<uint4*>(sC + r * CSTR + q16 * 16) = pf[i];
     }
-    for (int r = threadIdx.x; r < rows; r += 256) sCn[r] = cn[c0 + r];
+    if (static_cast<int>(threadIdx.x) < rows) sCn[threadIdx.x] = pfn;
+    const int n0 = c0 + CCH, nrows = min(CCH, kpad - n0);   // next chunk (nrows <= 0: none)
+#pragma unroll
+    for (int i = 0; i < PF; ++i) {
+      const int p = static_cast<int>(threadIdx.x) + 256 * i;
+      const int r = p / (D / 16), q16 = p % (D / 16);
+      if (r < nrows) pf[i] = *reinterpret_cast<const uint4*>(cq + static_cast<size_t>(n0 + r) * D + q16 * 16);
+    }
+    if (static_cast<int>(threadIdx.x) < nrows) pfn = cn[n0 + threadIdx.x];
     __syncthreads();
     for (int tile = 0; tile < rows / 32; ++tile) {
       v4i a[NDC];
