@@ -728,20 +728,47 @@ struct BlockRows {
   static constexpr int RQ = 256 / CG;         // 4-row quads covered per pass
   static constexpr int PASS = (KVB / 4 + RQ - 1) / RQ;
   float v[PASS][4][8];
-  __device__ __forceinline__ void load(const uint16_t* vv, const int32_t* pp, int p0, int N) {
+  // the 16-byte piece of pass ps, row rr of the quad (zeros past the block)
+  static __device__ __forceinline__ uint4 piece(const uint16_t* vv, const int32_t* pp, int p0, int N, int ps,
+                                                int rr) {
     const int cg = threadIdx.x % CG, q = threadIdx.x / CG;
+    const int r = (ps * RQ + q) * 4 + rr;
+    const int pos = p0 + r;
+    uint4 raw = make_uint4(0u, 0u, 0u, 0u);
+    if (r < KVB && pos < N) raw = *reinterpret_cast<const uint4*>(vv + static_cast<size_t>(clamp_tok(pp[pos], N)) * D + cg * 8);
+    return raw;
+  }
+  __device__ __forceinline__ void load(const uint16_t* vv, const int32_t* pp, int p0, int N) {
 #pragma unroll
     for (int ps = 0; ps < PASS; ++ps)
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
-        const int r = (ps * RQ + q) * 4 + rr;
-        const int pos = p0 + r;
-        uint4 raw = make_uint4(0u, 0u, 0u, 0u);
-        if (r < KVB && pos < N) raw = *reinterpret_cast<const uint4*>(vv + static_cast<size_t>(clamp_tok(pp[pos], N)) * D + cg * 8);
+        const uint4 raw = piece(vv, pp, p0, N, ps, rr);
         const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[ps][rr][e] = bf16_to_f32(static_cast<uint16_t>(w[e >> 1] >> ((e & 1) * 16)));
       }
+  }
+};
+
+// The same rows kept as packed bf16 (half the registers of BlockRows) and
+// widened on each use, for kernels that read every value twice.
+template <int D, int KVB>
+struct BlockRowsPacked {
+  using BR = BlockRows<D, KVB>;
+  static constexpr int CG = BR::CG, RQ = BR::RQ, PASS = BR::PASS;
+  uint32_t w[PASS][4][4];
+  __device__ __forceinline__ void load(const uint16_t* vv, const int32_t* pp, int p0, int N) {
+#pragma unroll
+    for (int ps = 0; ps < PASS; ++ps)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const uint4 raw = BR::piece(vv, pp, p0, N, ps, rr);
+        w[ps][rr][0] = raw.x; w[ps][rr][1] = raw.y; w[ps][rr][2] = raw.z; w[ps][rr][3] = raw.w;
+      }
+  }
+  __device__ __forceinline__ float at(int ps, int rr, int e) const {
+    return bf16_to_f32(static_cast<uint16_t>(w[ps][rr][e >> 1] >> ((e & 1) * 16)));
   }
 };
 
@@ -751,10 +778,12 @@ template <int D, int KVB>
 __global__ __launch_bounds__(256) void k_vblock_stats(const uint16_t* __restrict__ V, const int32_t* __restrict__ perm,
                                                       int N, int nblk, int vsmooth, int want_amax,
                                                       float* __restrict__ v_mean, uint32_t* __restrict__ vramax) {
-  using BR = BlockRows<D, KVB>;
+  using BR = BlockRowsPacked<D, KVB>;
+  // per-quad partial sums (fp64), then, once the mean is published, the
+  // per-quad maxima |v - mean| in the same memory
   __shared__ double sPart[BR::RQ][D];
   __shared__ float sMean[D];
-  __shared__ float sAm[BR::RQ][D];
+  float (*sAm)[D] = reinterpret_cast<float (*)[D]>(&sPart[0][0]);
   const int bh = blockIdx.y, b = blockIdx.x;
   const int p0 = b * KVB, nv = min(KVB, N - p0);
   const int cg = threadIdx.x % BR::CG, q = threadIdx.x / BR::CG;
@@ -767,7 +796,7 @@ __global__ __launch_bounds__(256) void k_vblock_stats(const uint16_t* __restrict
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) ps[e] += static_cast<double>(rows.v[pass][rr][e]);   // padded rows hold 0
+        for (int e = 0; e < 8; ++e) ps[e] += static_cast<double>(rows.at(pass, rr, e));   // padded rows hold 0
 #pragma unroll
     for (int e = 0; e < 8; ++e) sPart[q][cg * 8 + e] = ps[e];
     __syncthreads();
@@ -790,7 +819,7 @@ __global__ __launch_bounds__(256) void k_vblock_stats(const uint16_t* __restrict
       const int r = (pass * BR::RQ + q) * 4 + rr;
       if (r < nv) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) am[e] = fmaxf(am[e], fabsf(rows.v[pass][rr][e] - sMean[cg * 8 + e]));
+        for (int e = 0; e < 8; ++e) am[e] = fmaxf(am[e], fabsf(rows.at(pass, rr, e) - sMean[cg * 8 + e]));
       }
     }
 #pragma unroll
@@ -1058,7 +1087,7 @@ __global__ __launch_bounds__(256) void k_ksmooth(const uint16_t* __restrict__ K,
                                                  const int32_t* __restrict__ perm,
                                                  const float* __restrict__ mu, int N, int nblk,
                                                  uint8_t* __restrict__ Kq, float* __restrict__ k_scale) {
-  using BR = BlockRows<D, KVB>;
+  using BR = BlockRowsPacked<D, KVB>;
   __shared__ float sMax[4];
   const int bh = blockIdx.y, b = blockIdx.x;
   const int p0 = b * KVB;
@@ -1079,11 +1108,7 @@ __global__ __launch_bounds__(256) void k_ksmooth(const uint16_t* __restrict__ K,
       const int r = (ps * BR::RQ + q) * 4 + rr;
       const bool live = r < KVB && p0 + r < N;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float x = live ? rows.v[ps][rr][e] - m[e] : 0.0f;
-        rows.v[ps][rr][e] = x;
-        am = fmaxf(am, fabsf(x));
-      }
+      for (int e = 0; e < 8; ++e) am = fmaxf(am, fabsf(live ? rows.at(ps, rr, e) - m[e] : 0.0f));
     }
   am = wave_max(am);
   if ((threadIdx.x & 63) == 0) sMax[threadIdx.x >> 6] = am;
@@ -1099,7 +1124,10 @@ __global__ __launch_bounds__(256) void k_ksmooth(const uint16_t* __restrict__ K,
     for (int rr = 0; rr < 4; ++rr) {
       const int r = (ps * BR::RQ + q) * 4 + rr;
       if (r < KVB) {
-        const float* x = rows.v[ps][rr];
+        const bool live = p0 + r < N;      // padded positions hold code 0
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = live ? rows.at(ps, rr, e) - m[e] : 0.0f;
         const uint32_t lo = e4m3x4(div_rn(x[0], s, y), div_rn(x[1], s, y), div_rn(x[2], s, y), div_rn(x[3], s, y));
         const uint32_t hi = e4m3x4(div_rn(x[4], s, y), div_rn(x[5], s, y), div_rn(x[6], s, y), div_rn(x[7], s, y));
         const int prow = (r & ~63) | kstep_row_of_pos(r & 63);
