@@ -167,7 +167,11 @@ __global__ void k_init_centroids(const uint16_t* __restrict__ V, const int32_t* 
       bf16_to_f32(V[(static_cast<size_t>(bh) * N + tok) * D + c]);
 }
 
-// int8 centroid codes and the packed score offsets cn32 = (31 - row % 32) - 32*|c|^2;
+// rows of one centroid chunk of the assignment; the packed keys order the rows
+// of a chunk in their low log2(kKeyRows) bits
+constexpr int kKeyRows = 128;
+
+// int8 centroid codes and the packed score offsets cn32 = (127 - row % 128) - 128*|c|^2;
 // rows k..kpad-1 are padding (codes 0, offset INT_MIN: their key is never the maximum).
 template <int D>
 __global__ __launch_bounds__(256) void k_quant_centroids(const float* __restrict__ C,
@@ -191,17 +195,18 @@ __global__ __launch_bounds__(256) void k_quant_centroids(const float* __restrict
   }
   for (int o = 32; o > 0; o >>= 1) sq += __shfl_xor(sq, o, 64);
   if (lane == 0)
-    cn32[static_cast<size_t>(bh) * kpad + i] = i < k ? (31 - (i & 31)) - sq * 32 : INT_MIN;
+    cn32[static_cast<size_t>(bh) * kpad + i] = i < k ? (kKeyRows - 1 - (i & (kKeyRows - 1))) - sq * kKeyRows : INT_MIN;
 }
 
 // One assignment pass: label = argmin_c (|c_q|^2 - 2 v_q.c_q), lowest index on
 // ties.  C^T = Cq . Vq^T runs on v_mfma_i32_32x32x32_i8 (exact int32); each
 // lane folds its 16 accumulator rows of a 32-centroid tile into keys
-// 32*(2 v.c - |c|^2) + (31 - row-in-tile) = (acc << 6) + cn32 (one shift-add;
-// max = lowest distance, then lowest row; key >> 5 is the score exactly),
-// keeps a tile's maximum only if its score is strictly higher than the best
-// so far, and the two lane halves that share a token column are merged on
-// (score, index).
+// 128*(2 v.c - |c|^2) + (127 - row-in-chunk) = (acc << 8) + cn32 (one
+// shift-add; max = lowest distance, then lowest row of the 128-centroid
+// chunk; key >> 7 is the score exactly: |2 v.c - |c|^2| < 3 * 128 * 127^2 <
+// 2^23, so the key fits in 31 bits), keeps a chunk's maximum only if its
+// score is strictly higher than the best so far, and the two lane halves that
+// share a token column are merged on (score, index).
 // A workgroup covers 256 tokens (4 waves x 2 column tiles of 32); centroids
 // stream through LDS in chunks of 128.
 // BAL (balanced clusters, one proposal round): only tokens whose label in
@@ -258,7 +263,8 @@ __global__ __launch_bounds__(256, 2) void k_kmeans_assign(const int8_t* __restri
     }
   }
   int best[2] = {INT_MIN, INT_MIN};
-  int btile[2] = {0, 0};
+  int bchunk[2] = {0, 0};
+  static_assert(CCH == kKeyRows, "a key orders the rows of one centroid chunk");
   // Centroid chunks are prefetched into registers one chunk ahead: the
   // global loads of chunk c+1 are issued before chunk c's tiles are scored
   // and written to LDS after them.
@@ -292,6 +298,7 @@ __global__ __launch_bounds__(256, 2) void k_kmeans_assign(const int8_t* __restri
     }
     if (static_cast<int>(threadIdx.x) < nrows) pfn = cn[n0 + threadIdx.x];
     __syncthreads();
+    int cmax[2] = {INT_MIN, INT_MIN};
     for (int tile = 0; tile < rows / 32; ++tile) {
       v4i a[NDC];
 #pragma unroll
@@ -303,7 +310,6 @@ __global__ __launch_bounds__(256, 2) void k_kmeans_assign(const int8_t* __restri
         const int4 o4 = *reinterpret_cast<const int4*>(sCn + tile * 32 + 8 * i + 4 * g);
         off[4 * i + 0] = o4.x; off[4 * i + 1] = o4.y; off[4 * i + 2] = o4.z; off[4 * i + 3] = o4.w;
       }
-      const int gt = c0 / 32 + tile;
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         v16i acc = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
@@ -312,20 +318,23 @@ __global__ __launch_bounds__(256, 2) void k_kmeans_assign(const int8_t* __restri
           acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[c], bop[j][c], acc, 0, 0, 0);
         int key[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) key[r] = static_cast<int>((static_cast<uint32_t>(acc[r]) << 6) + off[r]);
-        int tmax = max(key[0], key[1]);
+        for (int r = 0; r < 16; ++r) key[r] = static_cast<int>((static_cast<uint32_t>(acc[r]) << 8) + off[r]);
+        int m = cmax[j];
 #pragma unroll
-        for (int r = 2; r < 16; r += 2) tmax = max(max(tmax, key[r]), key[r + 1]);
-        // tiles arrive in increasing index order: a later tile must win on
-        // score alone (the packed row only orders rows inside one tile)
-        if ((tmax >> 5) > (best[j] >> 5)) { best[j] = tmax; btile[j] = gt; }
+        for (int r = 0; r < 16; r += 2) m = max(max(m, key[r]), key[r + 1]);
+        cmax[j] = m;
       }
     }
+    // chunks arrive in increasing index order: a later chunk must win on
+    // score alone (the packed row only orders rows inside one chunk)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      if ((cmax[j] >> 7) > (best[j] >> 7)) { best[j] = cmax[j]; bchunk[j] = c0 / CCH; }
   }
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const int score = best[j] >> 5;
-    const int idx = btile[j] * 32 + (31 - (best[j] & 31));
+    const int score = best[j] >> 7;
+    const int idx = bchunk[j] * CCH + (CCH - 1 - (best[j] & (CCH - 1)));
     const int ps = __shfl_xor(score, 32, 64);
     const int pi = __shfl_xor(idx, 32, 64);
     const bool other = ps > score || (ps == score && pi < idx);
