@@ -215,9 +215,13 @@ def test_sort_bit_exact(N, k):
 
 
 # ------------------------------------------------------------------ k-means assignment
-@pytest.mark.parametrize("name,H,N", [("tiny", 2, None), ("mid", 2, None), ("video", 1, None), ("tiny", 1, 333)])
-def test_kmeans_assign_given_oracle_centroids(name, H, N):
+@pytest.mark.parametrize("name,H,N,k", [("tiny", 2, None, None), ("mid", 2, None, None), ("video", 1, None, None),
+                                         ("tiny", 1, 333, None),
+                                         ("mid", 1, 4000, 300)])   # 320 padded centroids: chunks of 128, 128, 64
+def test_kmeans_assign_given_oracle_centroids(name, H, N, k):
     w = inputs.WORKLOADS[name]
+    if k is not None:
+        w = dataclasses.replace(w, k=k)
     host, dev = gen(w, H=H, N=N)
     cfg = cfg_for(w, H=H, N=N)
     for h in range(H):
