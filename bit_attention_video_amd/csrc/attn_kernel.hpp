@@ -357,6 +357,41 @@ struct TraceRow {
   int row = 0;            // query row of this lane inside the workgroup
 };
 
+// Trace stores of block b (test-only instantiation; lane (g, col) holds key
+// 32*kt + 16*g + r of the block in S[kt][r], sorted order): the masked scores,
+// the running maximum after the block and the block's log2-domain scale ...
+template <int KVB, int NKT>
+__device__ __forceinline__ void trace_scores(const TraceRow& tr, size_t trow, const v16f* S, float m_new, float cb,
+                                             int g) {
+  if (!tr.S) return;
+  float* sp = tr.S + trow * KVB;
+#pragma unroll
+  for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4)
+      *reinterpret_cast<float4*>(sp + 32 * kt + 16 * g + 4 * r4) =
+          make_float4(S[kt][4 * r4], S[kt][4 * r4 + 1], S[kt][4 * r4 + 2], S[kt][4 * r4 + 3]);
+  if (g == 0) {
+    tr.m[trow] = m_new;
+    tr.c[trow] = cb;
+  }
+}
+// ... and the probability bytes (word 4h + q of P[s] holds keys 64s + 32h +
+// 16g + 4q .. +3) with their row sum
+template <int KVB, int NKS>
+__device__ __forceinline__ void trace_bytes(const TraceRow& tr, size_t trow, const v8i* P, float rs, int g) {
+  if (!tr.S) return;
+  uint8_t* pp = tr.P + trow * KVB;
+#pragma unroll
+  for (int s2 = 0; s2 < NKS; ++s2)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      *reinterpret_cast<uint4*>(pp + 64 * s2 + 32 * h + 16 * g) =
+          make_uint4(static_cast<uint32_t>(P[s2][4 * h]), static_cast<uint32_t>(P[s2][4 * h + 1]),
+                     static_cast<uint32_t>(P[s2][4 * h + 2]), static_cast<uint32_t>(P[s2][4 * h + 3]));
+  if (g == 0) tr.l[trow] = rs;
+}
+
 // Masks the padded keys of the tail block, takes the row maximum across the
 // two lane groups, moves the running maximum m (and with it the accumulator,
 // the pending row sums and l) to max(m, c_b * rowmax S), and returns the word
@@ -435,21 +470,7 @@ __device__ __forceinline__ void block_step(
   [[maybe_unused]] const float m_new = st.m_run;
   // lane (g, col) holds key 32*kt + 16*g + r of block b in S[kt][r] (sorted order)
   [[maybe_unused]] const size_t trow = static_cast<size_t>(b) * TT::ROWS + tr.row;
-  if constexpr (TR) {
-    if (tr.S) {
-      float* sp = tr.S + trow * KVB;
-#pragma unroll
-      for (int kt = 0; kt < NKT; ++kt)
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4)
-          *reinterpret_cast<float4*>(sp + 32 * kt + 16 * g + 4 * r4) =
-              make_float4(S[kt][4 * r4], S[kt][4 * r4 + 1], S[kt][4 * r4 + 2], S[kt][4 * r4 + 3]);
-      if (g == 0) {
-        tr.m[trow] = m_new;
-        tr.c[trow] = cb;
-      }
-    }
-  }
+  if constexpr (TR) trace_scores<KVB, NKT>(tr, trow, S, m_new, cb, g);
 
   v8i P[NKS];
   v4f rsum;
@@ -550,20 +571,7 @@ __device__ __forceinline__ void block_step(
   });
 
   const float rs = rsum[0];
-  if constexpr (TR) {
-    if (tr.S) {
-      // word 4h + q of P[s] holds keys 64s + 32h + 16g + 4q .. +3
-      uint8_t* pp = tr.P + trow * KVB;
-#pragma unroll
-      for (int s2 = 0; s2 < NKS; ++s2)
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-          *reinterpret_cast<uint4*>(pp + 64 * s2 + 32 * h + 16 * g) =
-              make_uint4(static_cast<uint32_t>(P[s2][4 * h]), static_cast<uint32_t>(P[s2][4 * h + 1]),
-                         static_cast<uint32_t>(P[s2][4 * h + 2]), static_cast<uint32_t>(P[s2][4 * h + 3]));
-      if (g == 0) tr.l[trow] = rs;
-    }
-  }
+  if constexpr (TR) trace_bytes<KVB, NKS>(tr, trow, P, rs, g);
   st.l_run += rs;
 #pragma unroll
   for (int i = 0; i < MS; ++i) st.RS[i] = i == slot ? rs : st.RS[i];
@@ -576,11 +584,11 @@ __device__ __forceinline__ void block_step(
 // and one operand pair stay live in the second phase.  hook(i) runs right
 // after matrix instruction i is issued (QK^T: 0 .. NKT*NDC-1, then per 64
 // keys the row sum and the P.V MFMAs).
-template <int D, int KVB, int VF, int PM, bool MASK, typename Hook>
+template <int D, int KVB, int VF, int PM, bool MASK, bool TR, typename Hook>
 __device__ __forceinline__ void block_step_split(
     Hook&& hook, SoftmaxState<D / 32, AttnTile<D, KVB, VF>::MSLOT>& st, v16f* S, const uint8_t* sV,
-    const uint8_t* sK, const LaneOffsets<D, KVB, VF>& lo, const v8i* qb, float cb, float kc, int slot, int nvalid,
-    int g, int col) {
+    const uint8_t* sK, const LaneOffsets<D, KVB, VF>& lo, const v8i* qb, float cb, float kc, int b, int slot,
+    int nvalid, int g, int col, const TraceRow& tr) {
   using TT = AttnTile<D, KVB, VF>;
   constexpr int NKT = TT::NKT, NKS = TT::NKS, NDT = TT::NDT, NDC = TT::NDC, VROW = TT::VROW, MS = TT::MSLOT;
   constexpr int NQK = NKT * NDC, NPV = 2 * NDT;
@@ -604,6 +612,8 @@ __device__ __forceinline__ void block_step_split(
   for (int kt = 1; kt < NKT; ++kt) pmax = tile_max(S[kt], pmax);
   float A8, Bq;
   softmax_update<D, KVB, VF, PM, MASK>(st, S, pmax, cb, kc, nvalid, g, A8, Bq);
+  [[maybe_unused]] const size_t trow = static_cast<size_t>(b) * TT::ROWS + tr.row;
+  if constexpr (TR) trace_scores<KVB, NKT>(tr, trow, S, st.m_run, cb, g);
   v8i P[NKS];
 #pragma unroll
   for (int kt = 0; kt < NKT; ++kt)
@@ -641,6 +651,7 @@ __device__ __forceinline__ void block_step_split(
     });
   });
   const float rs = rsum[0];
+  if constexpr (TR) trace_bytes<KVB, NKS>(tr, trow, P, rs, g);
   st.l_run += rs;
 #pragma unroll
   for (int i = 0; i < MS; ++i) st.RS[i] = i == slot ? rs : st.RS[i];
@@ -868,8 +879,8 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_fwd(AttnArgs p) {
           }
         });
       };
-      block_step_split<D, KVB, VF, PM, MASK>(hook, st, S, vslot(par), kslot(par), lo, qb, cq * k_cur, p.kc, slot,
-                                             MASK ? ntail : KVB, g, col);
+      block_step_split<D, KVB, VF, PM, MASK, TR != 0>(hook, st, S, vslot(par), kslot(par), lo, qb, cq * k_cur,
+                                                       p.kc, b, slot, MASK ? ntail : KVB, g, col, tr);
     } else {
       // K round r behind matrix instruction 4r, V round r behind 4r+2
       auto hook = [&](auto ic) {
@@ -960,7 +971,7 @@ hipError_t launch_attn_cfg(const AttnArgs& a, hipStream_t st) {
   const dim3 grid(static_cast<unsigned>(a.B * a.H * nqt));
   const dim3 blk(TT::NTH);
   if (a.tr_S) {
-    if constexpr (VF <= 1) {
+    if constexpr (VF != 2) {
       if (a.pm == 0) hipLaunchKernelGGL((k_attn_fwd<D, KVB, VF, 1, 0, 1>), grid, blk, 0, st, a);
       else hipLaunchKernelGGL((k_attn_fwd<D, KVB, VF, 1, 1, 1>), grid, blk, 0, st, a);
     } else {
