@@ -327,7 +327,6 @@ vc_status vc_dbg_attn_trace(const vc_config* cfg, const void* Q, const uint8_t* 
   Dims D;
   if (vc_status s = validate(cfg, false, &D)) return s;
   if (!cfg->out_fp32) return fail(VC_ERR_UNSUPPORTED, "the trace runs with fp32 output only (out_fp32 = 1)");
-  if (cfg->v_format == 2) return fail(VC_ERR_UNSUPPORTED, "the trace runs with E4M3, MXFP4 or NVFP4-style residuals");
   if (!Q || !Kq || !k_scale || !Vres || !v_scale || !v_mean || !O || !S || !P || !m || !c || !rowsum)
     return fail(VC_ERR_INVALID_ARG, "required pointer is NULL");
   if (misaligned(Q) || misaligned(Kq) || misaligned(Vres) || misaligned(v_scale) || misaligned(v_mean) ||

@@ -971,12 +971,8 @@ hipError_t launch_attn_cfg(const AttnArgs& a, hipStream_t st) {
   const dim3 grid(static_cast<unsigned>(a.B * a.H * nqt));
   const dim3 blk(TT::NTH);
   if (a.tr_S) {
-    if constexpr (VF != 2) {
-      if (a.pm == 0) hipLaunchKernelGGL((k_attn_fwd<D, KVB, VF, 1, 0, 1>), grid, blk, 0, st, a);
-      else hipLaunchKernelGGL((k_attn_fwd<D, KVB, VF, 1, 1, 1>), grid, blk, 0, st, a);
-    } else {
-      return hipErrorInvalidValue;
-    }
+    if (a.pm == 0) hipLaunchKernelGGL((k_attn_fwd<D, KVB, VF, 1, 0, 1>), grid, blk, 0, st, a);
+    else hipLaunchKernelGGL((k_attn_fwd<D, KVB, VF, 1, 1, 1>), grid, blk, 0, st, a);
   } else if (a.out_fp32) {
     if (a.pm == 0) hipLaunchKernelGGL((k_attn_fwd<D, KVB, VF, 1, 0, 0>), grid, blk, 0, st, a);
     else hipLaunchKernelGGL((k_attn_fwd<D, KVB, VF, 1, 1, 0>), grid, blk, 0, st, a);

@@ -215,10 +215,10 @@ vc_status vc_attn_fwd(const vc_config* cfg, const void* Q, const uint8_t* Kq,
  *   c       fp32  [nblk][256]  the block's log2-domain score scale
  *                 c = fp32(cq * k_scale[b]), cq = fp32(fp32(s_q*scale)*log2 e);
  *   rowsum  fp32  [nblk][256]  the block's row sum of the decoded bytes.
- * Rows at or beyond N hold the values for zero query codes.  Requires
- * out_fp32 = 1 and v_format 0, 1 or 3 (E4M3, MXFP4, NVFP4 style;
- * VC_ERR_UNSUPPORTED for MXFP8); bh and q_group out of range give
- * VC_ERR_INVALID_ARG.  The caller owns all buffers.
+ * Rows at or beyond N hold the values for zero query codes.  Any residual
+ * format; requires out_fp32 = 1 (VC_ERR_UNSUPPORTED otherwise); bh and
+ * q_group out of range give VC_ERR_INVALID_ARG.  The caller owns all
+ * buffers.
  */
 vc_status vc_dbg_attn_trace(const vc_config* cfg, const void* Q, const uint8_t* Kq,
                             const float* k_scale, const uint8_t* Vres, const void* v_scale,

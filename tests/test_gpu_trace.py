@@ -200,11 +200,15 @@ def test_trace_with_mxfp4_residuals_and_explicit_parameters():
     check_trace(w, host, prep_o, tr, 0, 2, "expcast", float(F.f32(scale)), beta)
 
 
-@pytest.mark.parametrize("name,N,mode,group", [("tiny", 900, "expcast", 2), ("mid", 5000, "exp2", 19),
-                                               ("mid", None, "shifted", 40)])
-def test_trace_with_nvfp4_style_residuals(name, N, mode, group):
-    # the two-phase block step of the NVFP4-style residuals forms the same
-    # scores, maxima, bytes and row sums
+@pytest.mark.parametrize("fmt,name,N,mode,group", [("nvfp4", "tiny", 900, "expcast", 2),
+                                                   ("nvfp4", "mid", 5000, "exp2", 19),
+                                                   ("nvfp4", "mid", None, "shifted", 40),
+                                                   ("mxfp8", "tiny", 900, "expcast", 2),
+                                                   ("mxfp8", "mid", 5000, "shifted", 19)])
+def test_trace_with_block_scaled_residuals(fmt, name, N, mode, group):
+    # the two-phase block step of the NVFP4-style residuals, and the MXFP8
+    # step with its two-deep operand ring, form the same scores, maxima,
+    # bytes and row sums
     import dataclasses
     w = inputs.WORKLOADS[name]
     N = N or w.N
@@ -212,11 +216,12 @@ def test_trace_with_nvfp4_style_residuals(name, N, mode, group):
     host = inputs.gen_all(w)
     q, k, v, init = host
     beta = oracle.DEFAULT_BETA
-    cfg = vb.make_config(1, 1, N, w.d, w.kv_block, w.k, w.iters, True, vb.NVFP4, True, 0.0, beta, MODES[mode])
+    vf = {"nvfp4": vb.NVFP4, "mxfp8": vb.MXFP8}[fmt]
+    cfg = vb.make_config(1, 1, N, w.d, w.kv_block, w.k, w.iters, True, vf, True, 0.0, beta, MODES[mode])
     prep = vb.vsmooth_prepare(cfg, to_device_bf16(k), to_device_bf16(v), torch.from_numpy(init).cuda())
     O_prod = vb.vc_attn_fwd(cfg, to_device_bf16(q), prep)
     prep_o = oracle.prepare_head(oracle.bf16_to_f64(k[0, 0]), oracle.bf16_to_f64(v[0, 0]), init[0, 0], w.k,
-                                 w.iters, w.kv_block, "nvfp4")
+                                 w.iters, w.kv_block, fmt)
     O_tr, tr = vb.dbg_attn_trace(cfg, to_device_bf16(q), prep, 0, group)
     assert torch.equal(O_tr, O_prod), "the trace instantiation's O differs from the production kernel's"
     check_trace(w, host, prep_o, tr, 0, group, mode, softmax_scale(w.d), beta)
