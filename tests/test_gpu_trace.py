@@ -250,9 +250,10 @@ def vsmooth_closed_form_inputs(N, d, kvb, seed=5):
     return Q, K, V, means
 
 
-@pytest.mark.parametrize("mode,d,kvb", [("expcast", 64, 64), ("exp2", 128, 128), ("shifted", 128, 64),
-                                         ("expcast", 128, 128)])
-def test_mean_restoration_closed_form(mode, d, kvb):
+@pytest.mark.parametrize("mode,d,kvb,fmt", [("expcast", 64, 64, "e4m3"), ("exp2", 128, 128, "e4m3"),
+                                             ("shifted", 128, 64, "e4m3"), ("expcast", 128, 128, "e4m3"),
+                                             ("expcast", 128, 128, "mxfp8"), ("shifted", 64, 64, "mxfp8")])
+def test_mean_restoration_closed_form(mode, d, kvb, fmt):
     """V-Smooth on (identity permutation, so the blocks are natural order and
     their means are the constructed ones): every probability byte is exactly
     2^(t - m) (times 2^8 when range-shifted), every mean and row sum is exact
@@ -260,23 +261,28 @@ def test_mean_restoration_closed_form(mode, d, kvb):
     partial sum is exact in fp32.  O must then equal the base-2 softmax of the
     integer scores applied to V itself up to the final normalisation's
     roundings (4 * 2^-24 relative), which pins the mean restoration: the
-    right block's mean, the rescaling of the mean term, and its scale."""
+    right block's mean, the rescaling of the mean term, and its scale.  The
+    residuals (multiples of 32 up to 448) are exact in E4M3 under a unit
+    scale and in MXFP8 under any power-of-two group scale."""
     from closed_forms import base2_softmax, unit_log2_scale
     N = 300
     Q, K, V, means = vsmooth_closed_form_inputs(N, d, kvb)
     assert np.all(np.abs(V) <= 1216) and np.all(V % 32 == 0)          # exact in bf16
     dv = {n: torch.from_numpy(x).to(torch.bfloat16).reshape(1, 1, N, d).cuda() for n, x in
           (("Q", Q), ("K", K), ("V", V))}
-    cfg = vb.make_config(1, 1, N, d, kvb, 1, 1, True, vb.E4M3, True, unit_log2_scale(), -0.25, MODES[mode])
+    vf = {"e4m3": vb.E4M3, "mxfp8": vb.MXFP8}[fmt]
+    cfg = vb.make_config(1, 1, N, d, kvb, 1, 1, True, vf, True, unit_log2_scale(), -0.25, MODES[mode])
     ident = torch.arange(N, dtype=torch.int32, device="cuda").reshape(1, 1, N)
     prep = vb.vsmooth_prepare_warm(cfg, dv["K"], dv["V"], perm_in=ident)
     assert np.array_equal(prep.v_mean[0, 0].cpu().numpy(), means.astype(np.float32))
-    assert torch.all(prep.v_scale == 1.0) and torch.all(prep.k_scale == 1.0)
+    assert torch.all(prep.k_scale == 1.0)
+    if fmt == "e4m3":
+        assert torch.all(prep.v_scale == 1.0)
     O = vb.vc_attn_fwd(cfg, dv["Q"], prep)[0, 0].cpu().numpy().astype(np.float64)
     S = Q @ K.T
     want = base2_softmax(S, V)
     err = np.abs(O - want)
-    log(f"  {mode} d {d} kv_block {kvb}: max rel err {np.max(err / np.maximum(np.abs(want), 1e-30)):.2e}, "
+    log(f"  {fmt} {mode} d {d} kv_block {kvb}: max rel err {np.max(err / np.maximum(np.abs(want), 1e-30)):.2e}, "
         f"mean term share {np.max(np.abs(base2_softmax(S, np.repeat(means, kvb, 0)[:N]))) / np.max(np.abs(want)):.2f}")
     assert np.all(err <= 4.0 * 2.0 ** -24 * np.abs(want) + 1e-30)
     # with the means dropped (a kernel that forgot to restore them) the output
