@@ -606,6 +606,7 @@ __device__ __forceinline__ void block_step_split(
                         *reinterpret_cast<const uint4*>(sK + kt * 32 * D + lo.k_rd[c][1]));
     S[kt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qb[c], c == 0 ? v16f{} : S[kt], 0, 0, 0, 0, 0, 0);
     hook(ic);
+    __builtin_amdgcn_sched_barrier(0);
   });
   float pmax = tile_max(S[0]);
 #pragma unroll
@@ -647,6 +648,7 @@ __device__ __forceinline__ void block_step_split(
       const v8i nxt = u + 1 < NPV ? vopnd(sj, u + 1) : cur;
       st.acc[T] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cur, P[sj], st.acc[T], 0, 0, T, osc, 0, 127);
       hook(std::integral_constant<int, base + 1 + u>{});
+      __builtin_amdgcn_sched_barrier(0);
       cur = nxt;
     });
   });
