@@ -214,7 +214,7 @@ __global__ __launch_bounds__(256) void k_quant_centroids(const float* __restrict
 // offset INT_MIN, so they are never chosen; the kernel writes each active
 // token's proposal (nearest cluster with room, lowest index on ties) to
 // `prop` and its exact squared distance |v|^2 - score to `pdist`, and -1 to
-// `prop` for every other token.
+// `prop` for every other token (whose `pdist` is left as it was).
 template <int D, bool BAL = false>
 __global__ __launch_bounds__(256, 2) void k_kmeans_assign(const int8_t* __restrict__ Vq,
                                                        const int8_t* __restrict__ Cq,
@@ -232,31 +232,52 @@ __global__ __launch_bounds__(256, 2) void k_kmeans_assign(const int8_t* __restri
   const int8_t* vq = Vq + static_cast<size_t>(bh) * N * D;
   const int8_t* cq = Cq + static_cast<size_t>(bh) * kpad * D;
   const int32_t* cn = cn32 + static_cast<size_t>(bh) * kpad;
-  const int tok0 = blockIdx.x * 256 + wave * 64;
-  bool active[2] = {true, true};
+  // token of column tile j of this wave (-1: none); jvalid[j]: the tile holds
+  // a token (wave-uniform), so the wave scores it
+  int tokj[2];
+  bool jvalid[2] = {true, true};
   if constexpr (BAL) {
+    // only the workgroup's unplaced tokens take part: they are packed in
+    // token order into the first column tiles (tile c is wave c % 4's
+    // tile c / 4), so late rounds with few of them score few tiles
+    __shared__ int32_t sAct[256];
+    __shared__ int32_t sWaveAct[4];
+    const int tk = blockIdx.x * 256 + static_cast<int>(threadIdx.x);
+    const bool act = tk < N && labels[static_cast<size_t>(bh) * N + tk] < 0;
+    if (tk < N && !act) prop[static_cast<size_t>(bh) * N + tk] = -1;    // placed tokens propose nothing
+    const uint64_t am = __ballot(act);
+    if (lane == 0) sWaveAct[wave] = __popcll(am);
+    __syncthreads();
+    int nact = 0, before = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      before += w < wave ? sWaveAct[w] : 0;
+      nact += sWaveAct[w];
+    }
+    if (act) sAct[before + __popcll(am & ((1ull << lane) - 1ull))] = tk;
+    __syncthreads();
+    if (nact == 0) return;                                  // every token of the workgroup is placed
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int tok = tok0 + j * 32 + col;
-      active[j] = tok < N && labels[static_cast<size_t>(bh) * N + tok] < 0;
+      const int c = wave + 4 * j, pos = c * 32 + col;
+      tokj[j] = pos < nact ? sAct[pos] : -1;
+      jvalid[j] = c * 32 < nact;
     }
-    if (!__syncthreads_or(active[0] || active[1])) {      // every token of the workgroup is placed
+  } else {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int tok = tok0 + j * 32 + col;
-        if (g == 0 && tok < N) prop[static_cast<size_t>(bh) * N + tok] = -1;
-      }
-      return;
+    for (int j = 0; j < 2; ++j) {
+      const int tok = blockIdx.x * 256 + wave * 64 + j * 32 + col;
+      tokj[j] = tok < N ? tok : -1;
     }
   }
 
   v4i bop[2][NDC];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const int tok = tok0 + j * 32 + col;
+    const int tok = tokj[j];
 #pragma unroll
     for (int c = 0; c < NDC; ++c) {
-      if (tok < N)
+      if (tok >= 0)
         bop[j][c] = *reinterpret_cast<const v4i*>(vq + static_cast<size_t>(tok) * D + 32 * c + 16 * g);
       else
         bop[j][c] = v4i{0, 0, 0, 0};
@@ -312,6 +333,7 @@ __global__ __launch_bounds__(256, 2) void k_kmeans_assign(const int8_t* __restri
       }
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
+        if (!jvalid[j]) continue;                           // wave-uniform
         v16i acc = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
         for (int c = 0; c < NDC; ++c)
@@ -333,13 +355,14 @@ __global__ __launch_bounds__(256, 2) void k_kmeans_assign(const int8_t* __restri
   }
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
+    if (!jvalid[j]) continue;                               // wave-uniform
     const int score = best[j] >> 7;
     const int idx = bchunk[j] * CCH + (CCH - 1 - (best[j] & (CCH - 1)));
     const int ps = __shfl_xor(score, 32, 64);
     const int pi = __shfl_xor(idx, 32, 64);
     const bool other = ps > score || (ps == score && pi < idx);
     const int lab = other ? pi : idx;
-    const int tok = tok0 + j * 32 + col;
+    const int tok = tokj[j];
     if constexpr (BAL) {
       // |v|^2 of the token: this lane holds half of its codes, the lane 32
       // apart the other half
@@ -349,12 +372,12 @@ __global__ __launch_bounds__(256, 2) void k_kmeans_assign(const int8_t* __restri
 #pragma unroll
         for (int q = 0; q < 4; ++q) vn = __builtin_amdgcn_sdot4(bop[j][c][q], bop[j][c][q], vn, false);
       vn += __shfl_xor(vn, 32, 64);
-      if (g == 0 && tok < N) {
-        prop[static_cast<size_t>(bh) * N + tok] = active[j] ? lab : -1;
+      if (g == 0 && tok >= 0) {
+        prop[static_cast<size_t>(bh) * N + tok] = lab;
         pdist[static_cast<size_t>(bh) * N + tok] = vn - (other ? ps : score);
       }
     } else {
-      if (g == 0 && tok < N) labels[static_cast<size_t>(bh) * N + tok] = lab;
+      if (g == 0 && tok >= 0) labels[static_cast<size_t>(bh) * N + tok] = lab;
     }
   }
 }
