@@ -674,6 +674,7 @@ __global__ __launch_bounds__(256) void k_sort_scatter(const int32_t* __restrict_
     int L = t < w1 ? lab[t] : -1;
     if (static_cast<unsigned>(L) >= static_cast<unsigned>(k)) L = -1;   // out-of-range labels are dropped
     uint64_t same = __ballot(L >= 0);
+    if (same == 0) continue;                     // no label to place in these 64 tokens (wave-uniform)
     for (int bit = 0; bit < nbits; ++bit) {
       const bool on = (L >> bit) & 1;
       const uint64_t m = __ballot(on);
