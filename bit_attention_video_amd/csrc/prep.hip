@@ -171,6 +171,13 @@ __global__ void k_init_centroids(const uint16_t* __restrict__ V, const int32_t* 
 // of a chunk in their low log2(kKeyRows) bits
 constexpr int kKeyRows = 128;
 
+// column tiles of 32 tokens per wave of the assignment (workgroup: 128 x this):
+// four share each centroid tile read from LDS and each chunk's overhead;
+// the balanced proposal rounds keep two, as their late rounds have few
+// tokens per workgroup and need the registers (and occupancy) less tight
+constexpr int kAssignTiles = 4;
+constexpr int kBalAssignTiles = 2;
+
 // int8 centroid codes and the packed score offsets cn32 = (127 - row % 128) - 128*|c|^2;
 // rows k..kpad-1 are padding (codes 0, offset INT_MIN: their key is never the maximum).
 template <int D>
@@ -198,6 +205,61 @@ __global__ __launch_bounds__(256) void k_quant_centroids(const float* __restrict
     cn32[static_cast<size_t>(bh) * kpad + i] = i < k ? (kKeyRows - 1 - (i & (kKeyRows - 1))) - sq * kKeyRows : INT_MIN;
 }
 
+// LDS operands of one 32-centroid tile: the centroid codes (the A operand)
+// and the key offsets of the 16 rows this lane's accumulators hold
+template <int NDC, int CSTR>
+__device__ __forceinline__ void assign_load_a(const int8_t* sC, int tile, int g, int col, v4i (&a)[NDC]) {
+#pragma unroll
+  for (int c = 0; c < NDC; ++c)
+    a[c] = *reinterpret_cast<const v4i*>(sC + (tile * 32 + col) * CSTR + 32 * c + 16 * g);
+}
+
+__device__ __forceinline__ void assign_load_off(const int32_t* sCn, int tile, int g, int32_t (&off)[16]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int4 o4 = *reinterpret_cast<const int4*>(sCn + tile * 32 + 8 * i + 4 * g);
+    off[4 * i + 0] = o4.x; off[4 * i + 1] = o4.y; off[4 * i + 2] = o4.z; off[4 * i + 3] = o4.w;
+  }
+}
+
+// 32 x 32 tile of C^T = centroid codes a . token codes b (exact int32)
+template <int NDC>
+__device__ __forceinline__ v16i assign_chain(const v4i (&a)[NDC], const v4i (&b)[NDC]) {
+  v16i acc = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+  for (int c = 0; c < NDC; ++c) acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[c], b[c], acc, 0, 0, 0);
+  return acc;
+}
+
+// the maximum of m and the tile's keys (acc << 8) + off
+__device__ __forceinline__ int assign_fold(const v16i& acc, const int32_t (&off)[16], int m) {
+#pragma unroll
+  for (int r = 0; r < 16; r += 2) {
+    const int k0 = static_cast<int>((static_cast<uint32_t>(acc[r]) << 8) + off[r]);
+    const int k1 = static_cast<int>((static_cast<uint32_t>(acc[r + 1]) << 8) + off[r + 1]);
+    m = max(max(m, k0), k1);
+  }
+  return m;
+}
+
+// Scores one centroid chunk (ntile tiles of 32 rows, in LDS) against the
+// wave's first NJ column tiles: per tile, each column tile's MFMA chain and
+// then the folding of its keys.  (Issuing the next chain before the fold, or
+// interleaving the two, measured slower: a wave then holds the matrix core
+// for longer bursts and the other waves of its SIMD wait.)
+template <int NJ, int NDC, int CSTR, int NJW>
+__device__ __forceinline__ void assign_chunk(const int8_t* sC, const int32_t* sCn, int ntile,
+                                             const v4i (&bop)[NJW][NDC], int (&cmax)[NJW], int g, int col) {
+  for (int tile = 0; tile < ntile; ++tile) {
+    v4i a[NDC];
+    int32_t off[16];
+    assign_load_a<NDC, CSTR>(sC, tile, g, col, a);
+    assign_load_off(sCn, tile, g, off);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) cmax[j] = assign_fold(assign_chain<NDC>(a, bop[j]), off, cmax[j]);
+  }
+}
+
 // One assignment pass: label = argmin_c (|c_q|^2 - 2 v_q.c_q), lowest index on
 // ties.  C^T = Cq . Vq^T runs on v_mfma_i32_32x32x32_i8 (exact int32); each
 // lane folds its 16 accumulator rows of a 32-centroid tile into keys
@@ -207,15 +269,15 @@ __global__ __launch_bounds__(256) void k_quant_centroids(const float* __restrict
 // 2^23, so the key fits in 31 bits), keeps a chunk's maximum only if its
 // score is strictly higher than the best so far, and the two lane halves that
 // share a token column are merged on (score, index).
-// A workgroup covers 256 tokens (4 waves x 2 column tiles of 32); centroids
-// stream through LDS in chunks of 128.
+// A workgroup covers 128 * NJW tokens (4 waves x NJW column tiles of 32);
+// centroids stream through LDS in chunks of 128.
 // BAL (balanced clusters, one proposal round): only tokens whose label in
 // `labels` is still -1 take part; full clusters carry zero codes and the
 // offset INT_MIN, so they are never chosen; the kernel writes each active
 // token's proposal (nearest cluster with room, lowest index on ties) to
 // `prop` and its exact squared distance |v|^2 - score to `pdist`, and -1 to
 // `prop` for every other token (whose `pdist` is left as it was).
-template <int D, bool BAL = false>
+template <int D, bool BAL, int NJW>
 __global__ __launch_bounds__(256, 2) void k_kmeans_assign(const int8_t* __restrict__ Vq,
                                                        const int8_t* __restrict__ Cq,
                                                        const int32_t* __restrict__ cn32, int N,
@@ -225,6 +287,7 @@ __global__ __launch_bounds__(256, 2) void k_kmeans_assign(const int8_t* __restri
   constexpr int NDC = D / 32;
   constexpr int CSTR = D + 16;
   constexpr int CCH = 128;
+  constexpr int WT = 128 * NJW;                 // tokens per workgroup
   __shared__ __attribute__((aligned(16))) int8_t sC[CCH * CSTR];
   __shared__ __attribute__((aligned(16))) int32_t sCn[CCH];
   const int bh = blockIdx.y;
@@ -232,48 +295,56 @@ __global__ __launch_bounds__(256, 2) void k_kmeans_assign(const int8_t* __restri
   const int8_t* vq = Vq + static_cast<size_t>(bh) * N * D;
   const int8_t* cq = Cq + static_cast<size_t>(bh) * kpad * D;
   const int32_t* cn = cn32 + static_cast<size_t>(bh) * kpad;
-  // token of column tile j of this wave (-1: none); jvalid[j]: the tile holds
-  // a token (wave-uniform), so the wave scores it
-  int tokj[2];
-  bool jvalid[2] = {true, true};
+  // token of column tile j of this wave (-1: none); the wave scores its
+  // first nj column tiles (wave-uniform)
+  int tokj[NJW];
+  int nj = NJW;
   if constexpr (BAL) {
     // only the workgroup's unplaced tokens take part: they are packed in
     // token order into the first column tiles (tile c is wave c % 4's
     // tile c / 4), so late rounds with few of them score few tiles
-    __shared__ int32_t sAct[256];
-    __shared__ int32_t sWaveAct[4];
-    const int tk = blockIdx.x * 256 + static_cast<int>(threadIdx.x);
-    const bool act = tk < N && labels[static_cast<size_t>(bh) * N + tk] < 0;
-    if (tk < N && !act) prop[static_cast<size_t>(bh) * N + tk] = -1;    // placed tokens propose nothing
-    const uint64_t am = __ballot(act);
-    if (lane == 0) sWaveAct[wave] = __popcll(am);
-    __syncthreads();
-    int nact = 0, before = 0;
+    constexpr int NG = WT / 256;                // groups of 256 tokens, one per thread
+    static_assert(WT % 256 == 0, "whole groups of 256 tokens");
+    __shared__ int32_t sAct[WT];
+    __shared__ int32_t sWaveAct[4 * NG];
+    int nact = 0;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      before += w < wave ? sWaveAct[w] : 0;
-      nact += sWaveAct[w];
+    for (int h = 0; h < NG; ++h) {
+      const int tk = blockIdx.x * WT + h * 256 + static_cast<int>(threadIdx.x);
+      const bool act = tk < N && labels[static_cast<size_t>(bh) * N + tk] < 0;
+      if (tk < N && !act) prop[static_cast<size_t>(bh) * N + tk] = -1;    // placed tokens propose nothing
+      const uint64_t am = __ballot(act);
+      if (lane == 0) sWaveAct[4 * h + wave] = __popcll(am);
+      __syncthreads();
+      int pre = 0, tot = 0;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        pre += w < wave ? sWaveAct[4 * h + w] : 0;
+        tot += sWaveAct[4 * h + w];
+      }
+      if (act) sAct[nact + pre + __popcll(am & ((1ull << lane) - 1ull))] = tk;
+      nact += tot;
     }
-    if (act) sAct[before + __popcll(am & ((1ull << lane) - 1ull))] = tk;
     __syncthreads();
     if (nact == 0) return;                                  // every token of the workgroup is placed
+    nj = 0;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < NJW; ++j) {
       const int c = wave + 4 * j, pos = c * 32 + col;
       tokj[j] = pos < nact ? sAct[pos] : -1;
-      jvalid[j] = c * 32 < nact;
+      nj += c * 32 < nact ? 1 : 0;
     }
   } else {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int tok = blockIdx.x * 256 + wave * 64 + j * 32 + col;
+    for (int j = 0; j < NJW; ++j) {
+      const int tok = blockIdx.x * WT + wave * 32 * NJW + j * 32 + col;
       tokj[j] = tok < N ? tok : -1;
     }
   }
 
-  v4i bop[2][NDC];
+  v4i bop[NJW][NDC];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
+  for (int j = 0; j < NJW; ++j) {
     const int tok = tokj[j];
 #pragma unroll
     for (int c = 0; c < NDC; ++c) {
@@ -283,8 +354,9 @@ __global__ __launch_bounds__(256, 2) void k_kmeans_assign(const int8_t* __restri
         bop[j][c] = v4i{0, 0, 0, 0};
     }
   }
-  int best[2] = {INT_MIN, INT_MIN};
-  int bchunk[2] = {0, 0};
+  int best[NJW], bchunk[NJW];
+#pragma unroll
+  for (int j = 0; j < NJW; ++j) { best[j] = INT_MIN; bchunk[j] = 0; }
   static_assert(CCH == kKeyRows, "a key orders the rows of one centroid chunk");
   // Centroid chunks are prefetched into registers one chunk ahead: the
   // global loads of chunk c+1 are issued before chunk c's tiles are scored
@@ -300,6 +372,10 @@ __global__ __launch_bounds__(256, 2) void k_kmeans_assign(const int8_t* __restri
     pf[i] = r < kpad ? *reinterpret_cast<const uint4*>(cq + static_cast<size_t>(r) * D + q16 * 16) : uint4{};
   }
   if (static_cast<int>(threadIdx.x) < min(CCH, kpad)) pfn = cn[threadIdx.x];
+  // nothing loaded so far may still be in flight when the chunk loop starts:
+  // the compiler then sees only the prefetch of the next chunk pending inside
+  // the loop and does not make every chunk's first MFMA wait for it
+  __builtin_amdgcn_s_waitcnt(0);
   for (int c0 = 0; c0 < kpad; c0 += CCH) {
     const int rows = min(CCH, kpad - c0);
     __syncthreads();                 // the previous chunk's tiles are scored
@@ -319,43 +395,25 @@ __global__ __launch_bounds__(256, 2) void k_kmeans_assign(const int8_t* __restri
     }
     if (static_cast<int>(threadIdx.x) < nrows) pfn = cn[n0 + threadIdx.x];
     __syncthreads();
-    int cmax[2] = {INT_MIN, INT_MIN};
-    for (int tile = 0; tile < rows / 32; ++tile) {
-      v4i a[NDC];
+    int cmax[NJW];
 #pragma unroll
-      for (int c = 0; c < NDC; ++c)
-        a[c] = *reinterpret_cast<const v4i*>(sC + (tile * 32 + col) * CSTR + 32 * c + 16 * g);
-      int32_t off[16];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int4 o4 = *reinterpret_cast<const int4*>(sCn + tile * 32 + 8 * i + 4 * g);
-        off[4 * i + 0] = o4.x; off[4 * i + 1] = o4.y; off[4 * i + 2] = o4.z; off[4 * i + 3] = o4.w;
-      }
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        if (!jvalid[j]) continue;                           // wave-uniform
-        v16i acc = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-        for (int c = 0; c < NDC; ++c)
-          acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[c], bop[j][c], acc, 0, 0, 0);
-        int key[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) key[r] = static_cast<int>((static_cast<uint32_t>(acc[r]) << 8) + off[r]);
-        int m = cmax[j];
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) m = max(max(m, key[r]), key[r + 1]);
-        cmax[j] = m;
-      }
+    for (int j = 0; j < NJW; ++j) cmax[j] = INT_MIN;
+    if (nj == NJW) {
+      assign_chunk<NJW, NDC, CSTR, NJW>(sC, sCn, rows / 32, bop, cmax, g, col);
+    } else if constexpr (BAL) {                             // wave-uniform
+      if constexpr (NJW > 3) if (nj == 3) assign_chunk<3, NDC, CSTR, NJW>(sC, sCn, rows / 32, bop, cmax, g, col);
+      if constexpr (NJW > 2) if (nj == 2) assign_chunk<2, NDC, CSTR, NJW>(sC, sCn, rows / 32, bop, cmax, g, col);
+      if (nj == 1) assign_chunk<1, NDC, CSTR, NJW>(sC, sCn, rows / 32, bop, cmax, g, col);
     }
     // chunks arrive in increasing index order: a later chunk must win on
     // score alone (the packed row only orders rows inside one chunk)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < NJW; ++j)
       if ((cmax[j] >> 7) > (best[j] >> 7)) { best[j] = cmax[j]; bchunk[j] = c0 / CCH; }
   }
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    if (!jvalid[j]) continue;                               // wave-uniform
+  for (int j = 0; j < NJW; ++j) {
+    if (j >= nj) continue;                                  // wave-uniform
     const int score = best[j] >> 7;
     const int idx = bchunk[j] * CCH + (CCH - 1 - (best[j] & (CCH - 1)));
     const int ps = __shfl_xor(score, 32, 64);
@@ -1375,7 +1433,7 @@ static hipError_t assign_t(const PrepArgs& a, int32_t* labels, hipStream_t st) {
   const int BH = a.B * a.H;
   hipLaunchKernelGGL(k_quant_centroids<D>, dim3((a.kpad + 3) / 4, BH), dim3(256), 0, st, a.C, a.sV, a.k, a.kpad,
                      a.Cq, a.cn32);
-  hipLaunchKernelGGL(k_kmeans_assign<D>, dim3((a.N + 255) / 256, BH), dim3(256), 0, st, a.Vq, a.Cq, a.cn32, a.N,
+  hipLaunchKernelGGL((k_kmeans_assign<D, false, kAssignTiles>), dim3((a.N + 128 * kAssignTiles - 1) / (128 * kAssignTiles), BH), dim3(256), 0, st, a.Vq, a.Cq, a.cn32, a.N,
                      a.kpad, labels);
   return hipGetLastError();
 }
@@ -1391,7 +1449,7 @@ static hipError_t bal_assign_t(const PrepArgs& a, int32_t* labels, hipStream_t s
   hipLaunchKernelGGL(k_bal_init, dim3((std::max(a.N, a.k) + 255) / 256, BH), dim3(256), 0, st, a.N, a.k, a.kvb,
                      a.rem, labels);
   for (int r = 0; r < kBalRounds; ++r) {
-    hipLaunchKernelGGL((k_kmeans_assign<D, true>), dim3((a.N + 255) / 256, BH), dim3(256), 0, st, a.Vq, a.Cq, a.cn32,
+    hipLaunchKernelGGL((k_kmeans_assign<D, true, kBalAssignTiles>), dim3((a.N + 128 * kBalAssignTiles - 1) / (128 * kBalAssignTiles), BH), dim3(256), 0, st, a.Vq, a.Cq, a.cn32,
                        a.N, a.kpad, labels, a.prop, a.pdist);
     if (hipError_t e = launch_sort(a, a.prop, a.perm_tmp, st)) return e;
     hipLaunchKernelGGL(k_bal_accept<D>, dim3(a.k, BH), dim3(kBalThreads), 0, st, a.perm_tmp, a.counts, a.starts,
