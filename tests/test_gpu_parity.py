@@ -217,6 +217,7 @@ def test_sort_bit_exact(N, k):
 # ------------------------------------------------------------------ k-means assignment
 @pytest.mark.parametrize("name,H,N,k", [("tiny", 2, None, None), ("mid", 2, None, None), ("video", 1, None, None),
                                          ("tiny", 1, 333, None),
+                                         ("tiny", 1, 513, 32),     # a second 512-token workgroup holding one token
                                          ("mid", 1, 4000, 300)])   # 320 padded centroids: chunks of 128, 128, 64
 def test_kmeans_assign_given_oracle_centroids(name, H, N, k):
     w = inputs.WORKLOADS[name]
