@@ -115,6 +115,11 @@ void carve_prep(Carver& cv, const Dims& D, vc::PrepArgs& a) {
     a.prop = cv.take<int32_t>(BH * D.N);
     a.pdist = cv.take<int32_t>(BH * D.N);
     a.rem = cv.take<int32_t>(BH * D.k);
+    for (int i = 0; i < 2; ++i) {
+      a.alist[i] = cv.take<int32_t>(BH * D.N);
+      a.acnt[i] = cv.take<int32_t>(BH);
+    }
+    a.ccnt = cv.take<int32_t>(BH * D.nsort);
   }
 }
 

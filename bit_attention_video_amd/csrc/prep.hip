@@ -271,19 +271,20 @@ __device__ __forceinline__ void assign_chunk(const int8_t* sC, const int32_t* sC
 // share a token column are merged on (score, index).
 // A workgroup covers 128 * NJW tokens (4 waves x NJW column tiles of 32);
 // centroids stream through LDS in chunks of 128.
-// BAL (balanced clusters, one proposal round): only tokens whose label in
-// `labels` is still -1 take part; full clusters carry zero codes and the
-// offset INT_MIN, so they are never chosen; the kernel writes each active
-// token's proposal (nearest cluster with room, lowest index on ties) to
-// `prop` and its exact squared distance |v|^2 - score to `pdist`, and -1 to
-// `prop` for every other token (whose `pdist` is left as it was).
+// BAL (balanced clusters, one proposal round): the acnt[bh] unplaced tokens
+// listed in alist take part; full clusters carry zero codes and the offset
+// INT_MIN, so they are never chosen; the kernel writes the proposal (nearest
+// cluster with room, lowest index on ties) of the i-th listed token to
+// prop[i] and its exact squared distance |v|^2 - score to pdist[token].
 template <int D, bool BAL, int NJW>
-__global__ __launch_bounds__(256, 2) void k_kmeans_assign(const int8_t* __restrict__ Vq,
+__global__ __launch_bounds__(256, BAL ? 4 : 2) void k_kmeans_assign(const int8_t* __restrict__ Vq,
                                                        const int8_t* __restrict__ Cq,
                                                        const int32_t* __restrict__ cn32, int N,
                                                        int kpad, int32_t* __restrict__ labels,
                                                        int32_t* __restrict__ prop = nullptr,
-                                                       int32_t* __restrict__ pdist = nullptr) {
+                                                       int32_t* __restrict__ pdist = nullptr,
+                                                       const int32_t* __restrict__ alist = nullptr,
+                                                       const int32_t* __restrict__ acnt = nullptr) {
   constexpr int NDC = D / 32;
   constexpr int CSTR = D + 16;
   constexpr int CCH = 128;
@@ -300,39 +301,18 @@ __global__ __launch_bounds__(256, 2) void k_kmeans_assign(const int8_t* __restri
   int tokj[NJW];
   int nj = NJW;
   if constexpr (BAL) {
-    // only the workgroup's unplaced tokens take part: they are packed in
-    // token order into the first column tiles (tile c is wave c % 4's
-    // tile c / 4), so late rounds with few of them score few tiles
-    constexpr int NG = WT / 256;                // groups of 256 tokens, one per thread
-    static_assert(WT % 256 == 0, "whole groups of 256 tokens");
-    __shared__ int32_t sAct[WT];
-    __shared__ int32_t sWaveAct[4 * NG];
-    int nact = 0;
-#pragma unroll
-    for (int h = 0; h < NG; ++h) {
-      const int tk = blockIdx.x * WT + h * 256 + static_cast<int>(threadIdx.x);
-      const bool act = tk < N && labels[static_cast<size_t>(bh) * N + tk] < 0;
-      if (tk < N && !act) prop[static_cast<size_t>(bh) * N + tk] = -1;    // placed tokens propose nothing
-      const uint64_t am = __ballot(act);
-      if (lane == 0) sWaveAct[4 * h + wave] = __popcll(am);
-      __syncthreads();
-      int pre = 0, tot = 0;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        pre += w < wave ? sWaveAct[4 * h + w] : 0;
-        tot += sWaveAct[4 * h + w];
-      }
-      if (act) sAct[nact + pre + __popcll(am & ((1ull << lane) - 1ull))] = tk;
-      nact += tot;
-    }
-    __syncthreads();
-    if (nact == 0) return;                                  // every token of the workgroup is placed
+    // the round's unplaced tokens (alist, in token order) go to the
+    // workgroups WT at a time; tile c of a workgroup is wave c % 4's tile
+    // c / 4, so a part-filled workgroup fills the first tiles of every wave
+    const int n = acnt[bh], j0 = blockIdx.x * WT;
+    if (j0 >= n) return;                                    // past the round's tokens
+    const int na = min(WT, n - j0);
     nj = 0;
 #pragma unroll
     for (int j = 0; j < NJW; ++j) {
       const int c = wave + 4 * j, pos = c * 32 + col;
-      tokj[j] = pos < nact ? sAct[pos] : -1;
-      nj += c * 32 < nact ? 1 : 0;
+      tokj[j] = pos < na ? alist[static_cast<size_t>(bh) * N + j0 + pos] : -1;
+      nj += c * 32 < na ? 1 : 0;
     }
   } else {
 #pragma unroll
@@ -431,7 +411,7 @@ __global__ __launch_bounds__(256, 2) void k_kmeans_assign(const int8_t* __restri
         for (int q = 0; q < 4; ++q) vn = __builtin_amdgcn_sdot4(bop[j][c][q], bop[j][c][q], vn, false);
       vn += __shfl_xor(vn, 32, 64);
       if (g == 0 && tok >= 0) {
-        prop[static_cast<size_t>(bh) * N + tok] = lab;
+        prop[static_cast<size_t>(bh) * N + blockIdx.x * WT + (wave + 4 * j) * 32 + col] = lab;   // list position
         pdist[static_cast<size_t>(bh) * N + tok] = vn - (other ? ps : score);
       }
     } else {
@@ -444,17 +424,106 @@ __global__ __launch_bounds__(256, 2) void k_kmeans_assign(const int8_t* __restri
 // Capacities: kv_block places per cluster, the last cluster the tail of the
 // sequence, so that after the stable sort every block holds one cluster.
 // Per pass: rem = capacities and labels = -1; then kBalRounds rounds of
-// (proposals by k_kmeans_assign<D, true>; proposals grouped by cluster with
-// the stable counting sort; k_bal_accept); then k_bal_fill places whatever
-// is left in token order, clusters in index order.
+// (proposals of the unplaced tokens by k_kmeans_assign<D, true>; proposals
+// grouped by cluster with the stable counting sort; k_bal_accept; the tokens
+// still unplaced listed for the next round by k_bal_count and k_bal_place);
+// then k_bal_fill places whatever is left in token order, clusters in index
+// order.
 constexpr int kBalRounds = 12;
 constexpr int kBalThreads = 256;
+constexpr int kAcceptPer = 8;      // proposers per thread held in registers by k_bal_accept
 
-__global__ void k_bal_init(int N, int k, int kvb, int32_t* __restrict__ rem, int32_t* __restrict__ labels) {
+__global__ void k_bal_init(int N, int k, int kvb, int32_t* __restrict__ rem, int32_t* __restrict__ labels,
+                           int32_t* __restrict__ alist, int32_t* __restrict__ acnt) {
   const int bh = blockIdx.y;
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < N) labels[static_cast<size_t>(bh) * N + i] = -1;
+  if (i < N) {
+    labels[static_cast<size_t>(bh) * N + i] = -1;
+    alist[static_cast<size_t>(bh) * N + i] = i;            // every token is unplaced
+  }
   if (i < k) rem[static_cast<size_t>(bh) * k + i] = i + 1 < k ? kvb : N - (k - 1) * kvb;
+  if (i == 0) acnt[bh] = N;
+}
+
+// The tokens of list `in` (cin[bh] of them, token order) that are still
+// unplaced after a round go, in the same order, to list `out`, and their
+// number to cout[bh]: k_bal_count counts them per chunk of kSortChunk list
+// entries, k_bal_place writes each chunk's behind those of the chunks before
+// it.  Each thread takes kCompactPer consecutive entries of its chunk.
+constexpr int kCompactThreads = 256;
+constexpr int kCompactPer = kSortChunk / kCompactThreads;
+
+// the unplaced tokens among a thread's entries of chunk ch (-1: none or placed)
+__device__ __forceinline__ int bal_survivors(const int32_t* li, const int32_t* lab, int n, int ch,
+                                             int (&tok)[kCompactPer]) {
+  int cnt = 0;
+#pragma unroll
+  for (int e = 0; e < kCompactPer; ++e) {
+    const int j = ch * kSortChunk + static_cast<int>(threadIdx.x) * kCompactPer + e;
+    tok[e] = j < n ? li[j] : -1;
+  }
+#pragma unroll
+  for (int e = 0; e < kCompactPer; ++e) {
+    if (tok[e] >= 0 && lab[tok[e]] >= 0) tok[e] = -1;         // placed
+    cnt += tok[e] >= 0 ? 1 : 0;
+  }
+  return cnt;
+}
+
+__global__ __launch_bounds__(kCompactThreads) void k_bal_count(const int32_t* __restrict__ in,
+                                                               const int32_t* __restrict__ cin,
+                                                               const int32_t* __restrict__ labels, int N,
+                                                               int nch, int32_t* __restrict__ ccnt) {
+  __shared__ int red[kCompactThreads / 64];
+  const int bh = blockIdx.y, ch = blockIdx.x;
+  const int n = cin[bh];
+  int tok[kCompactPer];
+  int cnt = ch * kSortChunk < n ? bal_survivors(in + static_cast<size_t>(bh) * N,
+                                                 labels + static_cast<size_t>(bh) * N, n, ch, tok) : 0;
+  for (int o = 32; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o, 64);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = cnt;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int t = 0;
+    for (int w = 0; w < kCompactThreads / 64; ++w) t += red[w];
+    ccnt[static_cast<size_t>(bh) * nch + ch] = t;
+  }
+}
+
+__global__ __launch_bounds__(kCompactThreads) void k_bal_place(const int32_t* __restrict__ in,
+                                                               const int32_t* __restrict__ cin,
+                                                               const int32_t* __restrict__ labels, int N,
+                                                               int nch, const int32_t* __restrict__ ccnt,
+                                                               int32_t* __restrict__ out,
+                                                               int32_t* __restrict__ cout) {
+  __shared__ int part[kCompactThreads / 64];
+  const int bh = blockIdx.y, ch = blockIdx.x, t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int n = cin[bh];
+  const int32_t* cc = ccnt + static_cast<size_t>(bh) * nch;
+  if (ch == 0 && t == 0) {
+    int tot = 0;
+    for (int c = 0; c < nch; ++c) tot += cc[c];
+    cout[bh] = tot;
+  }
+  if (ch * kSortChunk >= n) return;
+  int base = 0;                                   // survivors of the chunks before this one
+  for (int c = lane; c < ch; c += 64) base += cc[c];
+  for (int o = 32; o > 0; o >>= 1) base += __shfl_xor(base, o, 64);
+  int tok[kCompactPer];
+  const int cnt = bal_survivors(in + static_cast<size_t>(bh) * N, labels + static_cast<size_t>(bh) * N, n, ch, tok);
+  int incl = cnt;                                 // inclusive scan in the wave
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += v;
+  }
+  if (lane == 63) part[wave] = incl;
+  __syncthreads();
+  int pos = base + incl - cnt;
+  for (int w = 0; w < wave; ++w) pos += part[w];
+  int32_t* lo = out + static_cast<size_t>(bh) * N;
+#pragma unroll
+  for (int e = 0; e < kCompactPer; ++e)
+    if (tok[e] >= 0) lo[pos++] = tok[e];
 }
 
 // sum of v over the workgroup (every thread gets it)
@@ -502,6 +571,56 @@ __global__ __launch_bounds__(kBalThreads) void k_bal_accept(const int32_t* __res
   if (cnt <= r) {
     for (int i = t; i < cnt; i += kBalThreads) lab[list[i]] = c;
     r -= cnt;
+  } else if (cnt <= kAcceptPer * kBalThreads) {
+    // the same selection with the proposers' tokens and distances held in
+    // registers (proposer i: thread i % kBalThreads, slot i / kBalThreads),
+    // so the binary search does not gather them again at every step
+    int tk[kAcceptPer], dv[kAcceptPer];
+#pragma unroll
+    for (int e = 0; e < kAcceptPer; ++e) {
+      const int i = e * kBalThreads + t;
+      tk[e] = i < cnt ? list[i] : -1;
+    }
+#pragma unroll
+    for (int e = 0; e < kAcceptPer; ++e) dv[e] = tk[e] >= 0 ? dist[tk[e]] : INT_MAX;
+    int lo = INT_MAX, hi = INT_MIN;
+#pragma unroll
+    for (int e = 0; e < kAcceptPer; ++e)
+      if (tk[e] >= 0) {
+        lo = min(lo, dv[e]);
+        hi = max(hi, dv[e]);
+      }
+    lo = -bal_block_max(-lo, red);
+    hi = bal_block_max(hi, red);
+    while (lo < hi) {                                   // uniform across the workgroup
+      const int mid = lo + (hi - lo) / 2;
+      int n = 0;
+#pragma unroll
+      for (int e = 0; e < kAcceptPer; ++e) n += tk[e] >= 0 && dv[e] <= mid ? 1 : 0;
+      if (bal_block_sum(n, red) >= r) hi = mid;
+      else lo = mid + 1;
+    }
+    const int theta = lo;
+    int nl = 0;
+#pragma unroll
+    for (int e = 0; e < kAcceptPer; ++e) nl += tk[e] >= 0 && dv[e] < theta ? 1 : 0;
+    const int need = r - bal_block_sum(nl, red);       // >= 1 proposers at distance theta, in token order
+    const int lane = t & 63, wave = t >> 6;
+    int run = 0;
+#pragma unroll
+    for (int e = 0; e < kAcceptPer; ++e) {
+      if (e * kBalThreads >= cnt) break;                // uniform
+      const bool eq = tk[e] >= 0 && dv[e] == theta;
+      const uint64_t bal = __ballot(eq);
+      __syncthreads();
+      if (lane == 0) red[wave] = __popcll(bal);
+      __syncthreads();
+      int before = run + __popcll(bal & ((1ull << lane) - 1ull));
+      for (int w = 0; w < wave; ++w) before += red[w];
+      if (tk[e] >= 0 && (dv[e] < theta || (eq && before < need))) lab[tk[e]] = c;
+      for (int w = 0; w < kBalThreads / 64; ++w) run += red[w];
+    }
+    r = 0;
   } else {
     // theta = the r-th smallest distance: the smallest value with
     // #(dist <= theta) >= r (binary search over the exact integers)
@@ -550,18 +669,22 @@ __global__ __launch_bounds__(kBalThreads) void k_bal_accept(const int32_t* __res
   }
 }
 
-// Tokens left after the rounds take the remaining places: the u-th
-// unassigned token (token order) goes to the cluster holding place u when
-// the clusters' remaining places are laid out in index order.
+// Tokens left after the rounds (the ucnt[bh] of list ul, token order) take
+// the remaining places: the u-th goes to the cluster holding place u when the
+// clusters' remaining places are laid out in index order.
 constexpr int kFillThreads = 1024;
 __global__ __launch_bounds__(kFillThreads) void k_bal_fill(const int32_t* __restrict__ rem, int N, int k,
+                                                           const int32_t* __restrict__ ul,
+                                                           const int32_t* __restrict__ ucnt,
                                                            int32_t* __restrict__ labels) {
   constexpr int PER = kMaxClusters / kFillThreads;
   __shared__ int cum[kMaxClusters];
   __shared__ int part[kFillThreads];
-  __shared__ int red[kFillThreads / 64];
-  const int bh = blockIdx.x, t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int bh = blockIdx.x, t = threadIdx.x;
+  const int n = ucnt[bh];
+  if (n == 0) return;
   int32_t* lab = labels + static_cast<size_t>(bh) * N;
+  const int32_t* list = ul + static_cast<size_t>(bh) * N;
   // cum = exclusive prefix sum of rem over the clusters (PER per thread, then
   // an inclusive Hillis-Steele scan of the per-thread totals)
   int mine[PER];
@@ -587,37 +710,32 @@ __global__ __launch_bounds__(kFillThreads) void k_bal_fill(const int32_t* __rest
     acc += mine[e];
   }
   __syncthreads();
-  int run = 0;
-  for (int base = 0; base < N; base += kFillThreads) {
-    const int i = base + t;
-    const bool un = i < N && lab[i] < 0;
-    const uint64_t bal = __ballot(un);
-    __syncthreads();
-    if (lane == 0) red[wave] = __popcll(bal);
-    __syncthreads();
-    int u = run + __popcll(bal & ((1ull << lane) - 1ull));
-    for (int w = 0; w < wave; ++w) u += red[w];
-    if (un) {
-      int a = 0, b = k - 1;                 // the last cluster with cum <= u
-      while (a < b) {
-        const int m = (a + b + 1) / 2;
-        if (cum[m] <= u) a = m;
-        else b = m - 1;
-      }
-      lab[i] = a;
+  for (int u = t; u < n; u += kFillThreads) {
+    int a = 0, b = k - 1;                     // the last cluster with cum <= u
+    while (a < b) {
+      const int m = (a + b + 1) / 2;
+      if (cum[m] <= u) a = m;
+      else b = m - 1;
     }
-    for (int w = 0; w < kFillThreads / 64; ++w) run += red[w];
+    lab[list[u]] = a;
   }
 }
 
 // ---- stable counting sort by label ------------------------------------------------
+// Keys outside [0, k) are left out.  With ncnt, only the first ncnt[bh] keys of
+// a head take part (the chunks past them are skipped; chunk 0 always counts,
+// so a head without keys gets zero counts); with ids, key i belongs to token
+// ids[i] (the keys come in token order), which is what perm receives.
 __global__ __launch_bounds__(256) void k_sort_hist(const int32_t* __restrict__ labels, int N, int k,
-                                                   int nch, int32_t* __restrict__ hist) {
+                                                   int nch, int32_t* __restrict__ hist,
+                                                   const int32_t* __restrict__ ncnt) {
   __shared__ int32_t cnt[kMaxClusters];
   const int bh = blockIdx.y, ch = blockIdx.x;
+  const int n = ncnt ? min(N, ncnt[bh]) : N;       // keys in use
+  if (n > 0 && ch * kSortChunk >= n) return;       // a chunk past them (chunk 0 always counts)
   for (int i = threadIdx.x; i < k; i += 256) cnt[i] = 0;
   __syncthreads();
-  const int t0 = ch * kSortChunk, t1 = min(N, t0 + kSortChunk);
+  const int t0 = ch * kSortChunk, t1 = min(n, t0 + kSortChunk);
   for (int t = t0 + threadIdx.x; t < t1; t += 256) {
     const int L = labels[static_cast<size_t>(bh) * N + t];
     if (static_cast<unsigned>(L) < static_cast<unsigned>(k)) atomicAdd(&cnt[L], 1);
@@ -633,14 +751,16 @@ __global__ __launch_bounds__(256) void k_sort_hist(const int32_t* __restrict__ l
 // words of a chunk's row); each label's chunk counts are read in batches of
 // eight before they are added, so the loads overlap.  The label prefix is
 // one workgroup scan per group of 1024 labels, in label order.
-__global__ __launch_bounds__(1024) void k_sort_scan(int32_t* __restrict__ hist, int k, int nch,
+__global__ __launch_bounds__(1024) void k_sort_scan(int32_t* __restrict__ hist, int k, int nch_all,
                                                     int32_t* __restrict__ counts,
-                                                    int32_t* __restrict__ starts) {
+                                                    int32_t* __restrict__ starts,
+                                                    const int32_t* __restrict__ ncnt) {
   constexpr int PER = kMaxClusters / 1024;
   constexpr int CB = 8;                        // chunk counts read per batch
   __shared__ int32_t part[1024];
   const int bh = blockIdx.x;
-  int32_t* h = hist + static_cast<size_t>(bh) * nch * k;
+  const int nch = ncnt ? max(1, min(nch_all, (ncnt[bh] + kSortChunk - 1) / kSortChunk)) : nch_all;   // chunks in use
+  int32_t* h = hist + static_cast<size_t>(bh) * nch_all * k;
   int tot[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) {
@@ -692,27 +812,41 @@ __global__ __launch_bounds__(1024) void k_sort_scan(int32_t* __restrict__ hist, 
 }
 
 // Tokens of a chunk are placed in token order.  Each of the 4 waves owns a
-// contiguous quarter of the chunk: per-wave label counts (LDS) prefixed
-// across the waves give each wave its own base per label, and the wave then
-// walks its quarter 64 tokens at a time, ranking a token among the round's
-// equal labels by matching label bits with ballots (the lanes whose label
-// equals this lane's, below it) and advancing its bases.
+// contiguous quarter of the chunk, whose labels (and token ids) it loads into
+// registers at once: per-wave label counts (LDS) prefixed across the waves
+// give each wave its own base per label, and the wave then walks its quarter
+// 64 tokens at a time, ranking a token among the round's equal labels by
+// matching label bits with ballots (the lanes whose label equals this
+// lane's, below it) and advancing its bases.
 __global__ __launch_bounds__(256) void k_sort_scatter(const int32_t* __restrict__ labels,
                                                       const int32_t* __restrict__ hist, int N,
-                                                      int k, int nch, int32_t* __restrict__ perm) {
+                                                      int k, int nch, int32_t* __restrict__ perm,
+                                                      const int32_t* __restrict__ ids,
+                                                      const int32_t* __restrict__ ncnt) {
   constexpr int QW = kSortChunk / 4;            // tokens per wave
+  constexpr int NR = QW / 64;                   // rounds of 64 per wave
   __shared__ int32_t base[4][kMaxClusters];
   const int bh = blockIdx.y, ch = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int t0 = ch * kSortChunk, t1 = min(N, t0 + kSortChunk);
+  const int n = ncnt ? min(N, ncnt[bh]) : N;
+  if (ch * kSortChunk >= n) return;              // no key in this chunk
+  const int t0 = ch * kSortChunk, t1 = min(n, t0 + kSortChunk);
   const int w0 = t0 + wave * QW, w1 = min(t1, w0 + QW);
   const int32_t* lab = labels + static_cast<size_t>(bh) * N;
+  int key[NR], tok[NR];
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    const int t = w0 + 64 * i + lane;
+    int L = t < w1 ? lab[t] : -1;
+    if (static_cast<unsigned>(L) >= static_cast<unsigned>(k)) L = -1;   // out-of-range labels are dropped
+    key[i] = L;
+    tok[i] = ids && L >= 0 ? ids[static_cast<size_t>(bh) * N + t] : t;
+  }
   for (int i = threadIdx.x; i < 4 * k; i += 256) base[i / k][i % k] = 0;   // the k labels in use
   __syncthreads();
-  for (int t = w0 + lane; t < w1; t += 64) {
-    const int L = lab[t];
-    if (static_cast<unsigned>(L) < static_cast<unsigned>(k)) atomicAdd(&base[wave][L], 1);
-  }
+#pragma unroll
+  for (int i = 0; i < NR; ++i)
+    if (key[i] >= 0) atomicAdd(&base[wave][key[i]], 1);
   __syncthreads();
   for (int L = threadIdx.x; L < k; L += 256) {
     int run = hist[(static_cast<size_t>(bh) * nch + ch) * k + L];
@@ -727,10 +861,9 @@ __global__ __launch_bounds__(256) void k_sort_scatter(const int32_t* __restrict_
   int nbits = 1;
   while ((1 << nbits) < k) ++nbits;
   const uint64_t below = (1ull << lane) - 1ull;
-  for (int r0 = w0; r0 < w1; r0 += 64) {
-    const int t = r0 + lane;
-    int L = t < w1 ? lab[t] : -1;
-    if (static_cast<unsigned>(L) >= static_cast<unsigned>(k)) L = -1;   // out-of-range labels are dropped
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    const int L = key[i];
     uint64_t same = __ballot(L >= 0);
     if (same == 0) continue;                     // no label to place in these 64 tokens (wave-uniform)
     for (int bit = 0; bit < nbits; ++bit) {
@@ -742,7 +875,7 @@ __global__ __launch_bounds__(256) void k_sort_scatter(const int32_t* __restrict_
     const int total = __popcll(same);
     int pos = 0;
     if (L >= 0) pos = base[wave][L];
-    if (L >= 0) perm[static_cast<size_t>(bh) * N + pos + before] = t;
+    if (L >= 0) perm[static_cast<size_t>(bh) * N + pos + before] = tok[i];
     if (L >= 0 && before == total - 1) base[wave][L] = pos + total;
   }
 }
@@ -1447,15 +1580,26 @@ static hipError_t bal_assign_t(const PrepArgs& a, int32_t* labels, hipStream_t s
   hipLaunchKernelGGL(k_quant_centroids<D>, dim3((a.kpad + 3) / 4, BH), dim3(256), 0, st, a.C, a.sV, a.k, a.kpad,
                      a.Cq, a.cn32);
   hipLaunchKernelGGL(k_bal_init, dim3((std::max(a.N, a.k) + 255) / 256, BH), dim3(256), 0, st, a.N, a.k, a.kvb,
-                     a.rem, labels);
+                     a.rem, labels, a.alist[0], a.acnt[0]);
+  // round r reads the unplaced tokens from list r % 2 and leaves the ones
+  // still unplaced in the other list, so later rounds score (and sort) only
+  // those: past the first rounds nearly every workgroup would hold a few
+  constexpr int WT = 128 * kBalAssignTiles;
   for (int r = 0; r < kBalRounds; ++r) {
-    hipLaunchKernelGGL((k_kmeans_assign<D, true, kBalAssignTiles>), dim3((a.N + 128 * kBalAssignTiles - 1) / (128 * kBalAssignTiles), BH), dim3(256), 0, st, a.Vq, a.Cq, a.cn32,
-                       a.N, a.kpad, labels, a.prop, a.pdist);
-    if (hipError_t e = launch_sort(a, a.prop, a.perm_tmp, st)) return e;
+    const int32_t* lin = a.alist[r & 1];
+    const int32_t* cin = a.acnt[r & 1];
+    hipLaunchKernelGGL((k_kmeans_assign<D, true, kBalAssignTiles>), dim3((a.N + WT - 1) / WT, BH), dim3(256), 0, st,
+                       a.Vq, a.Cq, a.cn32, a.N, a.kpad, labels, a.prop, a.pdist, lin, cin);
+    if (hipError_t e = launch_sort_list(a, a.prop, lin, cin, a.perm_tmp, st)) return e;
     hipLaunchKernelGGL(k_bal_accept<D>, dim3(a.k, BH), dim3(kBalThreads), 0, st, a.perm_tmp, a.counts, a.starts,
                        a.pdist, a.N, a.k, a.kpad, a.rem, labels, a.Cq, a.cn32);
+    hipLaunchKernelGGL(k_bal_count, dim3(a.nsort, BH), dim3(kCompactThreads), 0, st, lin, cin, labels, a.N,
+                       a.nsort, a.ccnt);
+    hipLaunchKernelGGL(k_bal_place, dim3(a.nsort, BH), dim3(kCompactThreads), 0, st, lin, cin, labels, a.N,
+                       a.nsort, a.ccnt, a.alist[(r + 1) & 1], a.acnt[(r + 1) & 1]);
   }
-  hipLaunchKernelGGL(k_bal_fill, dim3(BH), dim3(kFillThreads), 0, st, a.rem, a.N, a.k, labels);
+  hipLaunchKernelGGL(k_bal_fill, dim3(BH), dim3(kFillThreads), 0, st, a.rem, a.N, a.k, a.alist[kBalRounds & 1],
+                     a.acnt[kBalRounds & 1], labels);
   return hipGetLastError();
 }
 hipError_t launch_bal_assign(const PrepArgs& a, int32_t* labels, hipStream_t st) {
@@ -1475,12 +1619,17 @@ hipError_t launch_cluster_order(const PrepArgs& a, hipStream_t st) {
   return a.d == 64 ? order_t<64>(a, st) : order_t<128>(a, st);
 }
 
-hipError_t launch_sort(const PrepArgs& a, const int32_t* labels, int32_t* perm, hipStream_t st) {
+hipError_t launch_sort_list(const PrepArgs& a, const int32_t* keys, const int32_t* ids, const int32_t* n,
+                            int32_t* perm, hipStream_t st) {
   const int BH = a.B * a.H;
-  hipLaunchKernelGGL(k_sort_hist, dim3(a.nsort, BH), dim3(256), 0, st, labels, a.N, a.k, a.nsort, a.hist);
-  hipLaunchKernelGGL(k_sort_scan, dim3(BH), dim3(1024), 0, st, a.hist, a.k, a.nsort, a.counts, a.starts);
-  hipLaunchKernelGGL(k_sort_scatter, dim3(a.nsort, BH), dim3(256), 0, st, labels, a.hist, a.N, a.k, a.nsort, perm);
+  hipLaunchKernelGGL(k_sort_hist, dim3(a.nsort, BH), dim3(256), 0, st, keys, a.N, a.k, a.nsort, a.hist, n);
+  hipLaunchKernelGGL(k_sort_scan, dim3(BH), dim3(1024), 0, st, a.hist, a.k, a.nsort, a.counts, a.starts, n);
+  hipLaunchKernelGGL(k_sort_scatter, dim3(a.nsort, BH), dim3(256), 0, st, keys, a.hist, a.N, a.k, a.nsort, perm,
+                     ids, n);
   return hipGetLastError();
+}
+hipError_t launch_sort(const PrepArgs& a, const int32_t* labels, int32_t* perm, hipStream_t st) {
+  return launch_sort_list(a, labels, nullptr, nullptr, perm, st);
 }
 
 template <int D>

@@ -34,9 +34,12 @@ struct PrepArgs {
   float* Ctmp;         // [BH,k,d]   renumbered centroids
   int32_t* init;       // [BH,k]     seeded initial token indices
   // balanced clusters (capped assignment)
-  int32_t* prop;       // [BH,N]     proposed cluster of each token in a round (-1: none)
-  int32_t* pdist;      // [BH,N]     squared int8 distance to it
+  int32_t* prop;       // [BH,N]     proposed cluster of the round's i-th unplaced token
+  int32_t* pdist;      // [BH,N]     squared int8 distance of each token to its proposal
   int32_t* rem;        // [BH,k]     places left per cluster
+  int32_t* alist[2];   // [BH,N]     unplaced tokens in token order (a round reads one, fills the other)
+  int32_t* acnt[2];    // [BH]       their numbers
+  int32_t* ccnt;       // [BH,nsort] their numbers per chunk of kSortChunk list entries
 };
 
 struct PrepOut {
@@ -76,6 +79,8 @@ hipError_t launch_init_centroids(const PrepArgs& a, const int32_t* init, hipStre
 hipError_t launch_assign(const PrepArgs& a, int32_t* labels, hipStream_t st);
 hipError_t launch_bal_assign(const PrepArgs& a, int32_t* labels, hipStream_t st);
 hipError_t launch_sort(const PrepArgs& a, const int32_t* labels, int32_t* perm, hipStream_t st);
+hipError_t launch_sort_list(const PrepArgs& a, const int32_t* keys, const int32_t* ids, const int32_t* n,
+                            int32_t* perm, hipStream_t st);
 hipError_t launch_cluster_order(const PrepArgs& a, hipStream_t st);
 hipError_t launch_update(const PrepArgs& a, const int32_t* perm, hipStream_t st);
 hipError_t launch_iota(int32_t* perm, int N, size_t total, hipStream_t st);
