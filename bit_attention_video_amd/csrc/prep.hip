@@ -75,7 +75,15 @@ __global__ void k_stats_final(const double* __restrict__ kpart, const uint32_t* 
                               int N, int nch, float* __restrict__ mu, float* __restrict__ sV) {
   const int bh = blockIdx.x, c = threadIdx.x;
   double s = 0.0;
-  for (int ch = 0; ch < nch; ++ch) s += kpart[(static_cast<size_t>(bh) * nch + ch) * D + c];
+  constexpr int U = 8;                          // partials loaded per batch, added in chunk order
+  for (int c0 = 0; c0 < nch; c0 += U) {
+    double v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = c0 + u < nch ? kpart[(static_cast<size_t>(bh) * nch + c0 + u) * D + c] : 0.0;
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (c0 + u < nch) s += v[u];
+  }
   mu[static_cast<size_t>(bh) * D + c] = static_cast<float>(s / static_cast<double>(N));
   if (c == 0) {
     const float a = __uint_as_float(vamax[bh]);
